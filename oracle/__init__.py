@@ -1,0 +1,55 @@
+"""CPU oracle for the grouped 4-bit expert GEMM — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. The product (the HIP library and its Python binding) never calls
+it, and it shares no code with the product: it is a plain, slow, fp64 numpy
+restatement of what the method computes, written so that each step can be
+checked against the source pages by eye.
+
+Sources (web pages about the `grouped-nf4-gemm` package, cited by title and
+section):
+
+* "grouped-nf4-gemm 0.33.1" (PyPI project page), opening description: one launch
+  computes the expert GEMM for every routed expert straight from 4-bit codes; each
+  code goes through a 16-value table, is multiplied by its block scale, products
+  are summed in fp32 and the result is rounded to bf16. NF4 follows the
+  bitsandbytes 4-bit layout; MXFP4 is OCP e2m1 codes with e8m0 block scales.
+* "grouped-nf4-gemm releases", v0.2.6 section "The patch point": the result is
+  the one of the per-expert loop that the kernel replaces — activation rows
+  sorted by expert, `sizes[e]` rows for expert e, one matmul per expert.
+* "grouped-nf4-gemm 0.33.1", section "Try it on CPU right now", blocks 1 and 2:
+  packer shapes, round-trip errors of about 0.09 (NF4) and 0.12 (MXFP4), and
+  that re-packing a decoded NF4 weight gives the same bytes.
+* "grouped-nf4-gemm capability index" (index.json), `system_manifest.owns`: the
+  package owns the input gradient of the grouped GEMM, dX = dY . W, computed on
+  the same packed bytes.
+
+Two public specifications that the pages rely on but do not print supply the
+value tables: the NF4 data type (QLoRA, Dettmers et al. 2023, appendix E) and
+the OCP Microscaling Formats (MX) v1.0 specification (e2m1 element, e8m0 scale).
+
+`PARITY` below says what pins each function (tests/test_oracle_*.py).
+"""
+from .codebooks import (NF4_TABLE_F32, NF4_TABLE_BITS, nf4_table_closed_form,
+                        e2m1_value, E2M1_TABLE, e8m0_value)
+from .pack import (quantize_pack_nf4, dequant_nf4, unpack_nf4_codes, pack_nf4_codes,
+                   quantize_pack_mxfp4, dequant_mxfp4, unpack_mxfp4_codes,
+                   pack_mxfp4_codes, nf4_w32, mxfp4_w32, bf16_rne_bits, fp16_rne_bits)
+from .grouped import (offsets, grouped_ref, loop_ref, dgrad_ref,
+                      sampled_fwd_ref, sampled_dgrad_ref, brute_force_ref,
+                      brute_force_dgrad)
+
+PARITY = {
+    "NF4_TABLE_F32": "pinned: published decimal values and closed-form quantiles",
+    "e2m1_value / E2M1_TABLE": "pinned: OCP value fixture tests/golden/e2m1_ocp.txt",
+    "e8m0_value": "pinned: math.ldexp over all 256 bytes, NaN at 255",
+    "quantize_pack_nf4": "pinned: page shapes, rel-err ~0.09, idempotence, "
+                         "brute-force nearest code",
+    "quantize_pack_mxfp4": "pinned: page shapes, rel-err ~0.12, brute-force nearest",
+    "nibble order": "parity unpinned against external bytes (no released bytes "
+                    "are available); pinned only by the stated convention",
+    "grouped_ref": "pinned: pure-Python brute force, exact integer cases, loop_ref",
+    "dgrad_ref": "pinned: adjoint identity with grouped_ref, pure-Python brute force",
+}
+
+__all__ = [n for n in dir() if not n.startswith("_")]
