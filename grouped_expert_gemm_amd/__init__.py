@@ -1,0 +1,259 @@
+"""grouped_expert_gemm_amd — Python binding of libgeg (grouped 4-bit expert GEMM, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/geg.h. torch supplies device
+memory and the current stream. There is no CPU fallback: host tensors are
+refused, and a missing library raises.
+
+    out = gnf4_grouped_gemm(a, sizes, w, absmax)          # NF4 forward
+    out = gmxfp4_grouped_gemm(a, sizes, blocks, scales)   # MXFP4 forward
+    dx  = gnf4_grouped_dgrad(dy, sizes, w, absmax)        # NF4 input gradient
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+__all__ = [
+    "GegError", "Opts", "Workspace", "lib", "header_functions",
+    "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
+    "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
+    "geg_version", "geg_launch_count", "GEG_OP_NF4_FWD", "GEG_OP_MXFP4_FWD", "GEG_OP_NF4_DGRAD",
+    "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgeg.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "geg.h")
+
+GEG_OP_NF4_FWD, GEG_OP_MXFP4_FWD, GEG_OP_NF4_DGRAD = 0, 1, 2
+DEVERR_NEGATIVE_SIZE, DEVERR_SIZES_EXCEED_M, DEVERR_FP16_RANGE = 0x1, 0x2, 0x4
+
+_STATUS = {0: "GEG_OK", 1: "GEG_ERR_NULL_POINTER", 2: "GEG_ERR_BAD_SHAPE", 3: "GEG_ERR_MISALIGNED",
+           4: "GEG_ERR_NOT_DEVICE_MEMORY", 5: "GEG_ERR_WORKSPACE", 6: "GEG_ERR_UNSUPPORTED_DEVICE",
+           7: "GEG_ERR_HIP", 8: "GEG_ERR_BAD_OPTION"}
+
+
+class GegError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+
+
+class Opts(ctypes.Structure):
+    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled; split_k 0 auto / 1..16."""
+    _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgeg.so (built in-tree by grouped_expert_gemm_amd.build)."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"{LIB_PATH} is missing: build it with `python -m grouped_expert_gemm_amd.build` "
+                    "(hipcc, gfx950). There is no fallback implementation.")
+            L = ctypes.CDLL(LIB_PATH)
+            gemm_args = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P, _P]
+            for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad"):
+                f = getattr(L, name)
+                f.argtypes, f.restype = gemm_args, ctypes.c_int
+            L.geg_workspace_bytes.argtypes = [_I32, _I64, _I64, _I64, _I32, _P]
+            L.geg_workspace_bytes.restype = _SZ
+            L.geg_workspace_init.argtypes, L.geg_workspace_init.restype = [_P, _SZ, _P], ctypes.c_int
+            L.geg_read_device_error.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), _P]
+            L.geg_read_device_error.restype = ctypes.c_int
+            for name in ("gnf4_dequant", "gmxfp4_dequant"):
+                f = getattr(L, name)
+                f.argtypes, f.restype = [_P, _P, _P, _P, _P, _I64, _I64, _I32, _P], ctypes.c_int
+            L.gnf4_quantize.argtypes, L.gnf4_quantize.restype = [_P, _P, _P, _I64, _I64, _P], ctypes.c_int
+            L.geg_status_string.argtypes, L.geg_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+            L.geg_last_error.argtypes, L.geg_last_error.restype = [], ctypes.c_char_p
+            L.geg_version.argtypes, L.geg_version.restype = [], ctypes.c_int32
+            L.geg_launch_count.argtypes, L.geg_launch_count.restype = [], ctypes.c_uint64
+            _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of every function declared in include/geg.h."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:geg|gnf4|gmxfp4)_\w+)\s*\(", txt)))
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GegError(status, lib().geg_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and t.device.type != "cuda":
+            raise GegError(4, "tensors must be on the GPU: this library has no CPU path "
+                              "(the CPU oracle under oracle/ is the reference for host data)")
+
+
+def geg_version() -> int:
+    return lib().geg_version()
+
+
+def geg_launch_count() -> int:
+    return lib().geg_launch_count()
+
+
+def geg_workspace_bytes(op, M, N, K, E, opts: Opts | None = None) -> int:
+    return lib().geg_workspace_bytes(op, M, N, K, E, ctypes.byref(opts) if opts else None)
+
+
+class Workspace:
+    """A device workspace (torch-allocated uint8 buffer), zeroed once on creation
+    and grown on demand. One workspace must not be shared by concurrent calls."""
+
+    def __init__(self, nbytes: int = 1 << 20, device=None):
+        import torch
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.buf = None
+        self.ensure(nbytes)
+
+    def ensure(self, nbytes: int, stream=None):
+        import torch
+        nbytes = max(256, (int(nbytes) + 255) & ~255)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            _check(lib().geg_workspace_init(_ptr(self.buf), nbytes, _stream(stream)))
+        return self
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def read_error(self, stream=None) -> int:
+        code = ctypes.c_int32(0)
+        _check(lib().geg_read_device_error(_ptr(self.buf), ctypes.byref(code), _stream(stream)))
+        return code.value
+
+    def reset(self, stream=None):
+        _check(lib().geg_workspace_init(_ptr(self.buf), self.nbytes, _stream(stream)))
+
+
+_default_ws = {}
+
+
+def _workspace(ws, need, device, stream):
+    if ws is None:
+        key = device.index
+        ws = _default_ws.get(key)
+        if ws is None:
+            ws = _default_ws[key] = Workspace(max(need, 1 << 20), device)
+    ws.ensure(need, stream)
+    return ws
+
+
+def _gemm(fn_name, op, a, sizes, wq, scales, out, workspace, opts, stream):
+    import torch
+    _require_gpu(a, sizes, wq, scales, out)
+    M, K = a.shape
+    E, N = wq.shape[0], wq.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    need = geg_workspace_bytes(op, M, N, K, E, opts)
+    ws = _workspace(workspace, need, a.device, stream)
+    f = getattr(lib(), fn_name)
+    _check(f(_ptr(a), _ptr(sizes), _ptr(wq), _ptr(scales), _ptr(out), M, N, K, E,
+             _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None, _stream(stream)))
+    return out
+
+
+def gnf4_grouped_gemm(a, sizes, w, absmax, out=None, workspace: Workspace | None = None,
+                      opts: Opts | None = None, stream=None):
+    """a bf16 [M,K] (rows grouped by expert), sizes int32 [E], w uint8 [E,N,K/2],
+    absmax fp32 [E,N,K/64] -> out bf16 [M,N]."""
+    return _gemm("gnf4_grouped_gemm", GEG_OP_NF4_FWD, a, sizes, w, absmax, out, workspace, opts, stream)
+
+
+def gmxfp4_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace | None = None,
+                        opts: Opts | None = None, stream=None):
+    """a bf16 [M,K], sizes int32 [E], blocks uint8 [E,N,K/2] (or [E,N,K/32,16]),
+    scales uint8 [E,N,K/32] -> out bf16 [M,N]."""
+    if blocks.dim() == 4:
+        blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
+    return _gemm("gmxfp4_grouped_gemm", GEG_OP_MXFP4_FWD, a, sizes, blocks, scales, out, workspace,
+                 opts, stream)
+
+
+def gnf4_grouped_dgrad(dy, sizes, w, absmax, dx=None, workspace: Workspace | None = None,
+                       opts: Opts | None = None, stream=None):
+    """dy bf16 [M,N], w uint8 [E,N,K/2], absmax fp32 [E,N,K/64] -> dx bf16 [M,K]."""
+    import torch
+    _require_gpu(dy, sizes, w, absmax, dx)
+    M, N = dy.shape
+    E, K = w.shape[0], w.shape[2] * 2
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    need = geg_workspace_bytes(GEG_OP_NF4_DGRAD, M, N, K, E, opts)
+    ws = _workspace(workspace, need, dy.device, stream)
+    _check(lib().gnf4_grouped_dgrad(_ptr(dy), _ptr(sizes), _ptr(w), _ptr(absmax), _ptr(dx), M, N, K, E,
+                                    _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None,
+                                    _stream(stream)))
+    return dx
+
+
+def _dequant(fn_name, wq, scales, bf16, f16, stream):
+    import torch
+    _require_gpu(wq, scales)
+    E, N, K = wq.shape[0], wq.shape[1], wq.shape[2] * 2
+    f32 = torch.empty((E, N, K), dtype=torch.float32, device=wq.device)
+    ob = torch.empty((E, N, K), dtype=torch.bfloat16, device=wq.device) if bf16 else None
+    oh = torch.empty((E, N, K), dtype=torch.float16, device=wq.device) if f16 else None
+    _check(getattr(lib(), fn_name)(_ptr(wq), _ptr(scales), _ptr(f32), _ptr(ob), _ptr(oh), N, K, E,
+                                   _stream(stream)))
+    return f32, ob, oh
+
+
+def gnf4_dequant(w, absmax, bf16=True, f16=True, stream=None):
+    """Decode NF4 [E,N,K/2] + [E,N,K/64] to (fp32, bf16|None, fp16|None) [E,N,K]."""
+    return _dequant("gnf4_dequant", w, absmax, bf16, f16, stream)
+
+
+def gmxfp4_dequant(blocks, scales, bf16=True, f16=True, stream=None):
+    """Decode MXFP4 [E,N,K/2] + [E,N,K/32] to (fp32, bf16|None, fp16|None) [E,N,K]."""
+    if blocks.dim() == 4:
+        blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
+    return _dequant("gmxfp4_dequant", blocks, scales, bf16, f16, stream)
+
+
+def gnf4_quantize(w, stream=None):
+    """NF4-pack fp32 weights [..., K] on the GPU -> (codes uint8 [..., K/2], absmax fp32 [..., K/64])."""
+    import torch
+    _require_gpu(w)
+    if w.dtype != torch.float32 or not w.is_contiguous():
+        raise GegError(2, "gnf4_quantize expects a contiguous fp32 tensor")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    codes = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(w.shape[:-1] + (K // 64,), dtype=torch.float32, device=w.device)
+    _check(lib().gnf4_quantize(_ptr(w), _ptr(codes), _ptr(absmax), rows, K, _stream(stream)))
+    return codes, absmax

