@@ -205,7 +205,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     const int64_t n_tiles = (N + geg::kTileN - 1) / geg::kTileN;
     const int64_t tile_experts = std::min<int64_t>(E, M / (std::max<int64_t>(p.thresh, 0) + 1));
     const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + tile_experts) * n_tiles;
-    hipError_t e = geg::launch_tile(fmt, g, persistent_grid(bound, 4), stream);
+    hipError_t e = geg::launch_tile(fmt, g, persistent_grid(bound, 1), stream);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     ++g_launches;
   }

@@ -18,10 +18,9 @@ constexpr int kSkinnyRows = 32;   // activation rows per skinny unit (2 MFMA row
 constexpr int kSkinnyCols = 16;   // weight rows (output columns) per skinny unit
 constexpr int kKStep = 128;       // K per skinny inner step
 
-// Tiled (prefill) path.
-constexpr int kTileM = 128;
-constexpr int kTileN = 128;
-constexpr int kTileK = 64;
+// Tiled (prefill) path: one 256x256 output tile per workgroup at a time.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
 
 struct GemmArgs {
   const uint16_t* a;      // bf16 [M, K]
