@@ -43,6 +43,8 @@ WORKLOADS = {
     "gptoss_down": ("gptoss_down_t2048", "gptoss_down_t1"),
     "mixtral": ("mixtral_w13_t4096", None),
     "mixtral_w2": ("mixtral_w2_t4096", None),
+    "mixtral_dgrad": ("mixtral_dgrad_w13", None),
+    "mixtral_dgrad_w2": ("mixtral_dgrad_w2", None),
 }
 KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "geg.cpp"]
 
@@ -144,7 +146,10 @@ def cpu_baseline(c, seed, budget_s=12.0):
             break
     flops, t_dq, t_mm, used = 0.0, 0.0, 0.0, 0
     t_start = time.perf_counter()
-    for e, (q, s) in packed * 8:
+    i = 0
+    while True:
+        e, (q, s) = packed[i % len(packed)]
+        i += 1
         t0 = time.perf_counter()
         W = oracle.dequant_nf4(q, s) if c.fmt == "nf4" else oracle.dequant_mxfp4(q, s)
         t1 = time.perf_counter()
@@ -202,11 +207,18 @@ def main():
     stack_bytes = codes.numel() + scales.numel() * scales.element_size()
     ncopies = max(1, int(np.ceil(ROTATE_BYTES / stack_bytes)))
     wcopies = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(ncopies - 1)]
-    out = torch.empty((cp.M, cp.N), dtype=torch.bfloat16, device=dev)
     ws = geg.Workspace(1 << 20)
+    if cp.op == "dgrad":
+        dy = torch.from_numpy(synthetic.dgrad_dy_bf16(cp, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+        dx = torch.empty((cp.M, cp.K), dtype=torch.bfloat16, device=dev)
 
-    def prefill(wc):
-        fn(a, sz, wc[0], wc[1], out=out, workspace=ws)
+        def prefill(wc):
+            geg.gnf4_grouped_dgrad(dy, sz, wc[0], wc[1], dx=dx, workspace=ws)
+    else:
+        out = torch.empty((cp.M, cp.N), dtype=torch.bfloat16, device=dev)
+
+        def prefill(wc):
+            fn(a, sz, wc[0], wc[1], out=out, workspace=ws)
 
     dec = None
     if dec_name:
@@ -283,9 +295,10 @@ def main():
             traffic = None
     result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_MFMA_TFLOPS, 1),
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
-                          "traffic": traffic, "kernel": f"grouped tile kernel ({cp.fmt}), {cp.name}",
+                          "traffic": traffic,
+                          "kernel": f"grouped {'dgrad' if cp.op == 'dgrad' else 'tile'} kernel ({cp.fmt}), {cp.name}",
                           "per_launch_gflop": flops / 1e9}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cp.op == "fwd":
         result["cpu_baseline"] = cpu_baseline(cp, args.seed, args.cpu_budget)
     result["kernel_sha"] = kernel_sha()
     print(json.dumps(result), flush=True)

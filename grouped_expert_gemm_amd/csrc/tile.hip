@@ -146,28 +146,39 @@ __device__ __forceinline__ void store_b(const RawStage& r, uint16_t* Bs, int64_t
 
 // One 32-k substep of the wavefront's 128x64 block: 8x4 MFMAs (rows past the
 // expert and columns past N compute on zeros and are never stored).
+// The 64-row halves of the block that hold no row of the expert are skipped
+// (`vrows` = rows of the tile at or past this wavefront's first row; the branch
+// is uniform across the wavefront).
 template <Fmt F>
 __device__ __forceinline__ void mma_substep(const uint16_t* As, const uint16_t* Bs, int s, int wm,
-                                            int wn, int lane, f32x4 (&acc)[8][4]) {
+                                            int wn, int lane, int vrows, f32x4 (&acc)[8][4]) {
   const int r16 = lane & 15;
   const int chunk = 4 * s + (lane >> 4);
   const uint16_t* ap = As + swz(128 * wm + r16, chunk);   // + 16 rows per i
   const uint16_t* bp = Bs + swz(64 * wn + r16, chunk);
-  u32x4 av[8], bv[4];
+  u32x4 bv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bv[j] = *reinterpret_cast<const u32x4*>(bp + 16 * BK * j);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) av[i] = *reinterpret_cast<const u32x4*>(ap + 16 * BK * i);
+  for (int ih = 0; ih < 2; ++ih) {
+    if (vrows > 64 * ih) {
+      u32x4 av[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const u32x4*>(ap + 16 * BK * (4 * ih + i));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<F>(av[i], bv[j], acc[i][j]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * ih + i][j] = mfma16<F>(av[i], bv[j], acc[4 * ih + i][j]);
+    }
+  }
 }
 
 template <Fmt F>
 __device__ __forceinline__ void run_tile(TileLds& L, const GemmArgs& g, const TileSrc& src,
-                                         int wave, int lane, uint32_t& range, f32x4 (&acc)[8][4]) {
+                                         int wave, int lane, int rows, uint32_t& range,
+                                         f32x4 (&acc)[8][4]) {
   const int wm = wave >> 2, wn = wave & 3;
+  const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
   const int64_t K = g.K;
   const int nst = (int)((K + BK - 1) / BK);
   RawStage raw;
@@ -181,12 +192,12 @@ __device__ __forceinline__ void run_tile(TileLds& L, const GemmArgs& g, const Ti
     const bool more = st + 1 < nst;
     const int64_t k1 = (int64_t)(st + 1) * BK;
     if (more) store_a<F>(raw, L.a[cur ^ 1], k1, K, wave, lane, range);
-    mma_substep<F>(L.a[cur], L.b[cur], 0, wm, wn, lane, acc);
+    mma_substep<F>(L.a[cur], L.b[cur], 0, wm, wn, lane, vrows, acc);
     if (more) {
       store_b<F>(raw, L.b[cur ^ 1], k1, K);
       if (st + 2 < nst) load_raw<F>(raw, src, K, (int64_t)(st + 2) * BK);
     }
-    mma_substep<F>(L.a[cur], L.b[cur], 1, wm, wn, lane, acc);
+    mma_substep<F>(L.a[cur], L.b[cur], 1, wm, wn, lane, vrows, acc);
     __syncthreads();
   }
 }
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const TileSrc src = tile_src<F>(g, e, row0, rows, n0, wave, lane);
-    run_tile<F>(L, g, src, wave, lane, range, acc);
+    run_tile<F>(L, g, src, wave, lane, rows, range, acc);
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores
