@@ -80,6 +80,7 @@ struct Plan {
   int64_t rc_bound;        // bound on skinny row chunks
   size_t counters_off, counters_bytes;
   size_t partials_off, partials_bytes;
+  size_t a16_off, a16_bytes;   // NF4 tile path: fp16 copy of the activations
   size_t total_bytes;
 };
 
@@ -135,6 +136,13 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     }
   }
   p.total_bytes = kHeader + p.counters_bytes + p.partials_bytes;
+  if (p.run_tile && op == GEG_OP_NF4_FWD) {
+    // Never inside the counter region, even when this call has no split-K: a
+    // later split-K call on the same workspace expects its counters at zero.
+    p.a16_off = kHeader + kCounterBytes + p.partials_bytes;
+    p.a16_bytes = round256((size_t)M * (size_t)K * 2);
+    p.total_bytes = p.a16_off + p.a16_bytes;
+  }
   return GEG_OK;
 }
 
@@ -200,8 +208,14 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.err = reinterpret_cast<uint32_t*>(wsb);
   g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
+  g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
 
   if (p.run_tile) {
+    if (fmt == geg::NF4) {
+      hipError_t e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * K, g.err, stream);
+      if (e != hipSuccess) return hip_fail(e, "activation conversion launch");
+      ++g_launches;
+    }
     const int64_t n_tiles = (N + geg::kTileN - 1) / geg::kTileN;
     const int64_t tile_experts = std::min<int64_t>(E, M / (std::max<int64_t>(p.thresh, 0) + 1));
     const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + tile_experts) * n_tiles;
@@ -293,7 +307,9 @@ geg_status geg_workspace_init(void* workspace, size_t workspace_bytes, hipStream
   geg_status st;
   if ((st = check_device()) != GEG_OK) return st;
   if ((st = check_device_ptr(workspace, "workspace")) != GEG_OK) return st;
-  hipError_t e = geg::launch_zero(workspace, workspace_bytes & ~size_t(3), stream);
+  // Only the error word and the split-K counters must start at zero.
+  const size_t zero_bytes = std::min(workspace_bytes, kHeader + kCounterBytes) & ~size_t(3);
+  hipError_t e = geg::launch_zero(workspace, zero_bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "workspace zero launch");
   ++g_launches;
   return GEG_OK;

@@ -24,6 +24,7 @@ constexpr int kTileN = 256;
 
 struct GemmArgs {
   const uint16_t* a;      // bf16 [M, K]
+  const uint16_t* a16;    // NF4 tile path: the same activations as fp16 in NF4 slot order
   const int32_t* sizes;   // [E]
   const uint8_t* wq;      // packed codes [E, N, K/2]
   const void* scales;     // NF4: fp32 [E, N, K/64]; MXFP4: u8 [E, N, K/32]
@@ -58,5 +59,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float*
 hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,
                                int64_t K, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_to_f16_slots(const uint16_t* a, uint16_t* a16, int64_t elems, uint32_t* err,
+                               hipStream_t s);
 
 }  // namespace geg

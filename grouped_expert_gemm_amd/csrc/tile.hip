@@ -2,19 +2,21 @@
 //
 // One persistent launch walks every 256x256 output tile of every expert that has
 // more rows than the skinny path takes. Per 64-wide K stage a workgroup stages
-// its activation tile (NF4: converted to fp16) and decodes its 256 weight rows
-// once into LDS — codes through the 16-value table, times the block scale — so
-// the decode is shared by all four wavefronts and all 256 rows of the tile
+// its activation tile (NF4: from the fp16 copy a prior pass made) and decodes
+// its 256 weight rows once into LDS: codes through the 16-value table, times the
+// block scale, so the decode is shared by all 256 rows of the tile
 // ("grouped-nf4-gemm 0.33.1", opening description: table decode in registers,
 // blockwise scaling, fp32 accumulation, bf16 epilogue, no dequantised copy of an
-// expert in memory). Eight wavefronts (two per SIMD, so one's decode VALU work
-// overlaps the other's MFMAs) each own a 128x64 block of the tile and run 8x4
-// 16x16x32 MFMAs per 32 k with their accumulators in AGPRs.
+// expert in memory). Eight wavefronts (two per SIMD) each own a 128x64 block of
+// the tile and run 8x4 16x16x32 MFMAs per 32 k.
 //
-// Pipeline: LDS holds two stages. While the MFMAs of stage s read one buffer, the
-// raw loads of stage s+1 (already in registers) are converted/decoded into the
-// other buffer and the loads of stage s+2 are issued, so one barrier per stage
-// separates writers and readers and global latency is hidden behind a stage.
+// Pipeline: LDS holds two stages. A stage runs as 16 groups of 4 MFMAs; each
+// group also issues one LDS operand read three groups ahead and one slice of the
+// next stage's staging work (activation rows into the other buffer, or weight
+// decode), so LDS latency and VALU work hide under the MFMAs. Raw activations
+// are loaded one stage ahead and raw codes two stages ahead, into registers. A
+// barrier after the staging groups publishes the next buffer, which lets the
+// last groups read the next stage's first operands early.
 // LDS rows are 128 B (64 halves) with the 16-byte chunk index XOR-swizzled by
 // the row, which makes both the row-wise stores and the MFMA operand reads
 // (16 rows, one chunk each) free of bank conflicts.
@@ -90,7 +92,8 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& g, int e, int64_t ro
                                             int64_t n0, int wave, int lane) {
   const int64_t K = g.K;
   TileSrc t;
-  t.a = g.a + row0 * K;
+  // NF4 reads the fp16 copy of the activations (already in the NF4 slot order).
+  t.a = (F == NF4 ? g.a16 : g.a) + row0 * K;
   t.na = clamp_bytes((int64_t)rows * K * 2);
   const int64_t nrows = min<int64_t>(BN, g.N - n0);
   const int64_t wrow0 = (int64_t)e * g.N + n0;
@@ -136,15 +139,15 @@ __device__ __forceinline__ void load_b(RawB& r, const TileSrc& t, int64_t k0, bo
     r.s = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, t.s_off, (uint32_t)(k0 >> 5), 0));
 }
 
-// One row chunk of raw activations -> LDS (NF4: fp16 in the NF4 slot order;
-// k past K is 0).
+// One row chunk of raw activations -> LDS (k past K is 0; only MXFP4 can have a
+// 32-wide K tail).
 template <Fmt F>
 __device__ __forceinline__ void store_a_piece(const RawA& r, int i, uint16_t* As, int64_t k0,
-                                              int64_t K, int wave, int lane, uint32_t& range) {
+                                              int64_t K, int wave, int lane) {
   const int chunk = lane & 7;
   const int row = 32 * wave + 8 * i + (lane >> 3);
-  u32x4 v = k0 + 8 * chunk < K ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
-  if constexpr (F == NF4) v = bf16x8_to_f16_slots(v, range);
+  u32x4 v = r.v[i];
+  if constexpr (F == MXFP4) v = k0 + 8 * chunk < K ? v : u32x4{0u, 0u, 0u, 0u};
   *reinterpret_cast<u32x4*>(&As[swz(row, chunk)]) = v;
 }
 
@@ -205,7 +208,7 @@ struct Ops {
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
 template <Fmt F, int H, int P>
 __device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64_t K, int st,
-                                           int nst, int wave, int lane, uint32_t& range,
+                                           int nst, int wave, int lane,
                                            RawA& ra, RawB (&rb)[2], Ops& ops,
                                            f32x4 (&acc)[8][4], uint32_t aoff, uint32_t boff) {
   const int cur = st & 1, nxt = cur ^ 1;
@@ -235,7 +238,7 @@ __device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64
     // On the last stage the pieces write stale data into the free buffer, which
     // nothing reads; this keeps the group free of branches.
     if (g < 4) {
-      store_a_piece<F>(ra, g, L.a[nxt], k1, K, wave, lane, range);
+      store_a_piece<F>(ra, g, L.a[nxt], k1, K, wave, lane);
       if (g == 3) load_a(ra, src, K, (int64_t)(st + 2) * BK, st + 2 < nst);
     } else {
       if (g == 4) dec = b_setup<F>(rb[P ^ 1], k1, K);
@@ -271,7 +274,7 @@ __device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64
 // halves; every wavefront runs the same barriers whatever its H).
 template <Fmt F, int H>
 __device__ __forceinline__ void run_tile_h(TileLds& L, const TileSrc& src, int64_t K, int wave,
-                                           int lane, uint32_t& range, f32x4 (&acc)[8][4]) {
+                                           int lane, f32x4 (&acc)[8][4]) {
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
@@ -286,7 +289,7 @@ __device__ __forceinline__ void run_tile_h(TileLds& L, const TileSrc& src, int64
   load_b<F>(rb[0], src, 0, true);
   load_b<F>(rb[1], src, BK, nst > 1);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_a_piece<F>(ra, q, L.a[0], 0, K, wave, lane, range);
+  for (int q = 0; q < 4; ++q) store_a_piece<F>(ra, q, L.a[0], 0, K, wave, lane);
   {
     const BDec<F> d = b_setup<F>(rb[0], 0, K);
 #pragma unroll
@@ -302,9 +305,9 @@ __device__ __forceinline__ void run_tile_h(TileLds& L, const TileSrc& src, int64
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
   for (int st = 0; st < nst; st += 2) {
-    tile_stage<F, H, 0>(L, src, K, st, nst, wave, lane, range, ra, rb, ops, acc, aoff, boff);
+    tile_stage<F, H, 0>(L, src, K, st, nst, wave, lane, ra, rb, ops, acc, aoff, boff);
     if (st + 1 < nst)
-      tile_stage<F, H, 1>(L, src, K, st + 1, nst, wave, lane, range, ra, rb, ops, acc, aoff, boff);
+      tile_stage<F, H, 1>(L, src, K, st + 1, nst, wave, lane, ra, rb, ops, acc, aoff, boff);
   }
 }
 
@@ -323,7 +326,6 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  uint32_t range = 0;
 
   // XCD-aware order: round r hands XCD x the tiles r*G + x*(G/8) .. + G/8 - 1.
   const int G = gridDim.x;
@@ -350,11 +352,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     const TileSrc src = tile_src<F>(g, e, row0, rows, n0, wave, lane);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, 2>(L, src, g.K, wave, lane, range, acc);
+      run_tile_h<F, 2>(L, src, g.K, wave, lane, acc);
     else if (vrows > 0)
-      run_tile_h<F, 1>(L, src, g.K, wave, lane, range, acc);
+      run_tile_h<F, 1>(L, src, g.K, wave, lane, acc);
     else
-      run_tile_h<F, 0>(L, src, g.K, wave, lane, range, acc);
+      run_tile_h<F, 0>(L, src, g.K, wave, lane, acc);
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores
@@ -393,9 +395,6 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       }
     }
     __syncthreads();  // the stage buffers are reused by the next tile
-  }
-  if constexpr (F == NF4) {
-    if (range_overflowed(range)) atomicOr(g.err, kErrFp16Range);
   }
 }
 

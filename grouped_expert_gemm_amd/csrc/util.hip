@@ -122,6 +122,20 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(uint32_t* __restrict__ p
     p[i] = 0u;
 }
 
+// bf16 activations -> fp16 in the NF4 slot order, 8 elements (16 bytes) per step.
+// The NF4 MFMA consumes fp16 activations; converting them once here, instead of
+// in every output-column tile that reads them, leaves the tile kernel a plain
+// copy. An element that overflows fp16 sets the range bit of the error word.
+__global__ __launch_bounds__(kThreads) void to_f16_kernel(const u32x4* __restrict__ a,
+                                                          u32x4* __restrict__ a16, int64_t chunks,
+                                                          uint32_t* __restrict__ err) {
+  uint32_t range = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks;
+       i += (int64_t)gridDim.x * kThreads)
+    a16[i] = bf16x8_to_f16_slots(a[i], range);
+  if (range_overflowed(range)) atomicOr(err, kErrFp16Range);
+}
+
 int grid_for(int64_t work) {
   int64_t g = (work + kThreads - 1) / kThreads;
   return (int)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
@@ -145,6 +159,16 @@ hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, in
                                int64_t K, hipStream_t s) {
   hipLaunchKernelGGL(quantize_nf4_kernel, dim3(grid_for(rows * (K >> 6))), dim3(kThreads), 0, s,
                      w, codes, absmax, rows, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f16_slots(const uint16_t* a, uint16_t* a16, int64_t elems, uint32_t* err,
+                               hipStream_t s) {
+  const int64_t chunks = elems >> 3;
+  int64_t g = (chunks + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > 2048 ? 2048 : g);
+  hipLaunchKernelGGL(to_f16_kernel, dim3((int)g), dim3(kThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(a), reinterpret_cast<u32x4*>(a16), chunks, err);
   return hipGetLastError();
 }
 

@@ -48,8 +48,10 @@
  *    geg_workspace_bytes(...) bytes, 256-byte aligned, zeroed once by
  *    geg_workspace_init before its first use. It holds the device error word,
  *    split-K arrival counters (a fixed 4 MiB region, left zeroed by every
- *    completed call) and split-K partials; calls on one workspace must be
- *    ordered (same stream); concurrent calls must not share one.
+ *    completed call), split-K partials and, for the NF4 tiled path, an fp16
+ *    copy of the activations (M * K * 2 bytes, rewritten by every call); calls
+ *    on one workspace must be ordered (same stream); concurrent calls must not
+ *    share one.
  */
 #ifndef GEG_H_
 #define GEG_H_

@@ -80,8 +80,11 @@ def test_small_workspace_is_refused():
 
 
 def test_workspace_sizes():
-    # prefill: no split-K, only the 256-byte header (error word)
-    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == 256
+    # NF4 prefill: the 256-byte header (error word), the split-K counter region
+    # (kept clear of other data) and the fp16 copy of the activations that the
+    # tiled path reads; MXFP4 reads bf16 activations as given
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == 256 + (4 << 20) + 16384 * 2048 * 2
+    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == 256
     one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 1))
     four = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 4))
