@@ -102,7 +102,11 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
   std::memset(&p, 0, sizeof(p));
   p.split = 1;
   if (op == GEG_OP_NF4_DGRAD) {
-    p.total_bytes = kHeader;
+    // dY as fp16 for the tiled kernel, outside the counter region
+    p.run_tile = M > 0;
+    p.a16_off = kHeader + kCounterBytes;
+    p.a16_bytes = round256((size_t)M * (size_t)N * 2);
+    p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
   p.thresh = force == 1 ? INT32_MAX : (force == 2 ? 0 : geg::kSkinnyRows);
@@ -273,20 +277,28 @@ geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_
   for (auto [ptr, name] : {std::pair<const void*, const char*>{dy, "dy"}, {sizes, "sizes"},
                            {w, "w"}, {absmax, "absmax"}, {dx, "dx"}, {workspace, "workspace"}})
     if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
-  geg::DgradArgs g;
-  g.dy = reinterpret_cast<const uint16_t*>(dy);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  geg::GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.a = reinterpret_cast<const uint16_t*>(dy);
+  g.a16 = reinterpret_cast<const uint16_t*>(wsb + p.a16_off);
   g.sizes = sizes;
   g.wq = w;
-  g.absmax = absmax;
-  g.dx = reinterpret_cast<uint16_t*>(dx);
+  g.scales = absmax;
+  g.out = reinterpret_cast<uint16_t*>(dx);
   g.M = M;
   g.N = N;
   g.K = K;
   g.E = E;
-  g.err = reinterpret_cast<uint32_t*>(workspace);
-  const int64_t k_tiles = (K + 127) / 128;
-  const int64_t bound = ((M + 127) / 128 + std::min<int64_t>(E, M)) * k_tiles;
-  hipError_t e = geg::launch_dgrad(g, persistent_grid(bound, 4), stream);
+  g.thresh = 0;   // every expert with rows goes through the tiled kernel
+  g.split = 1;
+  g.err = reinterpret_cast<uint32_t*>(wsb);
+  hipError_t e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * N, g.err, stream);
+  if (e != hipSuccess) return hip_fail(e, "dY conversion launch");
+  ++g_launches;
+  const int64_t k_tiles = (K + geg::kTileN - 1) / geg::kTileN;
+  const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + std::min<int64_t>(E, M)) * k_tiles;
+  e = geg::launch_tile_dgrad(g, persistent_grid(bound, 1), stream);
   if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
   ++g_launches;
   return GEG_OK;

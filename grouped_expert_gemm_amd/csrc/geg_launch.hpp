@@ -25,6 +25,7 @@ constexpr int kTileN = 256;
 struct GemmArgs {
   const uint16_t* a;      // bf16 [M, K]
   const uint16_t* a16;    // NF4 tile path: the same activations as fp16 in NF4 slot order
+                          // (dgrad: dY [M, N] as fp16 in NF4 slot order)
   const int32_t* sizes;   // [E]
   const uint8_t* wq;      // packed codes [E, N, K/2]
   const void* scales;     // NF4: fp32 [E, N, K/64]; MXFP4: u8 [E, N, K/32]
@@ -39,21 +40,10 @@ struct GemmArgs {
   float* partials;        // split-K partials [split, M, N]
 };
 
-struct DgradArgs {
-  const uint16_t* dy;     // bf16 [M, N]
-  const int32_t* sizes;
-  const uint8_t* wq;      // NF4 codes [E, N, K/2]
-  const float* absmax;    // [E, N, K/64]
-  uint16_t* dx;           // bf16 [M, K]
-  int64_t M, N, K;
-  int32_t E;
-  uint32_t* err;
-};
-
 // Each launcher returns the hipError_t of its launch.
 hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
-hipError_t launch_dgrad(const DgradArgs& g, int grid, hipStream_t s);
+hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,
                           uint16_t* bf16, uint16_t* f16, int64_t rows, int64_t K, hipStream_t s);
 hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,

@@ -38,11 +38,17 @@ constexpr int kXcds = 8;
 constexpr int kTileThreads = 512;
 constexpr int kTileWaves = kTileThreads / 64;
 constexpr int kEpiLd = 64 + 8;  // epilogue row stride in halves (144 B)
+constexpr int kLdT = 80;        // dgrad weight rows in LDS: 64 halves + 16 pad (160 B)
 
+// LDS of one workgroup: two stages of activation and weight tiles, or the
+// epilogue's result blocks. The dgrad weight tile is written transposed (one
+// contraction index per lane, scattered over 256 rows), so its rows are padded
+// instead of swizzled (a 160-byte stride keeps the operand reads conflict-free).
+template <bool DG>
 union TileLds {
   struct {
     uint16_t a[2][BM * BK];
-    uint16_t b[2][BN * BK];
+    uint16_t b[2][BN * (DG ? kLdT : BK)];
   };
   uint16_t epi[kTileWaves][128 * kEpiLd];  // per-wavefront bf16 result block
 };
@@ -59,6 +65,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * BK + ((chunk ^ (row & 7)) << 3);
 }
 
+// Weight-tile offset of (row, chunk): swizzled rows for the forward pass, padded
+// rows for dgrad.
+template <bool DG>
+__device__ __forceinline__ int bpos(int row, int chunk) {
+  return DG ? row * kLdT + chunk * 8 : swz(row, chunk);
+}
+
 // Where a tile's operands come from. Loads go through buffer resources whose
 // record count bounds every access: rows past the expert's last row and weight
 // rows past N read as zeros, and a load switched off (count 0) reads nothing.
@@ -67,9 +80,12 @@ struct TileSrc {
   const void* w;              // packed codes of the tile's weight rows
   const void* s;              // their scales
   int32_t na, nw, ns;         // bytes readable from each
-  uint32_t a_off;             // this lane's activation byte offset (row, chunk) at k = 0
-  uint32_t w_off;             // this thread's code byte offset (row t/2, half t%2) at k = 0
-  uint32_t s_off;             // this thread's scale-row byte offset at k = 0
+  uint32_t a_off;             // this lane's activation byte offset (row, chunk) at stage 0
+  uint32_t a_rows8;           // bytes between activation rows 8 apart
+  uint32_t w_off;             // this thread's code byte offset at stage 0
+  uint32_t w_step;            // code bytes per stage
+  uint32_t s_off;             // this thread's scale byte offset at stage 0
+  uint32_t s_step;            // scale bytes per stage
 };
 
 __device__ __forceinline__ int32_t clamp_bytes(int64_t bytes) {
@@ -87,29 +103,50 @@ struct RawB {
   float s;         // NF4: absmax of the row's 64-block; MXFP4: e8m0 byte of the 32-block
 };
 
-template <Fmt F>
+// Operand sources of the tile (expert e, rows row0.., output columns o0..).
+// Forward: out = A . W^T contracts over K; thread t stages codes of weight row t/2
+// (32 k per stage half t%2). dgrad: dX = dY . W contracts over N; thread t stages
+// weight row n = t%64 of the stage's 64, columns o0 + 32 (t/64) .. +32.
+template <Fmt F, bool DG>
 __device__ __forceinline__ TileSrc tile_src(const GemmArgs& g, int e, int64_t row0, int rows,
-                                            int64_t n0, int wave, int lane) {
-  const int64_t K = g.K;
+                                            int64_t o0, int wave, int lane) {
+  const int64_t K = g.K, N = g.N;
+  const int64_t C = DG ? N : K;   // contraction length = activation row length
   TileSrc t;
   // NF4 reads the fp16 copy of the activations (already in the NF4 slot order).
-  t.a = (F == NF4 ? g.a16 : g.a) + row0 * K;
-  t.na = clamp_bytes((int64_t)rows * K * 2);
-  const int64_t nrows = min<int64_t>(BN, g.N - n0);
-  const int64_t wrow0 = (int64_t)e * g.N + n0;
-  t.w = g.wq + wrow0 * (K >> 1);
-  t.nw = clamp_bytes(nrows * (K >> 1));
-  if constexpr (F == NF4) {
-    t.s = reinterpret_cast<const float*>(g.scales) + wrow0 * (K >> 6);
-    t.ns = clamp_bytes(nrows * (K >> 6) * 4);
-  } else {
-    t.s = reinterpret_cast<const uint8_t*>(g.scales) + wrow0 * (K >> 5);
-    t.ns = clamp_bytes(nrows * (K >> 5));
-  }
+  t.a = (F == NF4 ? g.a16 : g.a) + row0 * C;
+  t.na = clamp_bytes((int64_t)rows * C * 2);
+  t.a_off = (uint32_t)(((32 * wave + (lane >> 3)) * C + 8 * (lane & 7)) * 2);
+  t.a_rows8 = (uint32_t)(8 * C * 2);
   const int tid = threadIdx.x;
-  t.a_off = (uint32_t)(((32 * wave + (lane >> 3)) * K + 8 * (lane & 7)) * 2);
-  t.w_off = (uint32_t)((tid >> 1) * (K >> 1) + 16 * (tid & 1));
-  t.s_off = (uint32_t)(F == NF4 ? (tid >> 1) * (K >> 6) * 4 : (tid >> 1) * (K >> 5) + (tid & 1));
+  if constexpr (DG) {
+    t.w = g.wq + (int64_t)e * N * (K >> 1);
+    t.nw = clamp_bytes(N * (K >> 1));
+    t.s = reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6);
+    t.ns = clamp_bytes(N * (K >> 6) * 4);
+    const int n = tid & 63, kc = tid >> 6;
+    const int64_t kcol = o0 + 32 * kc;    // past K: never stored
+    t.w_off = (uint32_t)(n * (K >> 1) + (kcol >> 1));
+    t.w_step = (uint32_t)(BK * (K >> 1));
+    t.s_off = (uint32_t)((n * (K >> 6) + (kcol >> 6)) * 4);
+    t.s_step = (uint32_t)(BK * (K >> 6) * 4);
+  } else {
+    const int64_t nrows = min<int64_t>(BN, N - o0);
+    const int64_t wrow0 = (int64_t)e * N + o0;
+    t.w = g.wq + wrow0 * (K >> 1);
+    t.nw = clamp_bytes(nrows * (K >> 1));
+    if constexpr (F == NF4) {
+      t.s = reinterpret_cast<const float*>(g.scales) + wrow0 * (K >> 6);
+      t.ns = clamp_bytes(nrows * (K >> 6) * 4);
+    } else {
+      t.s = reinterpret_cast<const uint8_t*>(g.scales) + wrow0 * (K >> 5);
+      t.ns = clamp_bytes(nrows * (K >> 5));
+    }
+    t.w_off = (uint32_t)((tid >> 1) * (K >> 1) + 16 * (tid & 1));
+    t.w_step = BK / 2;
+    t.s_off = (uint32_t)(F == NF4 ? (tid >> 1) * (K >> 6) * 4 : (tid >> 1) * (K >> 5) + (tid & 1));
+    t.s_step = F == NF4 ? 4 : 2;
+  }
   return t;
 }
 
@@ -117,41 +154,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_on(const void* base, int3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, on ? n : 0, 0x00020000);
 }
 
-// Activations, coalesced: 8 lanes cover one row's 128 bytes; piece i holds rows
-// 8 i + lane/8 of the wavefront's 32.
-__device__ __forceinline__ void load_a_piece(RawA& r, int i, const TileSrc& t, int64_t K,
-                                             int64_t k0, bool on) {
-  r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_on(t.a, t.na, on), t.a_off,
-                                                 (uint32_t)(k0 * 2) + (uint32_t)(i * 16 * K), 0);
-}
-__device__ __forceinline__ void load_a(RawA& r, const TileSrc& t, int64_t K, int64_t k0, bool on) {
+// Activations of stage st, coalesced: 8 lanes cover one row's 128 bytes; piece
+// i holds rows 8 i + lane/8 of the wavefront's 32.
+__device__ __forceinline__ void load_a(RawA& r, const TileSrc& t, int st, bool on) {
+  const __amdgpu_buffer_rsrc_t R = rsrc_on(t.a, t.na, on);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_a_piece(r, i, t, K, k0, on);
+  for (int i = 0; i < 4; ++i)
+    r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(R, t.a_off, (uint32_t)st * (BK * 2) + (uint32_t)i * t.a_rows8, 0);
 }
 
 template <Fmt F>
-__device__ __forceinline__ void load_b(RawB& r, const TileSrc& t, int64_t k0, bool on) {
-  r.c = __builtin_amdgcn_raw_buffer_load_b128(rsrc_on(t.w, t.nw, on), t.w_off, (uint32_t)(k0 >> 1), 0);
+__device__ __forceinline__ void load_b(RawB& r, const TileSrc& t, int st, bool on) {
+  r.c = __builtin_amdgcn_raw_buffer_load_b128(rsrc_on(t.w, t.nw, on), t.w_off, (uint32_t)st * t.w_step, 0);
   const __amdgpu_buffer_rsrc_t S = rsrc_on(t.s, t.ns, on);
   if constexpr (F == NF4)
-    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(S, t.s_off, (uint32_t)((k0 >> 6) * 4), 0));
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(S, t.s_off, (uint32_t)st * t.s_step, 0));
   else
-    r.s = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, t.s_off, (uint32_t)(k0 >> 5), 0));
+    r.s = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, t.s_off, (uint32_t)st * t.s_step, 0));
 }
 
-// One row chunk of raw activations -> LDS (k past K is 0; only MXFP4 can have a
-// 32-wide K tail).
-template <Fmt F>
+// One row chunk of raw activations -> LDS. Chunks past the contraction length
+// C are zeroed (NF4 forward has C % 64 == 0; MXFP4 can have a 32-wide tail and
+// dgrad an 8-aligned one).
+template <Fmt F, bool DG>
 __device__ __forceinline__ void store_a_piece(const RawA& r, int i, uint16_t* As, int64_t k0,
-                                              int64_t K, int wave, int lane) {
+                                              int64_t C, int wave, int lane) {
   const int chunk = lane & 7;
   const int row = 32 * wave + 8 * i + (lane >> 3);
   u32x4 v = r.v[i];
-  if constexpr (F == MXFP4) v = k0 + 8 * chunk < K ? v : u32x4{0u, 0u, 0u, 0u};
+  if constexpr (F == MXFP4 || DG) v = k0 + 8 * chunk < C ? v : u32x4{0u, 0u, 0u, 0u};
   *reinterpret_cast<u32x4*>(&As[swz(row, chunk)]) = v;
 }
 
-// Per-stage decode state of a thread's weight row piece: the NF4 table scaled by
+// Per-stage decode state of a thread's weight piece: the NF4 table scaled by
 // the block's absmax, or the MXFP4 block scale (0 for a 32-wide piece past K).
 template <Fmt F> struct BDec;
 template <> struct BDec<NF4> { Lut16 lut; };
@@ -169,16 +204,33 @@ __device__ __forceinline__ BDec<F> b_setup(const RawB& r, int64_t k0, int64_t K)
   return d;
 }
 
-// Eight codes of the thread's piece -> decoded weights in LDS (row t/2, chunk
-// 4 (t%2) + q).
-template <Fmt F>
-__device__ __forceinline__ void store_b_piece(const RawB& r, const BDec<F>& d, int q, uint16_t* Bs) {
+// NF4 slot of contraction offset j (0..7) within an 8-chunk: the activations of
+// the NF4 path are stored in slot order [0, 2, 4, 6, 1, 3, 5, 7].
+__device__ __forceinline__ int nf4_slot(int j) { return (j >> 1) | ((j & 1) << 2); }
+
+// Eight codes of the thread's piece q -> decoded weights in LDS.
+// Forward: row t/2, chunk 4 (t%2) + q, one 16-byte store (slot order).
+// dgrad: the 8 codes are columns k = 32 (t/64) + 8 q + j of weight row n = t%64;
+// each value goes to LDS row k at the slot of n (2-byte stores; `bcol` is the
+// thread's column offset).
+template <Fmt F, bool DG>
+__device__ __forceinline__ void store_b_piece(const RawB& r, const BDec<F>& d, int q, uint16_t* Bs,
+                                              int bcol) {
   const int t = threadIdx.x;
-  const int row = t >> 1, c = 4 * (t & 1) + q;
-  if constexpr (F == NF4)
-    *reinterpret_cast<u32x4*>(&Bs[swz(row, c)]) = nf4_decode8(d.lut, r.c[q]);
-  else
-    *reinterpret_cast<u32x4*>(&Bs[swz(row, c)]) = mxfp4_decode8(r.c[q], d.sc);
+  if constexpr (DG) {
+    const u32x4 v = nf4_decode8(d.lut, r.c[q]);   // halves: k = 0, 2, 4, 6, 1, 3, 5, 7
+    uint16_t* p = Bs + (32 * (t >> 6) + 8 * q) * kLdT + bcol;
+    constexpr int kk[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      p[kk[h] * kLdT] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+  } else {
+    const int row = t >> 1, c = 4 * (t & 1) + q;
+    if constexpr (F == NF4)
+      *reinterpret_cast<u32x4*>(&Bs[swz(row, c)]) = nf4_decode8(d.lut, r.c[q]);
+    else
+      *reinterpret_cast<u32x4*>(&Bs[swz(row, c)]) = mxfp4_decode8(r.c[q], d.sc);
+  }
 }
 
 __device__ __forceinline__ u32x4 lds_frag(const uint16_t* p) {
@@ -206,18 +258,20 @@ struct Ops {
 // after group 7 publishes the next stage's buffer, which lets groups 12-15 read
 // its first operands ahead; barrier X at the end frees the current buffer.
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
-template <Fmt F, int H, int P>
-__device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64_t K, int st,
-                                           int nst, int wave, int lane,
+template <Fmt F, bool DG, int H, int P>
+__device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
+                                           int st, int nst, int wave, int lane, int bcol,
                                            RawA& ra, RawB (&rb)[2], Ops& ops,
                                            f32x4 (&acc)[8][4], uint32_t aoff, uint32_t boff) {
   const int cur = st & 1, nxt = cur ^ 1;
   const int64_t k1 = (int64_t)(st + 1) * BK;
   // Substep 1 reads chunk 4 + c where substep 0 reads chunk c: the swizzled
-  // chunk differs in bit 2, i.e. the half offset differs in bit 5.
+  // chunk differs in bit 2, i.e. the half offset differs in bit 5 (the padded
+  // dgrad weight rows are plainly 32 halves further).
   const uint16_t* A0 = L.a[cur] + aoff;
   const uint16_t* A1 = L.a[cur] + (aoff ^ 32u);
-  const uint16_t* B1 = L.b[cur] + (boff ^ 32u);
+  const uint16_t* B1 = L.b[cur] + (DG ? boff + 32u : boff ^ 32u);
+  constexpr int BR = 16 * (DG ? kLdT : BK);   // B fragment stride (16 rows)
   constexpr int NI = 4 * H;   // A fragments per substep
   u32x4 af[8];
   u32x4 b1[4];
@@ -231,19 +285,19 @@ __device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64
     if (g + 3 < NI) af[g + 3] = lds_frag(A0 + 16 * BK * (g + 3));
     if (g == 4 && NI > 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b1[j] = lds_frag(B1 + 16 * BK * j);
+      for (int j = 0; j < 4; ++j) b1[j] = lds_frag(B1 + BR * j);
     }
     if (g >= 5 && g - 5 < 3 && g - 5 < NI) af[g - 5] = lds_frag(A1 + 16 * BK * (g - 5));
     if (g < NI) mfma_row<F>(g < 3 ? ops.a[g] : af[g], ops.b, acc[g]);
     // On the last stage the pieces write stale data into the free buffer, which
     // nothing reads; this keeps the group free of branches.
     if (g < 4) {
-      store_a_piece<F>(ra, g, L.a[nxt], k1, K, wave, lane);
-      if (g == 3) load_a(ra, src, K, (int64_t)(st + 2) * BK, st + 2 < nst);
+      store_a_piece<F, DG>(ra, g, L.a[nxt], k1, C, wave, lane);
+      if (g == 3) load_a(ra, src, st + 2, st + 2 < nst);
     } else {
       if (g == 4) dec = b_setup<F>(rb[P ^ 1], k1, K);
-      store_b_piece<F>(rb[P ^ 1], dec, g - 4, L.b[nxt]);
-      if (g == 7) load_b<F>(rb[P ^ 1], src, (int64_t)(st + 3) * BK, st + 3 < nst);
+      store_b_piece<F, DG>(rb[P ^ 1], dec, g - 4, L.b[nxt], bcol);
+      if (g == 7) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -257,7 +311,7 @@ __device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64
     if (NI > 0) {
       if (g == 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(Bn + 16 * BK * j);
+        for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(Bn + BR * j);
       }
       if (g >= 5 && g - 5 < 3 && g - 5 < NI) ops.a[g - 5] = lds_frag(An + 16 * BK * (g - 5));
     }
@@ -272,51 +326,57 @@ __device__ __forceinline__ void tile_stage(TileLds& L, const TileSrc& src, int64
 
 // Main loop over the K stages of one tile (H = the wavefront's active 64-row
 // halves; every wavefront runs the same barriers whatever its H).
-template <Fmt F, int H>
-__device__ __forceinline__ void run_tile_h(TileLds& L, const TileSrc& src, int64_t K, int wave,
-                                           int lane, f32x4 (&acc)[8][4]) {
+template <Fmt F, bool DG, int H>
+__device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
+                                           int wave, int lane, f32x4 (&acc)[8][4]) {
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
-  const uint32_t boff = (uint32_t)swz(64 * wn + r16, lane >> 4);
-  const int nst = (int)((K + BK - 1) / BK);
+  const uint32_t boff = (uint32_t)bpos<DG>(64 * wn + r16, lane >> 4);
+  const int bcol = ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7);   // dgrad staging column
+  constexpr int BR = 16 * (DG ? kLdT : BK);
+  const int nst = (int)((C + BK - 1) / BK);
   RawA ra;
   RawB rb[2];
   Ops ops;
   // Prologue: stage 0 into buffer 0; raw data of stages 1 (activations) and
   // 1, 2 (codes) in flight.
-  load_a(ra, src, K, 0, true);
+  load_a(ra, src, 0, true);
   load_b<F>(rb[0], src, 0, true);
-  load_b<F>(rb[1], src, BK, nst > 1);
+  load_b<F>(rb[1], src, 1, nst > 1);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_a_piece<F>(ra, q, L.a[0], 0, K, wave, lane);
+  for (int q = 0; q < 4; ++q) store_a_piece<F, DG>(ra, q, L.a[0], 0, C, wave, lane);
   {
     const BDec<F> d = b_setup<F>(rb[0], 0, K);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_b_piece<F>(rb[0], d, q, L.b[0]);
+    for (int q = 0; q < 4; ++q) store_b_piece<F, DG>(rb[0], d, q, L.b[0], bcol);
   }
-  load_a(ra, src, K, BK, nst > 1);
-  load_b<F>(rb[0], src, 2 * BK, nst > 2);
+  load_a(ra, src, 1, nst > 1);
+  load_b<F>(rb[0], src, 2, nst > 2);
   __syncthreads();
   if constexpr (H > 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(L.b[0] + boff + 16 * BK * j);
+    for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(L.b[0] + boff + BR * j);
 #pragma unroll
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
   for (int st = 0; st < nst; st += 2) {
-    tile_stage<F, H, 0>(L, src, K, st, nst, wave, lane, ra, rb, ops, acc, aoff, boff);
+    tile_stage<F, DG, H, 0>(L, src, C, K, st, nst, wave, lane, bcol, ra, rb, ops, acc, aoff, boff);
     if (st + 1 < nst)
-      tile_stage<F, H, 1>(L, src, K, st + 1, nst, wave, lane, ra, rb, ops, acc, aoff, boff);
+      tile_stage<F, DG, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, ops, acc, aoff, boff);
   }
 }
 
-template <Fmt F>
+// Forward (DG = false): out[M, N] = a . W^T per expert. dgrad (DG = true, NF4):
+// out[M, K] = dY . W per expert, with `a16` holding dY as fp16.
+template <Fmt F, bool DG>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   __shared__ Plan plan;
-  __shared__ __attribute__((aligned(16))) TileLds L;
+  __shared__ __attribute__((aligned(16))) TileLds<DG> L;
 
-  const int n_tiles = (int)((g.N + BN - 1) / BN);
+  const int64_t C = DG ? g.N : g.K;   // contraction length
+  const int64_t O = DG ? g.K : g.N;   // output width
+  const int n_tiles = (int)((O + BN - 1) / BN);
   const int32_t thresh = g.thresh;
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
     if (s <= thresh) return 0;
@@ -349,14 +409,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const TileSrc src = tile_src<F>(g, e, row0, rows, n0, wave, lane);
+    const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, 2>(L, src, g.K, wave, lane, acc);
+      run_tile_h<F, DG, 2>(L, src, C, g.K, wave, lane, acc);
     else if (vrows > 0)
-      run_tile_h<F, 1>(L, src, g.K, wave, lane, acc);
+      run_tile_h<F, DG, 1>(L, src, C, g.K, wave, lane, acc);
     else
-      run_tile_h<F, 0>(L, src, g.K, wave, lane, acc);
+      run_tile_h<F, DG, 0>(L, src, C, g.K, wave, lane, acc);
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores
@@ -377,19 +437,19 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     {
       const int chunk = lane & 7;
       const int64_t col = n0 + 64 * wn + 8 * chunk;
-      const bool vec = (g.N & 7) == 0 && col + 8 <= g.N;
+      const bool vec = (O & 7) == 0 && col + 8 <= O;
       const uint16_t* src = E + (lane >> 3) * kEpiLd + 8 * chunk;
       for (int rr = 0; rr < 128; rr += 8) {
         const int lr = 128 * wm + rr + (lane >> 3);
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + rr * kEpiLd);
         if (lr < rows) {
-          uint16_t* dst = g.out + (row0 + lr) * g.N + col;
+          uint16_t* dst = g.out + (row0 + lr) * O + col;
           if (vec) {
             *reinterpret_cast<u32x4*>(dst) = v;
           } else {
 #pragma unroll
             for (int x = 0; x < 8; ++x)
-              if (col + x < g.N) dst[x] = (uint16_t)(v[x >> 1] >> (16 * (x & 1)));
+              if (col + x < O) dst[x] = (uint16_t)(v[x >> 1] >> (16 * (x & 1)));
           }
         }
       }
@@ -402,9 +462,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
   if (fmt == NF4)
-    hipLaunchKernelGGL(tile_kernel<NF4>, dim3(grid), dim3(kTileThreads), 0, s, g);
+    hipLaunchKernelGGL((tile_kernel<NF4, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
   else
-    hipLaunchKernelGGL(tile_kernel<MXFP4>, dim3(grid), dim3(kTileThreads), 0, s, g);
+    hipLaunchKernelGGL((tile_kernel<MXFP4, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((tile_kernel<NF4, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
   return hipGetLastError();
 }
 

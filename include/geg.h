@@ -49,7 +49,8 @@
  *    geg_workspace_init before its first use. It holds the device error word,
  *    split-K arrival counters (a fixed 4 MiB region, left zeroed by every
  *    completed call), split-K partials and, for the NF4 tiled path, an fp16
- *    copy of the activations (M * K * 2 bytes, rewritten by every call); calls
+ *    copy of the activations (M * K * 2 bytes; dgrad: of dY, M * N * 2 bytes;
+ *    rewritten by every call); calls
  *    on one workspace must be ordered (same stream); concurrent calls must not
  *    share one.
  */

@@ -85,7 +85,7 @@ def test_workspace_sizes():
     # tiled path reads; MXFP4 reads bf16 activations as given
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == 256 + (4 << 20) + 16384 * 2048 * 2
     assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
-    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == 256
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == 256 + (4 << 20) + 8192 * 28672 * 2
     one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 1))
     four = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 4))
     assert one == 256 and four >= 256 + 4 * 8 * 2048 * 4

@@ -221,6 +221,19 @@ def test_dgrad_small(geg):
     assert_close(bf16_to_f64(dx), ref, "dgrad small")
 
 
+def test_dgrad_medium_ragged(geg):
+    # two row blocks for one expert, a K that ends inside an output tile, and an
+    # N (the contraction) that ends 8 into its last 64-wide stage
+    log("case: dgrad medium ragged")
+    c, d = custom_case("nf4", 5, 448, 200, [0, 300, 3, 0, 70], seed=9)
+    rng = np.random.default_rng(10)
+    dy = synthetic.f32_to_bf16_bits(rng.standard_normal((373, 200)).astype(np.float32))
+    g = upload_case(d)
+    dx = geg.gnf4_grouped_dgrad(up_u16_as_bf16(dy), g["sizes"], g["w"], g["s"])
+    ref = oracle.dgrad_ref(dy, d["sizes"], C.weight_fn(d), c.K)
+    assert_close(bf16_to_f64(dx), ref, "dgrad medium")
+
+
 def test_graph_capture_replays(geg):
     import torch
     log("case: hip graph capture of decode + prefill calls, 3 replays")
