@@ -97,17 +97,30 @@ __device__ __forceinline__ float nf4_times(int i, float scale) {
   return v;
 }
 
+// Half h (entries 8h .. 8h+7) of the table of fp16 T[i] * scale (fp32 product,
+// one rounding to nearest even): fills lo[2h], lo[2h+1], hi[2h], hi[2h+1].
+__device__ __forceinline__ void nf4_scaled_lut_half(float scale, int h, Lut16& t) {
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 v;
+    v[0] = (_Float16)nf4_times(8 * h + 2 * i, scale);
+    v[1] = (_Float16)nf4_times(8 * h + 2 * i + 1, scale);
+    p[i] = __builtin_bit_cast(uint32_t, v);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    t.lo[2 * h + q] = perm(p[2 * q + 1], p[2 * q], 0x06040200u);
+    t.hi[2 * h + q] = perm(p[2 * q + 1], p[2 * q], 0x07050301u);
+  }
+}
+
 // fp16 of T[i] * scale for i = 0..15 (fp32 product, one rounding to nearest even).
 __device__ __forceinline__ Lut16 nf4_scaled_lut(float scale) {
-  uint32_t p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f16x2 h;
-    h[0] = (_Float16)nf4_times(2 * i, scale);
-    h[1] = (_Float16)nf4_times(2 * i + 1, scale);
-    p[i] = __builtin_bit_cast(uint32_t, h);
-  }
-  return lut_from_pairs(p);
+  Lut16 t;
+  nf4_scaled_lut_half(scale, 0, t);
+  nf4_scaled_lut_half(scale, 1, t);
+  return t;
 }
 
 // Look up four 4-bit indices (one per byte): s7 = idx & 7 per byte and
@@ -123,21 +136,28 @@ __device__ __forceinline__ void lut_lookup4(const Lut16& t, uint32_t s7, uint32_
 // high nibble and k = 2b+1 in its low nibble) into 8 fp16 values in the slot
 // order k = [0, 2, 4, 6, 1, 3, 5, 7] (the NF4 slot order): out[0] = {k0, k2},
 // out[1] = {k4, k6}, out[2] = {k1, k3}, out[3] = {k5, k7}.
-__device__ __forceinline__ u32x4 nf4_decode8(const Lut16& t, uint32_t x) {
-  const uint32_t xs = x >> 4;
-  const uint32_t s7e = xs & 0x07070707u;
+// The even-k half of nf4_decode8: {k0, k2}, {k4, k6} (high nibbles).
+__device__ __forceinline__ u32x2 nf4_decode8_even(const Lut16& t, uint32_t x) {
+  const uint32_t s7e = (x >> 4) & 0x07070707u;
   const uint32_t sele = ((x >> 5) & 0x04040404u) | 0x03020100u;
+  uint32_t lo, hi;
+  lut_lookup4(t, s7e, sele, lo, hi);
+  return u32x2{perm(hi, lo, 0x05010400u), perm(hi, lo, 0x07030602u)};
+}
+
+// The odd-k half of nf4_decode8: {k1, k3}, {k5, k7} (low nibbles).
+__device__ __forceinline__ u32x2 nf4_decode8_odd(const Lut16& t, uint32_t x) {
   const uint32_t s7o = x & 0x07070707u;
   const uint32_t selo = ((x >> 1) & 0x04040404u) | 0x03020100u;
-  uint32_t loe, hie, loo, hio;
-  lut_lookup4(t, s7e, sele, loe, hie);
-  lut_lookup4(t, s7o, selo, loo, hio);
-  u32x4 r;
-  r[0] = perm(hie, loe, 0x05010400u);
-  r[1] = perm(hie, loe, 0x07030602u);
-  r[2] = perm(hio, loo, 0x05010400u);
-  r[3] = perm(hio, loo, 0x07030602u);
-  return r;
+  uint32_t lo, hi;
+  lut_lookup4(t, s7o, selo, lo, hi);
+  return u32x2{perm(hi, lo, 0x05010400u), perm(hi, lo, 0x07030602u)};
+}
+
+__device__ __forceinline__ u32x4 nf4_decode8(const Lut16& t, uint32_t x) {
+  const u32x2 e = nf4_decode8_even(t, x);
+  const u32x2 o = nf4_decode8_odd(t, x);
+  return u32x4{e[0], e[1], o[0], o[1]};
 }
 
 // ------------------------------------------------------------------ MXFP4 decode

@@ -192,44 +192,59 @@ template <Fmt F> struct BDec;
 template <> struct BDec<NF4> { Lut16 lut; };
 template <> struct BDec<MXFP4> { float sc; };
 
+// Decode state setup, in two halves so that it spreads over two MFMA groups
+// (NF4: the scaled table's entries 0-7, then 8-15; MXFP4: the block scale).
 template <Fmt F>
-__device__ __forceinline__ BDec<F> b_setup(const RawB& r, int64_t k0, int64_t K) {
-  BDec<F> d;
+__device__ __forceinline__ void b_setup(BDec<F>& d, int h, const RawB& r, int64_t k0, int64_t K) {
   if constexpr (F == NF4) {
-    d.lut = nf4_scaled_lut(r.s);
-  } else {
+    nf4_scaled_lut_half(r.s, h, d.lut);
+  } else if (h == 1) {
     const bool ok = k0 + 32 * (threadIdx.x & 1) < K;
     d.sc = ok ? e8m0_to_f32(__builtin_bit_cast(uint32_t, r.s)) : 0.f;
   }
-  return d;
 }
 
 // NF4 slot of contraction offset j (0..7) within an 8-chunk: the activations of
 // the NF4 path are stored in slot order [0, 2, 4, 6, 1, 3, 5, 7].
 __device__ __forceinline__ int nf4_slot(int j) { return (j >> 1) | ((j & 1) << 2); }
 
-// Eight codes of the thread's piece q -> decoded weights in LDS.
-// Forward: row t/2, chunk 4 (t%2) + q, one 16-byte store (slot order).
-// dgrad: the 8 codes are columns k = 32 (t/64) + 8 q + j of weight row n = t%64;
-// each value goes to LDS row k at the slot of n (2-byte stores; `bcol` is the
-// thread's column offset).
+// Eight codes of the thread's piece q -> decoded weights in LDS, in two halves
+// (even k, then odd k) that run in consecutive MFMA groups.
+// Forward: row t/2, chunk 4 (t%2) + q, one 16-byte store (slot order) by the
+// odd half. dgrad: the codes are columns k = 32 (t/64) + 8 q + j of weight row
+// n = t%64; each value goes to LDS row k at the slot of n (2-byte stores; `bcol`
+// is the thread's column offset).
 template <Fmt F, bool DG>
-__device__ __forceinline__ void store_b_piece(const RawB& r, const BDec<F>& d, int q, uint16_t* Bs,
+__device__ __forceinline__ u32x2 b_piece_even(const RawB& r, const BDec<F>& d, int q, uint16_t* Bs,
                                               int bcol) {
-  const int t = threadIdx.x;
-  if constexpr (DG) {
-    const u32x4 v = nf4_decode8(d.lut, r.c[q]);   // halves: k = 0, 2, 4, 6, 1, 3, 5, 7
-    uint16_t* p = Bs + (32 * (t >> 6) + 8 * q) * kLdT + bcol;
-    constexpr int kk[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+  if constexpr (F == NF4) {
+    const u32x2 v = nf4_decode8_even(d.lut, r.c[q]);   // k = 0, 2 | 4, 6
+    if constexpr (DG) {
+      uint16_t* p = Bs + (32 * (threadIdx.x >> 6) + 8 * q) * kLdT + bcol;
 #pragma unroll
-    for (int h = 0; h < 8; ++h)
-      p[kk[h] * kLdT] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+      for (int h = 0; h < 4; ++h) p[2 * h * kLdT] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+    }
+    return v;
   } else {
-    const int row = t >> 1, c = 4 * (t & 1) + q;
-    if constexpr (F == NF4)
-      *reinterpret_cast<u32x4*>(&Bs[swz(row, c)]) = nf4_decode8(d.lut, r.c[q]);
-    else
-      *reinterpret_cast<u32x4*>(&Bs[swz(row, c)]) = mxfp4_decode8(r.c[q], d.sc);
+    return u32x2{0u, 0u};
+  }
+}
+
+template <Fmt F, bool DG>
+__device__ __forceinline__ void b_piece_odd(const RawB& r, const BDec<F>& d, int q, u32x2 even,
+                                            uint16_t* Bs, int bcol) {
+  const int t = threadIdx.x;
+  if constexpr (F == NF4) {
+    const u32x2 v = nf4_decode8_odd(d.lut, r.c[q]);    // k = 1, 3 | 5, 7
+    if constexpr (DG) {
+      uint16_t* p = Bs + (32 * (t >> 6) + 8 * q) * kLdT + bcol;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) p[(2 * h + 1) * kLdT] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+    } else {
+      *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = u32x4{even[0], even[1], v[0], v[1]};
+    }
+  } else {
+    *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = mxfp4_decode8(r.c[q], d.sc);
   }
 }
 
@@ -251,12 +266,15 @@ struct Ops {
   u32x4 a[3];
 };
 
-// One 64-k stage of the tile's main loop, in 16 groups of (up to) 4 MFMAs. Each
+// One 64-k stage of the tile's main loop, in 16 groups of (up to) 4 MFMAs:
+// groups 0-7 run substep 0 (k 0..31 of the stage), groups 8-15 substep 1. Each
 // group issues one LDS operand read three groups ahead of its use and one slice
-// of the next stage's staging work (groups 0-3: activation rows, 4-7: weight
-// decode), so that LDS latency and the VALU work overlap the MFMAs. Barrier Y
-// after group 7 publishes the next stage's buffer, which lets groups 12-15 read
-// its first operands ahead; barrier X at the end frees the current buffer.
+// of the next stage's staging work, so that LDS latency and VALU work overlap
+// the MFMAs: groups 0-3 store activation rows into the other buffer, groups 2-3
+// build the decode table, groups 4-11 decode and store the weights (half a
+// piece of 8 codes each). Barrier Y after group 11 publishes the next stage's
+// buffer, which lets groups 12-15 read its first operands ahead; barrier X at
+// the end frees the current buffer.
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
 template <Fmt F, bool DG, int H, int P>
 __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
@@ -271,56 +289,56 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
   const uint16_t* A0 = L.a[cur] + aoff;
   const uint16_t* A1 = L.a[cur] + (aoff ^ 32u);
   const uint16_t* B1 = L.b[cur] + (DG ? boff + 32u : boff ^ 32u);
+  const uint16_t* An = L.a[nxt] + aoff;
+  const uint16_t* Bn = L.b[nxt] + boff;
   constexpr int BR = 16 * (DG ? kLdT : BK);   // B fragment stride (16 rows)
-  constexpr int NI = 4 * H;   // A fragments per substep
-  u32x4 af[8];
+  constexpr int NI = 4 * H;                   // A fragments per substep
+  u32x4 af[16];      // A fragment of group g (substep g / 8, rows 16 (g % 8))
   u32x4 b1[4];
   BDec<F> dec;
+  u32x2 half;
 #pragma unroll
   for (int i = 0; i < 3; ++i) af[i] = ops.a[i];
 
-  // ---- substep 0 (groups 0-7), staging the next stage into the other buffer
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g + 3 < NI) af[g + 3] = lds_frag(A0 + 16 * BK * (g + 3));
-    if (g == 4 && NI > 0) {
+  for (int g = 0; g < 16; ++g) {
+    const int sub = g >> 3, i = g & 7;
+    // operand reads: A fragment of group g + 3 (if it has MFMAs), B of substep 1
+    // at group 4, the next stage's first operands after barrier Y
+    {
+      const int g3 = g + 3, i3 = g3 & 7;
+      if (g3 < 16 && i3 < NI) af[g3] = lds_frag((g3 < 8 ? A0 : A1) + 16 * BK * i3);
+    }
+    if (NI > 0 && g == 4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) b1[j] = lds_frag(B1 + BR * j);
     }
-    if (g >= 5 && g - 5 < 3 && g - 5 < NI) af[g - 5] = lds_frag(A1 + 16 * BK * (g - 5));
-    if (g < NI) mfma_row<F>(g < 3 ? ops.a[g] : af[g], ops.b, acc[g]);
-    // On the last stage the pieces write stale data into the free buffer, which
-    // nothing reads; this keeps the group free of branches.
+    if (NI > 0 && g == 12) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(Bn + BR * j);
+    }
+    if (g >= 13 && g - 13 < NI) ops.a[g - 13] = lds_frag(An + 16 * BK * (g - 13));
+    if (i < NI) mfma_row<F>(af[g], sub ? b1 : ops.b, acc[i]);
+    // staging of the next stage (on the last stage it writes stale data into the
+    // free buffer, which nothing reads; this keeps the groups free of branches)
     if (g < 4) {
       store_a_piece<F, DG>(ra, g, L.a[nxt], k1, C, wave, lane);
       if (g == 3) load_a(ra, src, st + 2, st + 2 < nst);
-    } else {
-      if (g == 4) dec = b_setup<F>(rb[P ^ 1], k1, K);
-      store_b_piece<F, DG>(rb[P ^ 1], dec, g - 4, L.b[nxt], bcol);
-      if (g == 7) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();   // Y: the next stage's buffer is complete
-  // ---- substep 1 (groups 8-15), reading the next stage's first operands ahead
-  const uint16_t* An = L.a[nxt] + aoff;
-  const uint16_t* Bn = L.b[nxt] + boff;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g + 3 < NI) af[(g + 3) & 7] = lds_frag(A1 + 16 * BK * (g + 3));
-    if (NI > 0) {
-      if (g == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(Bn + BR * j);
+    if (g == 2 || g == 3) b_setup<F>(dec, g - 2, rb[P ^ 1], k1, K);
+    if (g >= 4 && g < 12) {
+      const int q = (g - 4) >> 1;
+      if ((g & 1) == 0) {
+        half = b_piece_even<F, DG>(rb[P ^ 1], dec, q, L.b[nxt], bcol);
+      } else {
+        b_piece_odd<F, DG>(rb[P ^ 1], dec, q, half, L.b[nxt], bcol);
+        if (g == 11) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
       }
-      if (g >= 5 && g - 5 < 3 && g - 5 < NI) ops.a[g - 5] = lds_frag(An + 16 * BK * (g - 5));
     }
-    if (g < NI) mfma_row<F>(af[g], b1, acc[g]);
+    if (g == 11) __syncthreads();   // Y: the next stage's buffer is complete
     __builtin_amdgcn_sched_barrier(0);
   }
-  // X: every wavefront is done with the current buffer. Its reads have all
-  // completed (their MFMAs consumed them), so the barrier need not wait for the
-  // next stage's operand reads still in flight.
+  // X: every wavefront is done with the current buffer.
   __syncthreads();
 }
 
@@ -347,9 +365,14 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_a_piece<F, DG>(ra, q, L.a[0], 0, C, wave, lane);
   {
-    const BDec<F> d = b_setup<F>(rb[0], 0, K);
+    BDec<F> d;
+    b_setup<F>(d, 0, rb[0], 0, K);
+    b_setup<F>(d, 1, rb[0], 0, K);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_b_piece<F, DG>(rb[0], d, q, L.b[0], bcol);
+    for (int q = 0; q < 4; ++q) {
+      const u32x2 e = b_piece_even<F, DG>(rb[0], d, q, L.b[0], bcol);
+      b_piece_odd<F, DG>(rb[0], d, q, e, L.b[0], bcol);
+    }
   }
   load_a(ra, src, 1, nst > 1);
   load_b<F>(rb[0], src, 2, nst > 2);
