@@ -61,6 +61,7 @@ template <Fmt F, int CB, int D>
 __device__ __forceinline__ void load_group(Group<F, CB, D>& r, const GemmArgs& g, int e,
                                            int64_t n0, int kg, int first_step, int nsteps) {
   const int64_t K = g.K;
+  const bool pair_scales = (K & 127) == 0 && (reinterpret_cast<uintptr_t>(g.scales) & 7) == 0;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     if (i < nsteps) {
@@ -78,8 +79,17 @@ __device__ __forceinline__ void load_group(Group<F, CB, D>& r, const GemmArgs& g
           const u32x2 pa = *reinterpret_cast<const u32x2*>(wrow + ((k0 + 16 * kg) >> 1));
           const u32x2 pb = *reinterpret_cast<const u32x2*>(wrow + ((kb + 16 * kg) >> 1));
           r.code[i][cb] = u32x4{pa[0], pa[1], pb[0], pb[1]};
-          r.scale[i][cb][0] = srow[k0 >> 6];
-          r.scale[i][cb][1] = srow[kb >> 6];
+          if (pair_scales) {
+            // both absmax of the step in one 8-byte load (k0 / 64 is even and the
+            // scale rows are 8-byte aligned)
+            const u32x2 sv = *reinterpret_cast<const u32x2*>(srow + (k0 >> 6));
+            const uint32_t s0 = sv.x, s1 = sv.y;   // scalar copies before the bit casts
+            r.scale[i][cb][0] = __builtin_bit_cast(float, s0);
+            r.scale[i][cb][1] = __builtin_bit_cast(float, s1);
+          } else {
+            r.scale[i][cb][0] = srow[k0 >> 6];
+            r.scale[i][cb][1] = srow[kb >> 6];
+          }
         } else {
           const int64_t ka = k0 + 32 * kg;
           const int64_t kc = ka < K ? ka : K - 32;
@@ -182,38 +192,48 @@ __device__ __forceinline__ void unit_k_loop(const GemmArgs& g, const Lut16& lut,
 
   for (int c0 = step_begin; c0 < step_end; c0 += chunk_steps) {
     const int csteps = min(chunk_steps, step_end - c0);
-    // This wavefront's steps of the chunk: c0 + wave + 4i, in groups of D. The
-    // first group's weight loads go out before the activations are staged.
+    // This wavefront's steps of the chunk: c0 + wave + 4i, in groups of D.
     const int my_steps = csteps > wave ? (csteps - wave + kWaves - 1) / kWaves : 0;
+    // Activations [r8 rows (rows >= `rows` are zero), k in this chunk], 8 per
+    // group, AB loads per thread in flight together.
+    constexpr int AB = F == NF4 ? 8 : 4;
+    const int64_t kbase = (int64_t)c0 * kKStep;
+    const int gpr = csteps * (kKStep / 8);  // 8-element groups per row
+    const int ngroups = r8 * gpr;
+    u32x4 av[AB];
+    auto a_load = [&](int q0) {
+#pragma unroll
+      for (int b = 0; b < AB; ++b) {
+        const int q = q0 + b * kThreads;
+        const int rr = q / gpr;
+        const int64_t k = kbase + (q % gpr) * 8;
+        av[b] = u32x4{0u, 0u, 0u, 0u};
+        if (q < ngroups && rr < rows && k < g.K)
+          av[b] = *reinterpret_cast<const u32x4*>(g.a + (row0 + rr) * g.K + k);
+      }
+    };
+    auto a_store = [&](int q0) {
+#pragma unroll
+      for (int b = 0; b < AB; ++b) {
+        const int q = q0 + b * kThreads;
+        if (q < ngroups) {
+          u32x4 v = av[b];
+          if constexpr (F == NF4) v = bf16x8_to_f16_slots(v, range);
+          *reinterpret_cast<u32x4*>(&As[(q / gpr) * ld + (q % gpr) * 8]) = v;
+        }
+      }
+    };
+    // (NF4 issues its first activation loads ahead of the weights; for MXFP4 the
+    // extra live registers cost more occupancy than the overlap gains.)
+    if constexpr (F == NF4) a_load(threadIdx.x);
     Group<F, CB, D> b0, b1;
     load_group<F, CB, D>(b0, g, e, n0, kg, c0 + wave, min(D, my_steps));
     __syncthreads();  // LDS reads of the previous chunk are done
-    {
-      // Stage activations [rows, k in this chunk]: batches of 4 loads per
-      // thread are in flight together before they are converted and stored.
-      const int64_t kbase = (int64_t)c0 * kKStep;
-      const int gpr = csteps * (kKStep / 8);  // 8-element groups per row
-      const int ngroups = r8 * gpr;
-      for (int q0 = threadIdx.x; q0 < ngroups; q0 += 4 * kThreads) {
-        u32x4 v[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int q = q0 + b * kThreads;
-          const int rr = q / gpr;
-          const int64_t k = kbase + (q % gpr) * 8;
-          v[b] = u32x4{0u, 0u, 0u, 0u};
-          if (q < ngroups && rr < rows && k < g.K)
-            v[b] = *reinterpret_cast<const u32x4*>(g.a + (row0 + rr) * g.K + k);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int q = q0 + b * kThreads;
-          if (q < ngroups) {
-            if constexpr (F == NF4) v[b] = bf16x8_to_f16_slots(v[b], range);
-            *reinterpret_cast<u32x4*>(&As[(q / gpr) * ld + (q % gpr) * 8]) = v[b];
-          }
-        }
-      }
+    if constexpr (F != NF4) a_load(threadIdx.x);
+    a_store(threadIdx.x);
+    for (int q0 = threadIdx.x + AB * kThreads; q0 < ngroups; q0 += AB * kThreads) {
+      a_load(q0);
+      a_store(q0);
     }
     __syncthreads();
     // Two register buffers alternate: the next group's loads are in flight while
