@@ -9,12 +9,17 @@ HBM before timing; weight stacks rotate over enough copies (>2 GiB) that no
 launch finds its weights in the 256 MB Infinity Cache.
 
 Prints ONE JSON line:
-  value      prefill TFLOP/s (2*M*N*K over routed rows / prefill call time)
-  decode     packed-weight GB/s of the decode call (codes + absmax of touched experts)
-  roofline   prefill kernel vs the dense fp16/bf16 MFMA peak (2516.6 TFLOP/s)
-  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same prefill
+  value      prefill TFLOP/s (2*M*N*K over routed rows / prefill call time); for
+             the decode-only workloads (qwen3_t64, qwen3_down_t64) the decode
+             call's packed-weight GB/s
+  decode     packed-weight GB/s of the decode call (codes + scales of touched experts)
+  roofline   the dominant kernel (tiled/dgrad kernel; skinny kernel for decode-only
+             workloads) against its bound: algorithmic flops (or packed-weight
+             bytes) per launch over the kernel's own time, from the two HIP events
+             the library records around it on the launch stream
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same case
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload olmoe|qwen3|gptoss|mixtral]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -45,6 +50,9 @@ WORKLOADS = {
     "mixtral_w2": ("mixtral_w2_t4096", None),
     "mixtral_dgrad": ("mixtral_dgrad_w13", None),
     "mixtral_dgrad_w2": ("mixtral_dgrad_w2", None),
+    # decode-class only (no prefill leg): value is packed-weight GB/s
+    "qwen3_t64": (None, "qwen3_gate_up_t64"),
+    "qwen3_down_t64": (None, "qwen3_down_t64"),
 }
 KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "geg.cpp"]
 
@@ -126,9 +134,27 @@ def time_calls(fn, copies, steps, warmup, torch, use_graph=True):
     return [a.elapsed_time(b) for a, b in ev], "eager events"
 
 
-def cpu_baseline(c, seed, budget_s=12.0):
+def time_kernel(fn, copies, steps, warmup, geg, torch, slot, force_path=0):
+    """Average device time (ms) of one kernel of the call, from the two HIP events
+    the library records on the launch stream right before and after that kernel
+    (slot 0: tiled or dgrad kernel, slot 1: skinny kernel). The calls run back to
+    back with one event pair each; all are read after a final synchronisation."""
+    for i in range(warmup):
+        fn(copies[i % len(copies)], None)
+    torch.cuda.synchronize()
+    timers = [geg.KernelTimer(force_path) for _ in range(steps)]
+    for i in range(steps):
+        fn(copies[i % len(copies)], timers[i].opts())
+    torch.cuda.synchronize()
+    ms = [t.elapsed_ms()[slot] for t in timers]
+    ms = [m for m in ms if m is not None]
+    return float(np.mean(ms)) if ms else None
+
+
+def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s"):
     """The fp64 oracle (decode each expert to fp64, one matmul per expert) on as
-    many of the prefill's experts as fit in about budget_s seconds (at least one)."""
+    many of the case's experts as fit in about budget_s seconds (at least one),
+    as TFLOP/s or, for decode-class cases, packed-weight GB/s."""
     import oracle
     import synthetic
     from oracle import cases as C
@@ -144,7 +170,7 @@ def cpu_baseline(c, seed, budget_s=12.0):
             packed.append((e, synthetic.mxfp4_bytes(c, seed, e)))
         if len(packed) >= 32:
             break
-    flops, t_dq, t_mm, used = 0.0, 0.0, 0.0, 0
+    flops, wbytes, t_dq, t_mm, used = 0.0, 0, 0.0, 0.0, 0
     t_start = time.perf_counter()
     i = 0
     while True:
@@ -159,6 +185,7 @@ def cpu_baseline(c, seed, budget_s=12.0):
         t_dq += t1 - t0
         t_mm += t2 - t1
         flops += 2.0 * len(rows) * c.N * c.K
+        wbytes += c.N * c.K // 2 + (c.N * (c.K // 64) * 4 if c.fmt == "nf4" else c.N * (c.K // 32))
         used += 1
         del W, out
         if time.perf_counter() - t_start > budget_s:
@@ -169,7 +196,8 @@ def cpu_baseline(c, seed, budget_s=12.0):
         threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0]) or os.cpu_count()
     except Exception:
         threads = os.cpu_count()
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    value = flops / secs / 1e12 if unit == "TFLOP/s" else wbytes / secs / 1e9
+    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
             "sample": f"{c.name}: {used} expert GEMMs (cycling over the first {len(packed)} of "
                       f"{int(np.count_nonzero(sizes))} routed experts, {int(flops / 2 / c.N / c.K)} rows), "
                       "fp64 decode + numpy matmul",
@@ -186,6 +214,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (3 times): the "
+                         "reference kernel that scales the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -194,31 +225,44 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4,
+                          "copy_calibration_bytes_written": dst.numel() * 4}), flush=True)
+        return
     import grouped_expert_gemm_amd as geg
     import synthetic
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     pre_name, dec_name = WORKLOADS[args.workload]
-    cp = synthetic.case(pre_name)
+    cp = synthetic.case(pre_name or dec_name)
     fn = geg.gnf4_grouped_gemm if cp.fmt == "nf4" else geg.gmxfp4_grouped_gemm
 
+    # The weight stack of the workload (the decode leg uses the same experts).
     a, sz, sizes, codes, scales = make_inputs(cp, args.seed, torch, geg, dev)
     stack_bytes = codes.numel() + scales.numel() * scales.element_size()
     ncopies = max(1, int(np.ceil(ROTATE_BYTES / stack_bytes)))
     wcopies = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(ncopies - 1)]
-    ws = geg.Workspace(1 << 20)
-    if cp.op == "dgrad":
-        dy = torch.from_numpy(synthetic.dgrad_dy_bf16(cp, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
-        dx = torch.empty((cp.M, cp.K), dtype=torch.bfloat16, device=dev)
 
-        def prefill(wc):
-            geg.gnf4_grouped_dgrad(dy, sz, wc[0], wc[1], dx=dx, workspace=ws)
-    else:
-        out = torch.empty((cp.M, cp.N), dtype=torch.bfloat16, device=dev)
+    prefill = None
+    if pre_name:
+        ws = geg.Workspace(1 << 20)
+        if cp.op == "dgrad":
+            dy = torch.from_numpy(synthetic.dgrad_dy_bf16(cp, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+            dx = torch.empty((cp.M, cp.K), dtype=torch.bfloat16, device=dev)
 
-        def prefill(wc):
-            fn(a, sz, wc[0], wc[1], out=out, workspace=ws)
+            def prefill(wc, opts=None):
+                geg.gnf4_grouped_dgrad(dy, sz, wc[0], wc[1], dx=dx, workspace=ws, opts=opts)
+        else:
+            out = torch.empty((cp.M, cp.N), dtype=torch.bfloat16, device=dev)
+
+            def prefill(wc, opts=None):
+                fn(a, sz, wc[0], wc[1], out=out, workspace=ws, opts=opts)
 
     dec = None
     if dec_name:
@@ -229,77 +273,101 @@ def main():
         dout = torch.empty((cd.M, cd.N), dtype=torch.bfloat16, device=dev)
         dws = geg.Workspace(geg.geg_workspace_bytes(0 if cd.fmt == "nf4" else 1, cd.M, cd.N, cd.K, cd.E))
 
-        def decode(wc):
-            fn(da, dsz, wc[0], wc[1], out=dout, workspace=dws)
+        def decode(wc, opts=None):
+            fn(da, dsz, wc[0], wc[1], out=dout, workspace=dws, opts=opts)
         dec = (cd, dsizes, decode)
 
-    # correctness gate before timing: device error word clean
-    prefill(wcopies[0])
+    # correctness gate before timing: device error words clean
+    if prefill:
+        prefill(wcopies[0])
     if dec:
         dec[2](wcopies[0])
     torch.cuda.synchronize()
-    assert ws.read_error() == 0, "device error word set"
+    if prefill:
+        assert ws.read_error() == 0, "device error word set"
+    if dec:
+        assert dws.read_error() == 0, "device error word set (decode)"
 
     # ---- timed region: K steps of (prefill + decode), whole-step wall clock
-    for i in range(args.warmup):
-        prefill(wcopies[i % ncopies])
+    def step(i):
+        if prefill:
+            prefill(wcopies[i % ncopies])
         if dec:
             dec[2](wcopies[i % ncopies])
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        prefill(wcopies[i % ncopies])
-        if dec:
-            dec[2](wcopies[i % ncopies])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # ---- per-call event timing on the launch stream
-    pre_ms, pre_how = time_calls(prefill, wcopies, args.steps, args.warmup, torch)
-    flops = 2.0 * cp.M * cp.N * cp.K
-    pre_avg = float(np.mean(pre_ms))
-    tflops = flops / (pre_avg * 1e-3) / 1e12
     result = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC, "value": None, "unit": None, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16" if cp.fmt == "nf4" else "bf16", "data": "synthetic",
-        "config": {"workload": f"{cp.name}" + (f" + {dec[0].name}" if dec else ""),
-                   "format": cp.fmt, "E": cp.E, "K": cp.K, "N": cp.N, "prefill_rows": cp.M,
+        "config": {"workload": " + ".join(x for x in (pre_name, dec_name) if x),
+                   "format": cp.fmt, "E": cp.E, "K": cp.K, "N": cp.N,
+                   "prefill_rows": cp.M if pre_name else 0,
                    "decode_rows": dec[0].M if dec else 0, "top_k": cp.top_k,
                    "weight_copies_rotated": ncopies},
-        "prefill": {"ms": round(pre_avg, 5), "ms_min": round(float(np.min(pre_ms)), 5),
-                    "gflop": flops / 1e9, "tflops": round(tflops, 2), "timing": pre_how,
-                    "frac_of_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS, 4)},
     }
+    roof = None
+    # ---- prefill: per-call time (HIP graph of back-to-back calls) and the tiled
+    # kernel's own time (events around it)
+    if prefill:
+        pre_ms, pre_how = time_calls(prefill, wcopies, args.steps, args.warmup, torch)
+        flops = 2.0 * cp.M * cp.N * cp.K
+        pre_avg = float(np.mean(pre_ms))
+        tflops = flops / (pre_avg * 1e-3) / 1e12
+        kern_ms = time_kernel(prefill, wcopies, args.steps, args.warmup, geg, torch, 0)
+        ktflops = flops / (kern_ms * 1e-3) / 1e12
+        result["value"], result["unit"] = round(tflops, 2), "TFLOP/s"
+        result["prefill"] = {"ms": round(pre_avg, 5), "ms_min": round(float(np.min(pre_ms)), 5),
+                             "gflop": flops / 1e9, "tflops": round(tflops, 2), "timing": pre_how,
+                             "kernel_ms": round(kern_ms, 5), "kernel_tflops": round(ktflops, 2),
+                             "frac_of_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(ktflops, 2), "peak": round(PEAK_MFMA_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(ktflops / PEAK_MFMA_TFLOPS, 4),
+                "kernel": ("dgrad (tiled) kernel" if cp.op == "dgrad" else "tiled kernel")
+                          + f" ({cp.fmt}), {cp.name}",
+                "per_launch_gflop": round(flops / 1e9, 3), "kernel_ms": round(kern_ms, 5)}
     if dec:
         cd, dsizes, decode = dec
-        dec_ms, dec_how = time_calls(decode, wcopies, max(args.steps, 50), args.warmup, torch)
+        dsteps = max(args.steps, 50)
+        dec_ms, dec_how = time_calls(decode, wcopies, dsteps, args.warmup, torch)
         dbytes = touched_weight_bytes(cd, dsizes)
         dec_avg = float(np.mean(dec_ms))
         gbps = dbytes / (dec_avg * 1e-3) / 1e9
+        kern_ms = time_kernel(decode, wcopies, dsteps, args.warmup, geg, torch, 1)
+        kgbps = dbytes / (kern_ms * 1e-3) / 1e9
         result["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 5),
-                            "ms_min": round(float(np.min(dec_ms)), 5),
-                            "weight_bytes": dbytes, "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                            "timing": dec_how}
+                            "ms_min": round(float(np.min(dec_ms)), 5), "weight_bytes": dbytes,
+                            "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "timing": dec_how,
+                            "skinny_kernel_ms": round(kern_ms, 5), "skinny_kernel_gbps": round(kgbps, 1)}
+        if not prefill:
+            result["value"], result["unit"] = round(gbps, 1), "GB/s"
+            roof = {"bound": "hbm", "achieved": round(kgbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(kgbps / PEAK_HBM_GBPS, 4),
+                    "kernel": f"skinny kernel ({cd.fmt}), {cd.name}",
+                    "per_launch_bytes": dbytes, "kernel_ms": round(kern_ms, 5)}
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    tname = pre_name or dec_name
     if os.path.exists(tfile):
         try:
-            t = json.load(open(tfile))
-            rec = t.get(cp.name)
+            rec = json.load(open(tfile)).get(tname)
             if rec and rec.get("kernel_sha") == kernel_sha():
                 traffic = rec["hbm_bytes"]
         except Exception:
             traffic = None
-    result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_MFMA_TFLOPS, 1),
-                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
-                          "traffic": traffic,
-                          "kernel": f"grouped {'dgrad' if cp.op == 'dgrad' else 'tile'} kernel ({cp.fmt}), {cp.name}",
-                          "per_launch_gflop": flops / 1e9}
+    roof["traffic"] = traffic
+    result["roofline"] = roof
     if not args.no_cpu_baseline and cp.op == "fwd":
-        result["cpu_baseline"] = cpu_baseline(cp, args.seed, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(cp, args.seed, args.cpu_budget, result["unit"])
     result["kernel_sha"] = kernel_sha()
     print(json.dumps(result), flush=True)
 

@@ -43,8 +43,11 @@ class GegError(RuntimeError):
 
 
 class Opts(ctypes.Structure):
-    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled; split_k 0 auto / 1..16."""
-    _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled; split_k 0 auto / 1..16;
+    kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end, skinny
+    start/end) recorded around the call's kernels."""
+    _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("kernel_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -84,6 +87,42 @@ def lib() -> ctypes.CDLL:
             L.geg_launch_count.argtypes, L.geg_launch_count.restype = [], ctypes.c_uint64
             _lib = L
     return _lib
+
+
+class KernelTimer:
+    """Four HIP events (tiled-kernel start/end, skinny-kernel start/end) that a
+    call records around its kernels when passed through `opts()`; `elapsed_ms()`
+    returns (tile_ms, skinny_ms), None for a kernel the call did not launch."""
+
+    def __init__(self, force_path: int = 0, split_k: int = 0):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._ev = (ctypes.c_void_p * 4)()
+        for i in range(4):
+            if self._hip.hipEventCreate(ctypes.byref(self._ev, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise GegError("hipEventCreate failed")
+        self._opts = Opts(force_path, split_k, ctypes.cast(self._ev, ctypes.c_void_p))
+
+    def opts(self) -> "Opts":
+        return self._opts
+
+    def _ms(self, a, b):
+        if self._hip.hipEventSynchronize(ctypes.c_void_p(self._ev[b])) != 0:
+            return None
+        ms = ctypes.c_float(0.0)
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._ev[a]),
+                                         ctypes.c_void_p(self._ev[b])) != 0:
+            return None
+        return ms.value
+
+    def elapsed_ms(self):
+        return self._ms(0, 1), self._ms(2, 3)
+
+    def __del__(self):
+        try:
+            for i in range(4):
+                self._hip.hipEventDestroy(ctypes.c_void_p(self._ev[i]))
+        except Exception:
+            pass
 
 
 def header_functions() -> list:

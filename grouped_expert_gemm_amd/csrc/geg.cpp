@@ -71,6 +71,12 @@ geg_status check_device_ptr(const void* p, const char* name) {
   return GEG_OK;
 }
 
+// Record entry i of the caller's kernel timing events, if any.
+hipError_t record_event(const geg_opts* o, int i, hipStream_t stream) {
+  if (!o || !o->kernel_events || !o->kernel_events[i]) return hipSuccess;
+  return hipEventRecord(o->kernel_events[i], stream);
+}
+
 struct Plan {
   int32_t thresh;   // skinny path takes experts with 1..thresh rows
   int32_t split;    // skinny K splits
@@ -223,14 +229,18 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     const int64_t n_tiles = (N + geg::kTileN - 1) / geg::kTileN;
     const int64_t tile_experts = std::min<int64_t>(E, M / (std::max<int64_t>(p.thresh, 0) + 1));
     const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + tile_experts) * n_tiles;
-    hipError_t e = geg::launch_tile(fmt, g, persistent_grid(bound, 1), stream);
+    hipError_t e = record_event(opts, 0, stream);
+    if (e == hipSuccess) e = geg::launch_tile(fmt, g, persistent_grid(bound, 1), stream);
+    if (e == hipSuccess) e = record_event(opts, 1, stream);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     ++g_launches;
   }
   if (p.run_skinny) {
     const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
     const int64_t bound = p.rc_bound * n_chunks * p.split;
-    hipError_t e = geg::launch_skinny(fmt, g, persistent_grid(bound, 2), stream);
+    hipError_t e = record_event(opts, 2, stream);
+    if (e == hipSuccess) e = geg::launch_skinny(fmt, g, persistent_grid(bound, 2), stream);
+    if (e == hipSuccess) e = record_event(opts, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "skinny kernel launch");
     ++g_launches;
   }
@@ -298,7 +308,9 @@ geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_
   ++g_launches;
   const int64_t k_tiles = (K + geg::kTileN - 1) / geg::kTileN;
   const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + std::min<int64_t>(E, M)) * k_tiles;
-  e = geg::launch_tile_dgrad(g, persistent_grid(bound, 1), stream);
+  e = record_event(opts, 0, stream);
+  if (e == hipSuccess) e = geg::launch_tile_dgrad(g, persistent_grid(bound, 1), stream);
+  if (e == hipSuccess) e = record_event(opts, 1, stream);
   if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
   ++g_launches;
   return GEG_OK;

@@ -88,6 +88,12 @@ typedef enum {
 typedef struct {
   int32_t force_path; /* 0 auto; 1 every expert on the skinny (decode) path; 2 every expert tiled */
   int32_t split_k;    /* 0 auto; 1..16 K splits of the skinny path                                */
+  /* Optional kernel timing: NULL, or 4 events (entries may be NULL) that the call
+   * records on `stream` right before and after its tiled kernel (dgrad: the dgrad
+   * kernel) and right before and after its skinny kernel: {tile_start, tile_end,
+   * skinny_start, skinny_end}. Events of a kernel the call does not launch are
+   * not recorded. The caller creates the events (hipEventCreate) and owns them. */
+  hipEvent_t* kernel_events;
 } geg_opts;
 
 /* Operation ids for geg_workspace_bytes. */
