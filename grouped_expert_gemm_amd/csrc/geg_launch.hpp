@@ -15,6 +15,9 @@ constexpr int kThreads = 256;      // every kernel runs 4 wave64s per workgroup
 // each workgroup covers 16 weight rows, up to kSkinnyRows activation rows and
 // one of `split` K ranges (its four wavefronts split that range again).
 constexpr int kSkinnyRows = 32;   // activation rows per skinny unit (2 MFMA row groups)
+// Experts with up to this many rows take the skinny path (as several row units
+// when above kSkinnyRows); larger ones are tiled.
+constexpr int kSkinnyMaxRows = 64;
 constexpr int kSkinnyCols = 16;   // weight rows (output columns) per skinny unit
 constexpr int kKStep = 128;       // K per skinny inner step
 

@@ -297,7 +297,7 @@ __device__ __forceinline__ void unit_store(const GemmArgs& g, f32x4 (&acc)[G][CB
 }
 
 template <Fmt F, int CB>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) uint16_t As[kALdsHalves];
   __shared__ int s_last;
