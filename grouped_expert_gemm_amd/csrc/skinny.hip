@@ -33,7 +33,7 @@ namespace geg {
 namespace {
 
 constexpr int kWaves = kThreads / 64;
-constexpr int kALdsHalves = 24 * 1024;  // 48 KiB of staged activations
+constexpr int kALdsHalves = 34 * 1024;  // 68 KiB of staged activations (two workgroups per CU)
 constexpr int kAPad = 8;                // LDS row padding (halves)
 
 // K covered by one staged activation chunk for r8 (rows rounded up to 8) rows.
