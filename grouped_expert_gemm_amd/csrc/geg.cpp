@@ -115,7 +115,8 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
-  p.thresh = force == 1 ? INT32_MAX : (force == 2 ? 0 : geg::kSkinnyMaxRows);
+  const int32_t auto_thresh = M > geg::kLargeM ? geg::kSkinnyMaxRowsLargeM : geg::kSkinnyMaxRows;
+  p.thresh = force == 1 ? INT32_MAX : (force == 2 ? 0 : auto_thresh);
   p.run_skinny = force != 2 && M > 0;
   p.run_tile = force != 1 && M > p.thresh;
   const int64_t ksteps = (K + geg::kKStep - 1) / geg::kKStep;

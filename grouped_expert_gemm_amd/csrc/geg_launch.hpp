@@ -16,8 +16,12 @@ constexpr int kThreads = 256;      // every kernel runs 4 wave64s per workgroup
 // one of `split` K ranges (its four wavefronts split that range again).
 constexpr int kSkinnyRows = 32;   // activation rows per skinny unit (2 MFMA row groups)
 // Experts with up to this many rows take the skinny path (as several row units
-// when above kSkinnyRows); larger ones are tiled.
+// when above kSkinnyRows); larger ones are tiled. In a large batch the tiled
+// kernel fills the chip anyway and absorbs mid-size experts at a lower decode
+// cost per row, so the skinny path keeps only the smallest ones.
 constexpr int kSkinnyMaxRows = 64;
+constexpr int kSkinnyMaxRowsLargeM = 16;
+constexpr int64_t kLargeM = 2048;   // routed rows above which a batch counts as large
 constexpr int kSkinnyCols = 16;   // weight rows (output columns) per skinny unit
 constexpr int kKStep = 128;       // K per skinny inner step
 
