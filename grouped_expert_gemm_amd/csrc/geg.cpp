@@ -71,6 +71,19 @@ geg_status check_device_ptr(const void* p, const char* name) {
   return GEG_OK;
 }
 
+// Compute units of the current device (256 on MI355X when it cannot be queried).
+int cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      cus = prop.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  return cus;
+}
+
 // Record entry i of the caller's kernel timing events, if any.
 hipError_t record_event(const geg_opts* o, int i, hipStream_t stream) {
   if (!o || !o->kernel_events || !o->kernel_events[i]) return hipSuccess;
@@ -124,8 +137,16 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     const int64_t skinny_experts = std::min<int64_t>(E, M);
     // Widest column block (fewest re-reads of the staged activations) that still
     // gives about one workgroup per compute unit.
+    // The narrowest column block whose units still fit in one round of resident
+    // workgroups (two per CU): smaller units finish sooner, a second round costs
+    // a whole unit's latency chain. When none fits, the widest (fewest units).
     p.cb = 4;
-    while (p.cb > 1 && skinny_experts * ((N + 16 * p.cb - 1) / (16 * p.cb)) < 256) p.cb >>= 1;
+    for (int32_t cb = 1; cb <= 4; cb <<= 1) {
+      if (skinny_experts * ((N + 16 * cb - 1) / (16 * cb)) <= 2 * (int64_t)cu_count()) {
+        p.cb = cb;
+        break;
+      }
+    }
     const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
     p.rc_bound = (M + geg::kSkinnyRows - 1) / geg::kSkinnyRows + skinny_experts;
     int64_t split = split_req;
@@ -158,15 +179,7 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
 }
 
 int persistent_grid(int64_t units_bound, int per_cu) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      cus = prop.multiProcessorCount;
-    if (cus <= 0) cus = 256;
-  }
-  const int64_t cap = (int64_t)cus * per_cu;
+  const int64_t cap = (int64_t)cu_count() * per_cu;
   return (int)std::max<int64_t>(1, std::min<int64_t>(units_bound, cap));
 }
 
