@@ -97,29 +97,47 @@ __device__ __forceinline__ float nf4_times(int i, float scale) {
   return v;
 }
 
-// Half h (entries 8h .. 8h+7) of the table of fp16 T[i] * scale (fp32 product,
-// one rounding to nearest even): fills lo[2h], lo[2h+1], hi[2h], hi[2h+1].
-__device__ __forceinline__ void nf4_scaled_lut_half(float scale, int h, Lut16& t) {
-  uint32_t p[4];
+// Quarter j (entries 4j .. 4j+3) of the table of fp16 T[i] * scale (fp32
+// product, one rounding to nearest even): fills lo[j] and hi[j].
+__device__ __forceinline__ void nf4_scaled_lut_quarter(float scale, int j, Lut16& t) {
+  uint32_t p[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     f16x2 v;
-    v[0] = (_Float16)nf4_times(8 * h + 2 * i, scale);
-    v[1] = (_Float16)nf4_times(8 * h + 2 * i + 1, scale);
+    v[0] = (_Float16)nf4_times(4 * j + 2 * i, scale);
+    v[1] = (_Float16)nf4_times(4 * j + 2 * i + 1, scale);
     p[i] = __builtin_bit_cast(uint32_t, v);
   }
+  t.lo[j] = perm(p[1], p[0], 0x06040200u);
+  t.hi[j] = perm(p[1], p[0], 0x07050301u);
+}
+
+// {fp16(ta * s), fp16(tb * s)}: exact product, one rounding to nearest even,
+// one mixed-precision fma per value (the +0 addend can turn a -0.0 product into
+// +0.0, which no sum of products can tell apart).
+__device__ __forceinline__ uint32_t f16x2_times(float ta, float tb, float s) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(d) : "s"(ta), "v"(s));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(d) : "s"(tb), "v"(s));
+  return d;
+}
+
+// The same quarter with f16x2_times (two VALU instructions per pair instead of
+// three). For the GEMM kernels, whose decoded weights only enter sums.
+__device__ __forceinline__ void nf4_scaled_lut_quarter_mix(float scale, int j, Lut16& t) {
+  uint32_t p[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    t.lo[2 * h + q] = perm(p[2 * q + 1], p[2 * q], 0x06040200u);
-    t.hi[2 * h + q] = perm(p[2 * q + 1], p[2 * q], 0x07050301u);
-  }
+  for (int i = 0; i < 2; ++i)
+    p[i] = f16x2_times(nf4_value(4 * j + 2 * i), nf4_value(4 * j + 2 * i + 1), scale);
+  t.lo[j] = perm(p[1], p[0], 0x06040200u);
+  t.hi[j] = perm(p[1], p[0], 0x07050301u);
 }
 
 // fp16 of T[i] * scale for i = 0..15 (fp32 product, one rounding to nearest even).
 __device__ __forceinline__ Lut16 nf4_scaled_lut(float scale) {
   Lut16 t;
-  nf4_scaled_lut_half(scale, 0, t);
-  nf4_scaled_lut_half(scale, 1, t);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) nf4_scaled_lut_quarter(scale, j, t);
   return t;
 }
 

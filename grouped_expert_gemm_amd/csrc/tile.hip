@@ -163,6 +163,13 @@ __device__ __forceinline__ void load_a(RawA& r, const TileSrc& t, int st, bool o
     r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(R, t.a_off, (uint32_t)st * (BK * 2) + (uint32_t)i * t.a_rows8, 0);
 }
 
+// Piece i of load_a alone (one load per MFMA group keeps the vector memory
+// path from bunching up).
+__device__ __forceinline__ void load_a_piece(RawA& r, int i, const TileSrc& t, int st, bool on) {
+  r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_on(t.a, t.na, on), t.a_off,
+                                                 (uint32_t)st * (BK * 2) + (uint32_t)i * t.a_rows8, 0);
+}
+
 template <Fmt F>
 __device__ __forceinline__ void load_b(RawB& r, const TileSrc& t, int st, bool on) {
   r.c = __builtin_amdgcn_raw_buffer_load_b128(rsrc_on(t.w, t.nw, on), t.w_off, (uint32_t)st * t.w_step, 0);
@@ -186,19 +193,19 @@ __device__ __forceinline__ void store_a_piece(const RawA& r, int i, uint16_t* As
   *reinterpret_cast<u32x4*>(&As[swz(row, chunk)]) = v;
 }
 
-// Per-stage decode state of a thread's weight piece: the NF4 table scaled by
+// Decode state of a thread's weight row for one stage: the NF4 table scaled by
 // the block's absmax, or the MXFP4 block scale (0 for a 32-wide piece past K).
 template <Fmt F> struct BDec;
 template <> struct BDec<NF4> { Lut16 lut; };
 template <> struct BDec<MXFP4> { float sc; };
 
-// Decode state setup, in two halves so that it spreads over two MFMA groups
-// (NF4: the scaled table's entries 0-7, then 8-15; MXFP4: the block scale).
+// Part j (0..3) of the decode state of stage k0 from the raw scale: NF4 builds
+// table entries 4j .. 4j+3; MXFP4 converts the block scale at j = 0.
 template <Fmt F>
-__device__ __forceinline__ void b_setup(BDec<F>& d, int h, const RawB& r, int64_t k0, int64_t K) {
+__device__ __forceinline__ void b_setup(BDec<F>& d, int j, const RawB& r, int64_t k0, int64_t K) {
   if constexpr (F == NF4) {
-    nf4_scaled_lut_half(r.s, h, d.lut);
-  } else if (h == 1) {
+    nf4_scaled_lut_quarter_mix(r.s, j, d.lut);
+  } else if (j == 0) {
     const bool ok = k0 + 32 * (threadIdx.x & 1) < K;
     d.sc = ok ? e8m0_to_f32(__builtin_bit_cast(uint32_t, r.s)) : 0.f;
   }
@@ -208,43 +215,78 @@ __device__ __forceinline__ void b_setup(BDec<F>& d, int h, const RawB& r, int64_
 // the NF4 path are stored in slot order [0, 2, 4, 6, 1, 3, 5, 7].
 __device__ __forceinline__ int nf4_slot(int j) { return (j >> 1) | ((j & 1) << 2); }
 
-// Eight codes of the thread's piece q -> decoded weights in LDS, in two halves
-// (even k, then odd k) that run in consecutive MFMA groups.
-// Forward: row t/2, chunk 4 (t%2) + q, one 16-byte store (slot order) by the
-// odd half. dgrad: the codes are columns k = 32 (t/64) + 8 q + j of weight row
-// n = t%64; each value goes to LDS row k at the slot of n (2-byte stores; `bcol`
-// is the thread's column offset).
-template <Fmt F, bool DG>
-__device__ __forceinline__ u32x2 b_piece_even(const RawB& r, const BDec<F>& d, int q, uint16_t* Bs,
-                                              int bcol) {
-  if constexpr (F == NF4) {
-    const u32x2 v = nf4_decode8_even(d.lut, r.c[q]);   // k = 0, 2 | 4, 6
-    if constexpr (DG) {
-      uint16_t* p = Bs + (32 * (threadIdx.x >> 6) + 8 * q) * kLdT + bcol;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) p[2 * h * kLdT] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
-    }
-    return v;
+// Four NF4 codes in flight (the even-k or the odd-k half of an 8-code piece):
+// their v_perm selectors and the low bytes of their table entries. Byte b of
+// the packed dword holds k = 2b in its high nibble and k = 2b + 1 in its low one.
+struct NF4Half {
+  uint32_t s7;   // index & 7 per byte
+  uint32_t sel;  // 0x03020100 | 4 * (bit 3 of the index) per byte
+  uint32_t lo;
+};
+
+// `m4` = 0x04040404 and `base` = 0x03020100, kept in registers so that the mask
+// and the merge fold into one and-or.
+template <bool EVEN>
+__device__ __forceinline__ void nf4_half_select(uint32_t x, uint32_t m4, uint32_t base, NF4Half& h) {
+  if constexpr (EVEN) {
+    h.s7 = (x >> 4) & 0x07070707u;
+    h.sel = ((x >> 5) & m4) | base;
   } else {
-    return u32x2{0u, 0u};
+    h.s7 = x & 0x07070707u;
+    h.sel = ((x >> 1) & m4) | base;
   }
 }
 
+__device__ __forceinline__ void nf4_half_lo(const Lut16& t, NF4Half& h) {
+  h.lo = perm(perm(t.lo[3], t.lo[2], h.s7), perm(t.lo[1], t.lo[0], h.s7), h.sel);
+}
+
+// High bytes, then the four fp16 values as two slot-ordered pairs.
+__device__ __forceinline__ u32x2 nf4_half_out(const Lut16& t, const NF4Half& h) {
+  const uint32_t hi = perm(perm(t.hi[3], t.hi[2], h.s7), perm(t.hi[1], t.hi[0], h.s7), h.sel);
+  return u32x2{perm(hi, h.lo, 0x05010400u), perm(hi, h.lo, 0x07030602u)};
+}
+
+// dgrad: the four values of a half go to LDS rows k = 32 (t/64) + 8 q + 2 i + odd
+// (i = 0..3) at the thread's column `bcol` (2-byte stores).
+__device__ __forceinline__ void dg_store_half(uint16_t* Bs, int q, int odd, int bcol, u32x2 v) {
+  uint16_t* p = Bs + (32 * (threadIdx.x >> 6) + 8 * q + odd) * kLdT + bcol;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[2 * i * kLdT] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+}
+
+// Staging step r (0..2) of the thread's weight piece q (its 8 codes r.c[q]):
+// NF4 r = 0 selects the even-k codes and looks up their low bytes, r = 1
+// finishes them and selects the odd-k codes, r = 2 finishes the piece and stores
+// it; MXFP4 decodes and stores the whole piece at r = 0. Each step is 7-8 VALU
+// instructions, so that two steps fit under the four MFMAs of a group.
+// Forward: row t/2, chunk 4 (t%2) + q, one 16-byte store in slot order. dgrad:
+// the codes are columns k = 32 (t/64) + 8 q + j of weight row n = t%64; each
+// value goes to LDS row k at the slot of n.
 template <Fmt F, bool DG>
-__device__ __forceinline__ void b_piece_odd(const RawB& r, const BDec<F>& d, int q, u32x2 even,
-                                            uint16_t* Bs, int bcol) {
+__device__ __forceinline__ void b_step(int q, int r, const RawB& rb, const BDec<F>& d, NF4Half& h,
+                                       u32x2& even, uint16_t* Bs, int bcol, uint32_t m4,
+                                       uint32_t base) {
   const int t = threadIdx.x;
   if constexpr (F == NF4) {
-    const u32x2 v = nf4_decode8_odd(d.lut, r.c[q]);    // k = 1, 3 | 5, 7
-    if constexpr (DG) {
-      uint16_t* p = Bs + (32 * (t >> 6) + 8 * q) * kLdT + bcol;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) p[(2 * h + 1) * kLdT] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+    const uint32_t x = rb.c[q];
+    if (r == 0) {
+      nf4_half_select<true>(x, m4, base, h);
+      nf4_half_lo(d.lut, h);
+    } else if (r == 1) {
+      even = nf4_half_out(d.lut, h);
+      if constexpr (DG) dg_store_half(Bs, q, 0, bcol, even);
+      nf4_half_select<false>(x, m4, base, h);
     } else {
-      *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = u32x4{even[0], even[1], v[0], v[1]};
+      nf4_half_lo(d.lut, h);
+      const u32x2 odd = nf4_half_out(d.lut, h);
+      if constexpr (DG)
+        dg_store_half(Bs, q, 1, bcol, odd);
+      else
+        *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = u32x4{even[0], even[1], odd[0], odd[1]};
     }
-  } else {
-    *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = mxfp4_decode8(r.c[q], d.sc);
+  } else if (r == 0) {
+    *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = mxfp4_decode8(rb.c[q], d.sc);
   }
 }
 
@@ -268,20 +310,26 @@ struct Ops {
 
 // One 64-k stage of the tile's main loop, in 16 groups of (up to) 4 MFMAs:
 // groups 0-7 run substep 0 (k 0..31 of the stage), groups 8-15 substep 1. Each
-// group issues one LDS operand read three groups ahead of its use and one slice
-// of the next stage's staging work, so that LDS latency and VALU work overlap
-// the MFMAs: groups 0-3 store activation rows into the other buffer, groups 2-3
-// build the decode table, groups 4-11 decode and store the weights (half a
-// piece of 8 codes each). Barrier Y after group 11 publishes the next stage's
-// buffer, which lets groups 12-15 read its first operands ahead; barrier X at
-// the end frees the current buffer.
+// group issues its LDS operand read three groups ahead of use and a slice of the
+// staging work, spread so that no group holds more than about two VALU
+// instructions per MFMA: the MFMA pipe hides that much VALU work of the same
+// wavefront, while a denser burst stalls it.
+//   groups 0-3    store the next stage's activation rows (from registers)
+//   groups 0-1    finish the next stage's decode table (entries 8-15)
+//   groups 2-13   decode and store the next stage's weights, piece q in groups
+//                 2 + 3q .. 4 + 3q
+//   barrier Y after group 13 publishes the next stage's buffers; groups 14-15
+//   read its first operands ahead and build the first half of the table of the
+//   stage after it (entries 0-7, from the raw scale already in registers)
+//   barrier X at the end frees the current buffers.
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
 template <Fmt F, bool DG, int H, int P>
 __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
                                            int st, int nst, int wave, int lane, int bcol,
-                                           RawA& ra, RawB (&rb)[2], Ops& ops,
-                                           f32x4 (&acc)[8][4], uint32_t aoff, uint32_t boff) {
-  const int cur = st & 1, nxt = cur ^ 1;
+                                           RawA& ra, RawB (&rb)[2], BDec<F>& dec, Ops& ops,
+                                           f32x4 (&acc)[8][4], uint32_t aoff, uint32_t boff,
+                                           uint32_t m4, uint32_t base) {
+  constexpr int cur = P, nxt = P ^ 1;   // st % 2 == P
   const int64_t k1 = (int64_t)(st + 1) * BK;
   // Substep 1 reads chunk 4 + c where substep 0 reads chunk c: the swizzled
   // chunk differs in bit 2, i.e. the half offset differs in bit 5 (the padded
@@ -295,8 +343,8 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
   constexpr int NI = 4 * H;                   // A fragments per substep
   u32x4 af[16];      // A fragment of group g (substep g / 8, rows 16 (g % 8))
   u32x4 b1[4];
-  BDec<F> dec;
-  u32x2 half;
+  NF4Half h;
+  u32x2 even;
 #pragma unroll
   for (int i = 0; i < 3; ++i) af[i] = ops.a[i];
 
@@ -313,32 +361,36 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
 #pragma unroll
       for (int j = 0; j < 4; ++j) b1[j] = lds_frag(B1 + BR * j);
     }
-    if (NI > 0 && g == 12) {
+    if (NI > 0 && g == 14) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(Bn + BR * j);
     }
-    if (g >= 13 && g - 13 < NI) ops.a[g - 13] = lds_frag(An + 16 * BK * (g - 13));
+    if (g == 14 && NI > 0) ops.a[0] = lds_frag(An);
+    if (g == 15 && NI > 1) ops.a[1] = lds_frag(An + 16 * BK);
+    if (g == 15 && NI > 2) ops.a[2] = lds_frag(An + 32 * BK);
     if (i < NI) mfma_row<F>(af[g], sub ? b1 : ops.b, acc[i]);
     // staging of the next stage (on the last stage it writes stale data into the
     // free buffer, which nothing reads; this keeps the groups free of branches)
     if (g < 4) {
       store_a_piece<F, DG>(ra, g, L.a[nxt], k1, C, wave, lane);
-      if (g == 3) load_a(ra, src, st + 2, st + 2 < nst);
+      load_a_piece(ra, g, src, st + 2, st + 2 < nst);
     }
-    if (g == 2 || g == 3) b_setup<F>(dec, g - 2, rb[P ^ 1], k1, K);
-    if (g >= 4 && g < 12) {
-      const int q = (g - 4) >> 1;
-      if ((g & 1) == 0) {
-        half = b_piece_even<F, DG>(rb[P ^ 1], dec, q, L.b[nxt], bcol);
-      } else {
-        b_piece_odd<F, DG>(rb[P ^ 1], dec, q, half, L.b[nxt], bcol);
-        if (g == 11) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
-      }
+    if (g == 0 || g == 1) b_setup<F>(dec, g + 2, rb[P ^ 1], k1, K);
+    if (g >= 2 && g < 14) {
+      b_step<F, DG>((g - 2) / 3, (g - 2) % 3, rb[P ^ 1], dec, h, even, L.b[nxt], bcol, m4, base);
+      if (g == 13) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
     }
-    if (g == 11) __syncthreads();   // Y: the next stage's buffer is complete
+    if (g == 13) __syncthreads();   // Y: the next stage's buffers are complete
+    if (g == 14 || g == 15) b_setup<F>(dec, g - 14, rb[P], k1 + BK, K);
+    // one MFMA, then up to two VALU instructions, four times
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
-  // X: every wavefront is done with the current buffer.
+  // X: every wavefront is done with the current buffers.
   __syncthreads();
 }
 
@@ -354,28 +406,34 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   const int bcol = ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7);   // dgrad staging column
   constexpr int BR = 16 * (DG ? kLdT : BK);
   const int nst = (int)((C + BK - 1) / BK);
+  uint32_t m4 = 0x04040404u, base = 0x03020100u;
+  asm volatile("" : "+v"(base));
+  asm volatile("" : "+s"(m4));
   RawA ra;
   RawB rb[2];
+  BDec<F> dec;
   Ops ops;
   // Prologue: stage 0 into buffer 0; raw data of stages 1 (activations) and
-  // 1, 2 (codes) in flight.
+  // 1, 2 (codes) in flight; the first half of stage 1's decode state.
   load_a(ra, src, 0, true);
   load_b<F>(rb[0], src, 0, true);
   load_b<F>(rb[1], src, 1, nst > 1);
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_a_piece<F, DG>(ra, q, L.a[0], 0, C, wave, lane);
   {
-    BDec<F> d;
-    b_setup<F>(d, 0, rb[0], 0, K);
-    b_setup<F>(d, 1, rb[0], 0, K);
+    NF4Half h;
+    u32x2 even;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x2 e = b_piece_even<F, DG>(rb[0], d, q, L.b[0], bcol);
-      b_piece_odd<F, DG>(rb[0], d, q, e, L.b[0], bcol);
-    }
+    for (int j = 0; j < 4; ++j) b_setup<F>(dec, j, rb[0], 0, K);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 3; ++r) b_step<F, DG>(q, r, rb[0], dec, h, even, L.b[0], bcol, m4, base);
   }
   load_a(ra, src, 1, nst > 1);
   load_b<F>(rb[0], src, 2, nst > 2);
+  b_setup<F>(dec, 0, rb[1], BK, K);
+  b_setup<F>(dec, 1, rb[1], BK, K);
   __syncthreads();
   if constexpr (H > 0) {
 #pragma unroll
@@ -384,9 +442,9 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
   for (int st = 0; st < nst; st += 2) {
-    tile_stage<F, DG, H, 0>(L, src, C, K, st, nst, wave, lane, bcol, ra, rb, ops, acc, aoff, boff);
+    tile_stage<F, DG, H, 0>(L, src, C, K, st, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff, m4, base);
     if (st + 1 < nst)
-      tile_stage<F, DG, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, ops, acc, aoff, boff);
+      tile_stage<F, DG, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff, m4, base);
   }
 }
 
