@@ -13,8 +13,8 @@ Prints ONE JSON line:
              the decode-only workloads (qwen3_t64, qwen3_down_t64) the decode
              call's packed-weight GB/s
   decode     packed-weight GB/s of the decode call (codes + scales of touched experts)
-  roofline   the dominant kernel (tiled/dgrad kernel; skinny kernel for decode-only
-             workloads) against its bound: algorithmic flops (or packed-weight
+  roofline   the dominant kernel (tiled/dgrad kernel; the decode kernels -- vector
+             and/or skinny path -- for decode-only workloads) against its bound: algorithmic flops (or packed-weight
              bytes) per launch over the kernel's own time, from the two HIP events
              the library records around it on the launch stream
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same case
@@ -54,7 +54,7 @@ WORKLOADS = {
     "qwen3_t64": (None, "qwen3_gate_up_t64"),
     "qwen3_down_t64": (None, "qwen3_down_t64"),
 }
-KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "geg.cpp"]
+KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "geg.cpp"]
 
 
 def kernel_sha() -> str:
@@ -137,7 +137,7 @@ def time_calls(fn, copies, steps, warmup, torch, use_graph=True):
 def time_kernel(fn, copies, steps, warmup, geg, torch, slot, force_path=0):
     """Average device time (ms) of one kernel of the call, from the two HIP events
     the library records on the launch stream right before and after that kernel
-    (slot 0: tiled or dgrad kernel, slot 1: skinny kernel). The calls run back to
+    (slot 0: tiled or dgrad kernel, slot 1: the decode kernels). The calls run back to
     back with one event pair each; all are read after a final synchronisation."""
     for i in range(warmup):
         fn(copies[i % len(copies)], None)
@@ -347,12 +347,12 @@ def main():
         result["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 5),
                             "ms_min": round(float(np.min(dec_ms)), 5), "weight_bytes": dbytes,
                             "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "timing": dec_how,
-                            "skinny_kernel_ms": round(kern_ms, 5), "skinny_kernel_gbps": round(kgbps, 1)}
+                            "decode_kernels_ms": round(kern_ms, 5), "decode_kernels_gbps": round(kgbps, 1)}
         if not prefill:
             result["value"], result["unit"] = round(gbps, 1), "GB/s"
             roof = {"bound": "hbm", "achieved": round(kgbps, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(kgbps / PEAK_HBM_GBPS, 4),
-                    "kernel": f"skinny kernel ({cd.fmt}), {cd.name}",
+                    "kernel": f"decode kernels ({cd.fmt}), {cd.name}",
                     "per_launch_bytes": dbytes, "kernel_ms": round(kern_ms, 5)}
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")

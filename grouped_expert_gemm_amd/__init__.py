@@ -43,9 +43,9 @@ class GegError(RuntimeError):
 
 
 class Opts(ctypes.Structure):
-    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled; split_k 0 auto / 1..16;
-    kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end, skinny
-    start/end) recorded around the call's kernels."""
+    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled / 3 vector; split_k 0 auto /
+    1..16; kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end,
+    decode start/end) recorded around the call's kernels."""
     _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p)]
 
@@ -90,9 +90,9 @@ def lib() -> ctypes.CDLL:
 
 
 class KernelTimer:
-    """Four HIP events (tiled-kernel start/end, skinny-kernel start/end) that a
+    """Four HIP events (tiled-kernel start/end, decode-kernels start/end) that a
     call records around its kernels when passed through `opts()`; `elapsed_ms()`
-    returns (tile_ms, skinny_ms), None for a kernel the call did not launch."""
+    returns (tile_ms, decode_ms), None for kernels the call did not launch."""
 
     def __init__(self, force_path: int = 0, split_k: int = 0):
         self._hip = ctypes.CDLL("libamdhip64.so")

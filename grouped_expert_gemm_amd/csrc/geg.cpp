@@ -91,7 +91,9 @@ hipError_t record_event(const geg_opts* o, int i, hipStream_t stream) {
 }
 
 struct Plan {
-  int32_t thresh;   // skinny path takes experts with 1..thresh rows
+  int32_t thresh;   // decode paths (vector, skinny) take experts with 1..thresh rows
+  int32_t vec_rows; // vector path takes 1..vec_rows, skinny vec_rows+1..thresh
+  bool run_vec;
   int32_t split;    // skinny K splits
   int32_t cb;       // skinny column blocks of 16 weight rows per wavefront
   bool run_skinny;
@@ -116,7 +118,7 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const geg_opts* o, Plan& p) {
   const int32_t force = o ? o->force_path : 0;
   const int32_t split_req = o ? o->split_k : 0;
-  if (force < 0 || force > 2) return fail(GEG_ERR_BAD_OPTION, "force_path must be 0, 1 or 2");
+  if (force < 0 || force > 3) return fail(GEG_ERR_BAD_OPTION, "force_path must be 0, 1, 2 or 3");
   if (split_req < 0 || split_req > 16) return fail(GEG_ERR_BAD_OPTION, "split_k must be 0..16");
   std::memset(&p, 0, sizeof(p));
   p.split = 1;
@@ -129,9 +131,14 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     return GEG_OK;
   }
   const int32_t auto_thresh = M > geg::kLargeM ? geg::kSkinnyMaxRowsLargeM : geg::kSkinnyMaxRows;
-  p.thresh = force == 1 ? INT32_MAX : (force == 2 ? 0 : auto_thresh);
-  p.run_skinny = force != 2 && M > 0;
-  p.run_tile = force != 1 && M > p.thresh;
+  p.thresh = (force == 1 || force == 3) ? INT32_MAX : (force == 2 ? 0 : auto_thresh);
+  if (force == 0)
+    p.vec_rows = M <= geg::kVecMaxM ? p.thresh : 0;
+  else
+    p.vec_rows = force == 3 ? INT32_MAX : 0;
+  p.run_vec = p.vec_rows > 0 && M > 0;
+  p.run_skinny = p.thresh > p.vec_rows && M > 0;
+  p.run_tile = force != 1 && force != 3 && M > p.thresh;
   const int64_t ksteps = (K + geg::kKStep - 1) / geg::kKStep;
   if (p.run_skinny) {
     const int64_t skinny_experts = std::min<int64_t>(E, M);
@@ -229,6 +236,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.thresh = p.thresh;
   g.split = p.split;
   g.cb = p.cb;
+  g.vec_rows = p.vec_rows;
   g.err = reinterpret_cast<uint32_t*>(wsb);
   g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
@@ -249,10 +257,17 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     ++g_launches;
   }
+  if (p.run_vec) {
+    hipError_t e = record_event(opts, 2, stream);
+    if (e == hipSuccess) e = geg::launch_vec(fmt, g, cu_count(), stream);
+    if (e == hipSuccess && !p.run_skinny) e = record_event(opts, 3, stream);
+    if (e != hipSuccess) return hip_fail(e, "vector kernel launch");
+    ++g_launches;
+  }
   if (p.run_skinny) {
     const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
     const int64_t bound = p.rc_bound * n_chunks * p.split;
-    hipError_t e = record_event(opts, 2, stream);
+    hipError_t e = p.run_vec ? hipSuccess : record_event(opts, 2, stream);
     if (e == hipSuccess) e = geg::launch_skinny(fmt, g, persistent_grid(bound, 2), stream);
     if (e == hipSuccess) e = record_event(opts, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "skinny kernel launch");

@@ -25,6 +25,15 @@ constexpr int64_t kLargeM = 2048;   // routed rows above which a batch counts as
 constexpr int kSkinnyCols = 16;   // weight rows (output columns) per skinny unit
 constexpr int kKStep = 128;       // K per skinny inner step
 
+// Vector path: experts with few rows (the token-decode case) take packed dot
+// products on the vector ALUs, kVecRows activation rows per wavefront unit.
+// A batch of at most kVecMaxM routed rows takes it for every expert that is not
+// tiled; a larger batch leaves its small experts to the skinny kernel (one
+// launch instead of two: the second launch costs more than it saves).
+constexpr int kVecRows = 4;
+constexpr int64_t kVecMaxM = 64;
+constexpr int64_t kVecOneRowM = 8;   // batches up to this many rows: one row per unit
+
 // Tiled (prefill) path: one 256x256 output tile per workgroup at a time.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
@@ -42,6 +51,8 @@ struct GemmArgs {
   int32_t thresh;         // skinny path takes experts with 1..thresh rows
   int32_t split;          // skinny K splits
   int32_t cb;             // skinny: 16-row column blocks per wavefront (1, 2 or 4)
+  int32_t vec_rows;       // vector path takes experts with 1..vec_rows rows (0: none);
+                          // the skinny path takes vec_rows+1..thresh
   uint32_t* err;          // device error word
   int32_t* counters;      // split-K arrival counters
   float* partials;        // split-K partials [split, M, N]
@@ -49,6 +60,7 @@ struct GemmArgs {
 
 // Each launcher returns the hipError_t of its launch.
 hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s);
+hipError_t launch_vec(int fmt, const GemmArgs& g, int cus, hipStream_t s);   // sizes its own grid
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,

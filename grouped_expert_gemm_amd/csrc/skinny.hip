@@ -183,6 +183,7 @@ __device__ __forceinline__ void unit_k_loop(const GemmArgs& g, const Lut16& lut,
                                             int kg, int col, uint32_t& range,
                                             f32x4 (&acc)[G][CB]) {
   constexpr int D = 4 / CB;  // steps per prefetch group
+  constexpr int NB = CB == 4 ? 3 : 4;   // groups in flight (as many as the registers hold)
   const int ld = kc + kAPad;
   const int chunk_steps = kc / kKStep;
 #pragma unroll
@@ -226,8 +227,14 @@ __device__ __forceinline__ void unit_k_loop(const GemmArgs& g, const Lut16& lut,
     // (NF4 issues its first activation loads ahead of the weights; for MXFP4 the
     // extra live registers cost more occupancy than the overlap gains.)
     if constexpr (F == NF4) a_load(threadIdx.x);
-    Group<F, CB, D> b0, b1;
-    load_group<F, CB, D>(b0, g, e, n0, kg, c0 + wave, min(D, my_steps));
+    // The first NB groups of weight loads go out before the activations are
+    // staged, so that the whole unit's weight stream is requested at once when it
+    // fits (the common decode case) and staging overlaps the weights' latency.
+    Group<F, CB, D> b[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (j * D < my_steps)
+        load_group<F, CB, D>(b[j], g, e, n0, kg, c0 + wave + kWaves * j * D, min(D, my_steps - j * D));
     __syncthreads();  // LDS reads of the previous chunk are done
     if constexpr (F != NF4) a_load(threadIdx.x);
     a_store(threadIdx.x);
@@ -236,19 +243,20 @@ __device__ __forceinline__ void unit_k_loop(const GemmArgs& g, const Lut16& lut,
       a_store(q0);
     }
     __syncthreads();
-    // Two register buffers alternate: the next group's loads are in flight while
-    // the current group is decoded.
-    for (int s0 = 0; s0 < my_steps; s0 += 2 * D) {
-      if (s0 + D < my_steps)
-        load_group<F, CB, D>(b1, g, e, n0, kg, c0 + wave + kWaves * (s0 + D), min(D, my_steps - s0 - D));
-      compute_group<F, CB, D, G>(b0, lut, As, ld, r8, (int64_t)c0 * kKStep, g.K, (wave + kWaves * s0) * kKStep,
-                                 min(D, my_steps - s0), kg, col, acc);
-      if (s0 + D >= my_steps) break;
-      if (s0 + 2 * D < my_steps)
-        load_group<F, CB, D>(b0, g, e, n0, kg, c0 + wave + kWaves * (s0 + 2 * D),
-                             min(D, my_steps - s0 - 2 * D));
-      compute_group<F, CB, D, G>(b1, lut, As, ld, r8, (int64_t)c0 * kKStep, g.K, (wave + kWaves * (s0 + D)) * kKStep,
-                                 min(D, my_steps - s0 - D), kg, col, acc);
+    // NB register buffers rotate: a buffer is reloaded with the group NB ahead as
+    // soon as it has been decoded.
+    for (int s0 = 0; s0 < my_steps; s0 += NB * D) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int s = s0 + j * D;
+        if (s < my_steps) {
+          compute_group<F, CB, D, G>(b[j], lut, As, ld, r8, (int64_t)c0 * kKStep, g.K,
+                                     (wave + kWaves * s) * kKStep, min(D, my_steps - s), kg, col, acc);
+          if (s + NB * D < my_steps)
+            load_group<F, CB, D>(b[j], g, e, n0, kg, c0 + wave + kWaves * (s + NB * D),
+                                 min(D, my_steps - s - NB * D));
+        }
+      }
     }
   }
 }
@@ -309,8 +317,9 @@ __global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
   const int cols = kSkinnyCols * CB;
   const int n_chunks = (int)((g.N + cols - 1) / cols);
   const int32_t thresh = g.thresh;
+  const int32_t lo = max(1, g.vec_rows + 1);   // smaller experts take the vector path
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
-    if (s < 1 || s > thresh) return 0;
+    if (s < lo || s > thresh) return 0;
     return ((s + kSkinnyRows - 1) / kSkinnyRows) * n_chunks * S;
   });
 

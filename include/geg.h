@@ -86,13 +86,16 @@ typedef enum {
 
 /* Optional knobs (NULL = automatic). Used by tests to pin a path. */
 typedef struct {
-  int32_t force_path; /* 0 auto; 1 every expert on the skinny (decode) path; 2 every expert tiled */
+  /* 0 auto; 1 every expert on the skinny path; 2 every expert tiled; 3 every
+   * expert on the vector path (experts with more than 4 rows in chunks of 4) */
+  int32_t force_path;
   int32_t split_k;    /* 0 auto; 1..16 K splits of the skinny path                                */
   /* Optional kernel timing: NULL, or 4 events (entries may be NULL) that the call
    * records on `stream` right before and after its tiled kernel (dgrad: the dgrad
-   * kernel) and right before and after its skinny kernel: {tile_start, tile_end,
-   * skinny_start, skinny_end}. Events of a kernel the call does not launch are
-   * not recorded. The caller creates the events (hipEventCreate) and owns them. */
+   * kernel) and right before and after its decode kernels (vector and skinny, in
+   * that order): {tile_start, tile_end, decode_start, decode_end}. Events of
+   * kernels the call does not launch are not recorded. The caller creates the
+   * events (hipEventCreate) and owns them. */
   hipEvent_t* kernel_events;
 } geg_opts;
 
@@ -108,9 +111,12 @@ typedef struct {
  *   w       u8 [E, N, K/2] NF4 codes (high nibble = even k), 16-B aligned
  *   absmax  fp32 [E, N, K/64], 4-B aligned
  *   out     bf16 [M, N], 16-B aligned
- *   K % 64 == 0. Experts with at most 32 rows take the skinny path (weights
+ *   K % 64 == 0. Paths (automatic choice): in a batch of at most 64 rows every
+ *   expert takes the vector path (packed dot products on the vector ALUs,
+ *   weight rows read whole, up to 4 activation rows per pass); in a larger batch
+ *   experts with up to 64 rows (16 when M > 2048) take the skinny path (weights
  *   streamed once, MFMA over row groups of 16, optional split-K with a
- *   fixed-order reduction); larger experts take the tiled MFMA path.
+ *   fixed-order reduction) and larger experts the tiled MFMA path.
  */
 geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* w,
                              const float* absmax, void* out, int64_t M, int64_t N, int64_t K,

@@ -48,7 +48,7 @@ def test_bad_shapes_are_refused():
 
 
 def test_bad_options_are_refused():
-    assert _gemm(opts=geg.Opts(3, 0)) == 8
+    assert _gemm(opts=geg.Opts(4, 0)) == 8
     assert _gemm(opts=geg.Opts(0, 17)) == 8
     assert _gemm(opts=geg.Opts(0, -1)) == 8
 
@@ -72,7 +72,7 @@ def test_misaligned_pointers_are_refused():
 
 
 def test_small_workspace_is_refused():
-    o = geg.Opts(0, 4)
+    o = geg.Opts(1, 4)                              # skinny path, 4 K splits
     need = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, o)
     assert need > 256                               # split-K needs counters and partials
     assert _gemm(M=8, N=2048, K=2048, E=64, ws_bytes=need - 256, opts=o) == 5
@@ -86,9 +86,12 @@ def test_workspace_sizes():
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == 256 + (4 << 20) + 16384 * 2048 * 2
     assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == 256 + (4 << 20) + 8192 * 28672 * 2
-    one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 1))
-    four = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(0, 4))
+    # skinny split-K partials; a small batch on the automatic path goes to the
+    # vector path, which needs nothing beyond the header
+    one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(1, 1))
+    four = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(1, 4))
     assert one == 256 and four >= 256 + 4 * 8 * 2048 * 4
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64) == 256
     assert geg.geg_workspace_bytes(7, 8, 8, 64, 1) == 0
 
 

@@ -12,7 +12,7 @@ from gpu_util import (TOL, assert_close, bf16_to_f64, bits16, log, up, up_u16_as
 
 pytestmark = pytest.mark.gpu
 
-PATHS = {"auto": None, "skinny": (1, 0), "tiled": (2, 0)}
+PATHS = {"auto": None, "skinny": (1, 0), "tiled": (2, 0), "vec": (3, 0)}
 
 
 @pytest.fixture(scope="module")
@@ -62,7 +62,7 @@ def ref_of(d):
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
-@pytest.mark.parametrize("path", ["auto", "skinny", "tiled"])
+@pytest.mark.parametrize("path", ["auto", "skinny", "tiled", "vec"])
 def test_tiny_config(geg, seed, path):
     c = synthetic.case("tiny")
     log(f"case: tiny seed={seed} path={path}")
@@ -72,7 +72,7 @@ def test_tiny_config(geg, seed, path):
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
-@pytest.mark.parametrize("path", ["auto", "skinny", "tiled"])
+@pytest.mark.parametrize("path", ["auto", "skinny", "tiled", "vec"])
 def test_medium_ragged(geg, fmt, path):
     # several 128x128 tiles, ragged row and column tails, zero-row experts at both
     # ends, skinny (<=32 rows) and tiled experts mixed, K with a 64 (NF4) or 96
@@ -109,7 +109,7 @@ def test_exact_integer_case_is_bitwise(geg, fmt):
     ref = ref_of(d)
     refbits = P.bf16_rne_bits(ref.astype(np.float32))
     assert np.array_equal(synthetic.bf16_bits_to_f32(refbits), ref)       # exact in bf16
-    for path in ["skinny", "tiled"]:
+    for path in ["skinny", "tiled", "vec"]:
         out = run_fwd(geg, c, upload_case(d), path)
         gb = bits16(out)
         bad = np.argwhere(gb != refbits)
@@ -126,11 +126,29 @@ def test_decode_equals_tiled_and_splits_agree(geg, fmt):
     g = upload_case(d)
     ref = ref_of(d)
     outs = {}
-    for path, split in [("skinny", 1), ("skinny", 2), ("skinny", 3), ("skinny", 8), ("tiled", 0), ("auto", 0)]:
+    for path, split in [("skinny", 1), ("skinny", 2), ("skinny", 3), ("skinny", 8), ("tiled", 0), ("vec", 0),
+                        ("auto", 0)]:
         o = run_fwd(geg, c, g, path, split)
         assert_close(bf16_to_f64(o), ref, f"{name} {path} split={split}")
         outs[(path, split)] = bf16_to_f64(o)
     assert np.max(np.abs(outs[("skinny", 1)] - outs[("tiled", 0)])) <= 2 * TOL * max(1, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("fmt,K", [("nf4", 768), ("nf4", 2048), ("nf4", 4096), ("mxfp4", 1024),
+                                   ("mxfp4", 2880)])
+def test_vector_path_shapes(geg, fmt, K):
+    # the vector path's lane layouts: rows of <= 32 chunks (two weight rows per
+    # load, K = 768 / 1024), exactly one row per load (2048), several loads per
+    # row with a partial last one (2880: 90 chunks) or full ones (4096); N = 200
+    # leaves a ragged last unit; 5 and 9 rows take 2 and 3 row chunks
+    sizes = [1, 0, 2, 3, 4, 5, 9, 0, 1]
+    log(f"case: vector path {fmt} K={K} N=200 sizes={sizes}")
+    c, d = custom_case(fmt, len(sizes), K, 200, sizes, seed=11)
+    g = upload_case(d)
+    ref = ref_of(d)
+    for path in ["vec", "auto"]:
+        out = run_fwd(geg, c, g, path)
+        assert_close(bf16_to_f64(out), ref, f"vector {fmt} K={K} {path}")
 
 
 def test_determinism_nonmutation_and_canary(geg):
