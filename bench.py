@@ -14,7 +14,7 @@ Prints ONE JSON line:
              call's packed-weight GB/s
   decode     packed-weight GB/s of the decode call (codes + scales of touched experts)
   roofline   the dominant kernel (tiled/dgrad kernel; the decode kernels -- vector
-             and/or skinny path -- for decode-only workloads) against its bound: algorithmic flops (or packed-weight
+             or narrow path -- for decode-only workloads) against its bound: algorithmic flops (or packed-weight
              bytes) per launch over the kernel's own time, from the two HIP events
              the library records around it on the launch stream
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same case
@@ -54,7 +54,8 @@ WORKLOADS = {
     "qwen3_t64": (None, "qwen3_gate_up_t64"),
     "qwen3_down_t64": (None, "qwen3_down_t64"),
 }
-KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "geg.cpp"]
+KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip",
+                  "geg.cpp"]
 
 
 def kernel_sha() -> str:

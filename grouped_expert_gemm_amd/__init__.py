@@ -43,8 +43,8 @@ class GegError(RuntimeError):
 
 
 class Opts(ctypes.Structure):
-    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled / 3 vector; split_k 0 auto /
-    1..16; kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end,
+    """geg_opts: force_path 0 auto / 1 skinny / 2 tiled / 3 vector / 4 narrow; split_k 0
+    auto / 1..16 (skinny); kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end,
     decode start/end) recorded around the call's kernels."""
     _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p)]

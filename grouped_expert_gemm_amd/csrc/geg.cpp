@@ -94,6 +94,7 @@ struct Plan {
   int32_t thresh;   // decode paths (vector, skinny) take experts with 1..thresh rows
   int32_t vec_rows; // vector path takes 1..vec_rows, skinny vec_rows+1..thresh
   bool run_vec;
+  bool narrow;      // the skinny-range experts go to the narrow kernel instead
   int32_t split;    // skinny K splits
   int32_t cb;       // skinny column blocks of 16 weight rows per wavefront
   bool run_skinny;
@@ -118,7 +119,7 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const geg_opts* o, Plan& p) {
   const int32_t force = o ? o->force_path : 0;
   const int32_t split_req = o ? o->split_k : 0;
-  if (force < 0 || force > 3) return fail(GEG_ERR_BAD_OPTION, "force_path must be 0, 1, 2 or 3");
+  if (force < 0 || force > 4) return fail(GEG_ERR_BAD_OPTION, "force_path must be 0..4");
   if (split_req < 0 || split_req > 16) return fail(GEG_ERR_BAD_OPTION, "split_k must be 0..16");
   std::memset(&p, 0, sizeof(p));
   p.split = 1;
@@ -131,16 +132,18 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     return GEG_OK;
   }
   const int32_t auto_thresh = M > geg::kLargeM ? geg::kSkinnyMaxRowsLargeM : geg::kSkinnyMaxRows;
-  p.thresh = (force == 1 || force == 3) ? INT32_MAX : (force == 2 ? 0 : auto_thresh);
+  p.thresh = (force == 1 || force == 3 || force == 4) ? INT32_MAX : (force == 2 ? 0 : auto_thresh);
+  // the narrow kernel serves the skinny range unless the skinny kernel is forced
+  p.narrow = force != 1;
   if (force == 0)
     p.vec_rows = M <= geg::kVecMaxM ? p.thresh : 0;
   else
     p.vec_rows = force == 3 ? INT32_MAX : 0;
   p.run_vec = p.vec_rows > 0 && M > 0;
   p.run_skinny = p.thresh > p.vec_rows && M > 0;
-  p.run_tile = force != 1 && force != 3 && M > p.thresh;
+  p.run_tile = (force == 0 || force == 2) && M > p.thresh;
   const int64_t ksteps = (K + geg::kKStep - 1) / geg::kKStep;
-  if (p.run_skinny) {
+  if (p.run_skinny && !p.narrow) {
     const int64_t skinny_experts = std::min<int64_t>(E, M);
     // Widest column block (fewest re-reads of the staged activations) that still
     // gives about one workgroup per compute unit.
@@ -264,7 +267,13 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     if (e != hipSuccess) return hip_fail(e, "vector kernel launch");
     ++g_launches;
   }
-  if (p.run_skinny) {
+  if (p.run_skinny && p.narrow) {
+    hipError_t e = p.run_vec ? hipSuccess : record_event(opts, 2, stream);
+    if (e == hipSuccess) e = geg::launch_narrow(fmt, g, cu_count(), stream);
+    if (e == hipSuccess) e = record_event(opts, 3, stream);
+    if (e != hipSuccess) return hip_fail(e, "narrow kernel launch");
+    ++g_launches;
+  } else if (p.run_skinny) {
     const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
     const int64_t bound = p.rc_bound * n_chunks * p.split;
     hipError_t e = p.run_vec ? hipSuccess : record_event(opts, 2, stream);

@@ -60,7 +60,8 @@ struct GemmArgs {
 
 // Each launcher returns the hipError_t of its launch.
 hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s);
-hipError_t launch_vec(int fmt, const GemmArgs& g, int cus, hipStream_t s);   // sizes its own grid
+hipError_t launch_vec(int fmt, const GemmArgs& g, int cus, hipStream_t s);      // sizes its own grid
+hipError_t launch_narrow(int fmt, const GemmArgs& g, int cus, hipStream_t s);   // sizes its own grid
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,

@@ -1,0 +1,232 @@
+// Narrow path of the grouped 4-bit GEMM: experts with a few to a few dozen
+// routed rows (a decode batch of many tokens).
+//
+// The weights are streamed once per 16 or 32 activation rows and decoded once in
+// registers, as in the other decode paths; the layout is built around the memory
+// side. A workgroup unit is (expert, 16 RB activation rows, 64 CBW weight rows;
+// RB = CBW = 1 or 2); each of its four wavefronts owns CBW blocks of 16 weight rows over the
+// whole K range, so there is no cross-wavefront reduction. Per 128-wide K step a
+// wavefront loads, for each of its 16-row blocks, one 16-byte piece per lane
+// (lane l: weight row l % 16, codes k in [32 (l / 16), +32) of the step), i.e.
+// 64 contiguous bytes of each of 16 rows per load instruction; it scales its
+// private copy of the 16-entry table by the absmax of that piece's 64-block
+// (NF4) and decodes the piece into the B operands of four 16x16x32 MFMAs. The
+// activations of the step are staged once per workgroup in LDS (fp16 in the NF4
+// slot order, or bf16), double-buffered with one barrier per step; global loads
+// run NS - 1 steps ahead of use.
+//
+// MFMA k slots: MFMA j of a step takes codes 8j .. 8j+7 of every lane's piece, so
+// its 32 k are {32 g + 8 j + i : g = 0..3, i = 0..7}; the activation operand reads
+// the same k. NF4: the fp32 product table x absmax is rounded once to fp16
+// (mixed-precision fma). MXFP4: the gfx950 scaled fp4 -> bf16 conversion.
+#include <algorithm>
+
+#include "geg_device.hpp"
+#include "geg_launch.hpp"
+
+namespace geg {
+
+namespace {
+
+constexpr int kNStep = 128;                    // K per step
+constexpr int kNALd = kNStep + 8;              // staged activation row stride (halves, 272 B)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t nrsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Raw data of one K step held in registers: this thread's share of the
+// activation stage and the wavefront's weight pieces.
+template <int RB, int CBW>
+struct StepRaw {
+  u32x4 a[RB];          // activations: rows 16r + t/16, k chunk t%16 (8 values)
+  u32x4 w[CBW];         // codes of weight row n0 + 16 cb + l%16, k in [32 (l/16), +32)
+  uint32_t s[CBW];      // NF4: fp32 absmax bits; MXFP4: e8m0 byte
+};
+
+template <Fmt F, int RB, int CBW>
+__device__ __forceinline__ void load_step(StepRaw<RB, CBW>& d, const __amdgpu_buffer_rsrc_t& A,
+                                          const __amdgpu_buffer_rsrc_t& W,
+                                          const __amdgpu_buffer_rsrc_t& S, int64_t K, int64_t N,
+                                          int64_t n0, int st, int lane) {
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)st * kNStep;
+  // activations: thread t loads 16 B of row 16r + t/16 at k0 + 8 (t%16); pieces
+  // past K read as zero (offsets pushed past the buffer)
+  {
+    const int64_t k = k0 + 8 * (t & 15);
+    const uint32_t mask = k < K ? 0u : 0xFFFFFFF0u;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int64_t row = 16 * q + (t >> 4);
+      d.a[q] = __builtin_amdgcn_raw_buffer_load_b128(A, (uint32_t)((row * K + k) * 2) | mask, 0, 0);
+    }
+  }
+  const int64_t kc = k0 + 32 * (lane >> 4);        // first k of this lane's piece
+  const uint32_t mask = kc < K ? 0u : 0xFFFFFFF0u;
+#pragma unroll
+  for (int cb = 0; cb < CBW; ++cb) {
+    const int64_t n = n0 + 16 * cb + (lane & 15);  // rows past N read as zero (buffer bounds)
+    d.w[cb] = __builtin_amdgcn_raw_buffer_load_b128(W, (uint32_t)(n * (K >> 1) + (kc >> 1)) | mask, 0, 0);
+    if constexpr (F == NF4)
+      d.s[cb] = __builtin_amdgcn_raw_buffer_load_b32(S, (uint32_t)((n * (K >> 6) + (kc >> 6)) * 4) | mask, 0, 0);
+    else
+      d.s[cb] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, (uint32_t)(n * (K >> 5) + (kc >> 5)) | mask, 0, 0);
+  }
+}
+
+template <Fmt F, int RB, int CBW, int NS>
+__global__ __launch_bounds__(kThreads) void narrow_kernel(GemmArgs g) {
+  __shared__ Plan plan;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][RB * 16 * kNALd];
+  constexpr int RPU = 16 * RB;                     // activation rows per unit
+  constexpr int CPU = 4 * 16 * CBW;                // weight rows per unit
+  const int32_t n_cols = (int32_t)((g.N + CPU - 1) / CPU);
+  const int32_t lo = max(1, g.vec_rows + 1), hi = g.thresh;
+  const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
+    return (s >= lo && s <= hi) ? ((s + RPU - 1) / RPU) * n_cols : 0;
+  });
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t K = g.K, N = g.N;
+  const int nst = (int)((K + kNStep - 1) / kNStep);
+  uint32_t range = 0;
+
+  for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int e = find_expert(plan, g.E, u);
+    const int32_t lu = u - plan.upre[e];
+    const int64_t row0 = plan.off[e] + (int64_t)(lu / n_cols) * RPU;
+    const int rows = (int)min<int64_t>(RPU, plan.off[e + 1] - row0);
+    const int64_t n0 = (int64_t)(lu % n_cols) * CPU + 16 * CBW * wave;
+    const __amdgpu_buffer_rsrc_t A = nrsrc(g.a + row0 * K, (int64_t)rows * K * 2);
+    const __amdgpu_buffer_rsrc_t W = nrsrc(g.wq + (int64_t)e * N * (K >> 1), N * (K >> 1));
+    const __amdgpu_buffer_rsrc_t S =
+        F == NF4 ? nrsrc(reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6), N * (K >> 6) * 4)
+                 : nrsrc(reinterpret_cast<const uint8_t*>(g.scales) + (int64_t)e * N * (K >> 5), N * (K >> 5));
+
+    f32x4 acc[RB][CBW];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb) acc[r][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // stage the activations of step st (registers -> LDS buffer st % 2)
+    auto stage = [&](const StepRaw<RB, CBW>& r, int st) {
+      uint16_t* Ab = As[st & 1];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        u32x4 v = r.a[q];
+        if constexpr (F == NF4) v = bf16x8_to_f16_slots(v, range);
+        *reinterpret_cast<u32x4*>(&Ab[(16 * q + (t >> 4)) * kNALd + 8 * (t & 15)]) = v;
+      }
+    };
+    StepRaw<RB, CBW> raw[NS];
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < nst) load_step<F, RB, CBW>(raw[i], A, W, S, K, N, n0, i, lane);
+    __syncthreads();   // the previous unit is done with both LDS buffers
+    stage(raw[0], 0);
+    __syncthreads();
+
+    // Step st: stage st+1, load st+NS-1, compute st from LDS buffer st % 2 and
+    // the step's weight registers. raw[] rotates through NS slots (compile-time
+    // indices: the loop body covers NS steps).
+    for (int s0 = 0; s0 < nst; s0 += NS) {
+#pragma unroll
+      for (int jn = 0; jn < NS; ++jn) {
+        const int st = s0 + jn;
+        if (st < nst) {
+          StepRaw<RB, CBW>& cur = raw[jn];
+          if (st + 1 < nst) stage(raw[(jn + 1) % NS], st + 1);
+          if (st + NS - 1 < nst) load_step<F, RB, CBW>(raw[(jn + NS - 1) % NS], A, W, S, K, N, n0, st + NS - 1, lane);
+          const uint16_t* Ab = As[st & 1];
+          // A operand of MFMA j, row block r: row 16r + l%16, k = 32 (l/16) + 8 j
+          u32x4 af[RB][4];
+#pragma unroll
+          for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              af[r][j] = *reinterpret_cast<const u32x4*>(
+                  &Ab[(16 * r + (lane & 15)) * kNALd + 32 * (lane >> 4) + 8 * j]);
+#pragma unroll
+          for (int cb = 0; cb < CBW; ++cb) {
+            if constexpr (F == NF4) {
+              Lut16 lut;
+              const float sc = __builtin_bit_cast(float, cur.s[cb]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) nf4_scaled_lut_quarter_mix(sc, q, lut);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u32x4 b = nf4_decode8(lut, cur.w[cb][j]);
+#pragma unroll
+                for (int r = 0; r < RB; ++r) acc[r][cb] = mfma16<NF4>(af[r][j], b, acc[r][cb]);
+              }
+            } else {
+              const float sc = e8m0_to_f32(cur.s[cb]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u32x4 b = mxfp4_decode8(cur.w[cb][j], sc);
+#pragma unroll
+                for (int r = 0; r < RB; ++r) acc[r][cb] = mfma16<MXFP4>(af[r][j], b, acc[r][cb]);
+              }
+            }
+          }
+          __syncthreads();   // buffer st+1 complete; buffer st free for step st+2
+        }
+      }
+    }
+    // acc[r][cb][q]: activation row 16r + 4 (l/16) + q, weight row n0 + 16 cb + l%16
+#pragma unroll
+    for (int cb = 0; cb < CBW; ++cb) {
+      const int64_t n = n0 + 16 * cb + (lane & 15);
+      if (n < N) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int lr = 16 * r + 4 * (lane >> 4) + q;
+            if (lr < rows) g.out[(row0 + lr) * N + n] = to_bf16(acc[r][cb][q]);
+          }
+      }
+    }
+  }
+  if constexpr (F == NF4) {
+    if (range_overflowed(range)) atomicOr(g.err, kErrFp16Range);
+  }
+}
+
+template <Fmt F, int RB, int CBW, int NS>
+hipError_t launch_n(const GemmArgs& g, int cus, hipStream_t s) {
+  auto k = narrow_kernel<F, RB, CBW, NS>;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, kThreads, 0) != hipSuccess || b <= 0) b = 1;
+    per_cu = b;
+  }
+  constexpr int RPU = 16 * RB, CPU = 64 * CBW;
+  const int64_t chunks = (g.M + RPU - 1) / RPU + std::min<int64_t>(g.E, g.M);
+  const int64_t units = chunks * ((g.N + CPU - 1) / CPU);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)per_cu * cus));
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+template <Fmt F>
+hipError_t launch_narrow_fmt(const GemmArgs& g, int cus, hipStream_t s) {
+  // 32-row units (two 16-row blocks per wavefront, 128 weight rows per unit) when
+  // the batch's experts are expected to hold more than 16 rows; otherwise 16-row
+  // units over 64 weight rows (more, smaller units keep more wavefronts busy).
+  return g.thresh > 16 && g.M > 16 * (int64_t)std::min<int64_t>(g.E, g.M) ? launch_n<F, 2, 2, 3>(g, cus, s)
+                                                                           : launch_n<F, 1, 1, 3>(g, cus, s);
+}
+
+}  // namespace
+
+hipError_t launch_narrow(int fmt, const GemmArgs& g, int cus, hipStream_t s) {
+  return fmt == NF4 ? launch_narrow_fmt<NF4>(g, cus, s) : launch_narrow_fmt<MXFP4>(g, cus, s);
+}
+
+}  // namespace geg

@@ -86,10 +86,11 @@ typedef enum {
 
 /* Optional knobs (NULL = automatic). Used by tests to pin a path. */
 typedef struct {
-  /* 0 auto; 1 every expert on the skinny path; 2 every expert tiled; 3 every
-   * expert on the vector path (experts with more than 4 rows in chunks of 4) */
+  /* 0 auto; 1 every expert on the skinny kernel; 2 every expert tiled; 3 every
+   * expert on the vector path (experts with more than 4 rows in chunks of 4);
+   * 4 every expert on the narrow kernel (in chunks of 16 or 32 rows) */
   int32_t force_path;
-  int32_t split_k;    /* 0 auto; 1..16 K splits of the skinny path                                */
+  int32_t split_k;    /* 0 auto; 1..16 K splits of the skinny kernel (force_path 1)            */
   /* Optional kernel timing: NULL, or 4 events (entries may be NULL) that the call
    * records on `stream` right before and after its tiled kernel (dgrad: the dgrad
    * kernel) and right before and after its decode kernels (vector and skinny, in
@@ -114,9 +115,11 @@ typedef struct {
  *   K % 64 == 0. Paths (automatic choice): in a batch of at most 64 rows every
  *   expert takes the vector path (packed dot products on the vector ALUs,
  *   weight rows read whole, up to 4 activation rows per pass); in a larger batch
- *   experts with up to 64 rows (16 when M > 2048) take the skinny path (weights
- *   streamed once, MFMA over row groups of 16, optional split-K with a
- *   fixed-order reduction) and larger experts the tiled MFMA path.
+ *   experts with up to 64 rows (16 when M > 2048) take the narrow kernel
+ *   (weights streamed once per 16 or 32 rows, decoded into MFMA operands, each
+ *   wavefront over the whole K range) and larger experts the tiled MFMA path.
+ *   The skinny kernel (K split over wavefronts and optionally over workgroups
+ *   with a fixed-order reduction) serves the same rows when forced.
  */
 geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* w,
                              const float* absmax, void* out, int64_t M, int64_t N, int64_t K,

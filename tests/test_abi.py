@@ -48,7 +48,7 @@ def test_bad_shapes_are_refused():
 
 
 def test_bad_options_are_refused():
-    assert _gemm(opts=geg.Opts(4, 0)) == 8
+    assert _gemm(opts=geg.Opts(5, 0)) == 8
     assert _gemm(opts=geg.Opts(0, 17)) == 8
     assert _gemm(opts=geg.Opts(0, -1)) == 8
 

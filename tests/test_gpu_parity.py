@@ -12,7 +12,7 @@ from gpu_util import (TOL, assert_close, bf16_to_f64, bits16, log, up, up_u16_as
 
 pytestmark = pytest.mark.gpu
 
-PATHS = {"auto": None, "skinny": (1, 0), "tiled": (2, 0), "vec": (3, 0)}
+PATHS = {"auto": None, "skinny": (1, 0), "tiled": (2, 0), "vec": (3, 0), "narrow": (4, 0)}
 
 
 @pytest.fixture(scope="module")
@@ -62,7 +62,7 @@ def ref_of(d):
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
-@pytest.mark.parametrize("path", ["auto", "skinny", "tiled", "vec"])
+@pytest.mark.parametrize("path", ["auto", "skinny", "tiled", "vec", "narrow"])
 def test_tiny_config(geg, seed, path):
     c = synthetic.case("tiny")
     log(f"case: tiny seed={seed} path={path}")
@@ -72,7 +72,7 @@ def test_tiny_config(geg, seed, path):
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
-@pytest.mark.parametrize("path", ["auto", "skinny", "tiled", "vec"])
+@pytest.mark.parametrize("path", ["auto", "skinny", "tiled", "vec", "narrow"])
 def test_medium_ragged(geg, fmt, path):
     # several 128x128 tiles, ragged row and column tails, zero-row experts at both
     # ends, skinny (<=32 rows) and tiled experts mixed, K with a 64 (NF4) or 96
@@ -109,7 +109,7 @@ def test_exact_integer_case_is_bitwise(geg, fmt):
     ref = ref_of(d)
     refbits = P.bf16_rne_bits(ref.astype(np.float32))
     assert np.array_equal(synthetic.bf16_bits_to_f32(refbits), ref)       # exact in bf16
-    for path in ["skinny", "tiled", "vec"]:
+    for path in ["skinny", "tiled", "vec", "narrow"]:
         out = run_fwd(geg, c, upload_case(d), path)
         gb = bits16(out)
         bad = np.argwhere(gb != refbits)
@@ -127,7 +127,7 @@ def test_decode_equals_tiled_and_splits_agree(geg, fmt):
     ref = ref_of(d)
     outs = {}
     for path, split in [("skinny", 1), ("skinny", 2), ("skinny", 3), ("skinny", 8), ("tiled", 0), ("vec", 0),
-                        ("auto", 0)]:
+                        ("narrow", 0), ("auto", 0)]:
         o = run_fwd(geg, c, g, path, split)
         assert_close(bf16_to_f64(o), ref, f"{name} {path} split={split}")
         outs[(path, split)] = bf16_to_f64(o)
@@ -146,7 +146,7 @@ def test_vector_path_shapes(geg, fmt, K):
     c, d = custom_case(fmt, len(sizes), K, 200, sizes, seed=11)
     g = upload_case(d)
     ref = ref_of(d)
-    for path in ["vec", "auto"]:
+    for path in ["vec", "narrow", "auto"]:
         out = run_fwd(geg, c, g, path)
         assert_close(bf16_to_f64(out), ref, f"vector {fmt} K={K} {path}")
 
