@@ -178,6 +178,25 @@ __device__ __forceinline__ u32x4 nf4_decode8(const Lut16& t, uint32_t x) {
   return u32x4{e[0], e[1], o[0], o[1]};
 }
 
+// The same with the selector constants passed in registers (m4 = 0x04040404,
+// base = 0x03020100, made opaque by the caller): the mask and the merge then fold
+// into one and-or per four codes.
+__device__ __forceinline__ u32x4 nf4_decode8(const Lut16& t, uint32_t x, uint32_t m4, uint32_t base) {
+  uint32_t lo, hi;
+  lut_lookup4(t, (x >> 4) & 0x07070707u, ((x >> 5) & m4) | base, lo, hi);
+  const uint32_t e0 = perm(hi, lo, 0x05010400u), e1 = perm(hi, lo, 0x07030602u);
+  lut_lookup4(t, x & 0x07070707u, ((x >> 1) & m4) | base, lo, hi);
+  return u32x4{e0, e1, perm(hi, lo, 0x05010400u), perm(hi, lo, 0x07030602u)};
+}
+
+// Selector constants for the and-or form above, hidden from constant folding.
+__device__ __forceinline__ void nf4_selector_consts(uint32_t& m4, uint32_t& base) {
+  m4 = 0x04040404u;
+  base = 0x03020100u;
+  asm volatile("" : "+v"(base));
+  asm volatile("" : "+s"(m4));
+}
+
 // ------------------------------------------------------------------ MXFP4 decode
 // e8m0 byte -> fp32 scale 2^(x-127): normal for 1..254, 2^-127 (subnormal) for 0,
 // NaN for 255.

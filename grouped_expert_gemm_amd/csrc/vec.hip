@@ -68,6 +68,8 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, in
       F == NF4 ? vrsrc(reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6), N * (K >> 6) * 4)
                : vrsrc(reinterpret_cast<const uint8_t*>(g.scales) + (int64_t)e * N * (K >> 5), N * (K >> 5));
   const __amdgpu_buffer_rsrc_t A = vrsrc(g.a + row0 * K, (int64_t)rows * K * 2);
+  uint32_t m4, base;
+  nf4_selector_consts(m4, base);
   float acc[U][RV];
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -122,7 +124,7 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, in
         for (int m = 0; m < RV; ++m) d[m] = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4 w = nf4_decode8(lut, code[u][j]);   // codes k = 8j .. 8j+7, slot order
+          const u32x4 w = nf4_decode8(lut, code[u][j], m4, base);   // codes k = 8j .. 8j+7, slot order
 #pragma unroll
           for (int m = 0; m < RV; ++m)
             if (m < rows)
