@@ -131,7 +131,13 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
-  const int32_t auto_thresh = M > geg::kLargeM ? geg::kSkinnyMaxRowsLargeM : geg::kSkinnyMaxRows;
+  // A decode-class batch (at most kDecodeAvgRows routed rows per expert on
+  // average) keeps every expert off the tiled path: its few tiles would run one
+  // per CU over the whole K range, slower than streaming the weights once per
+  // 32 rows on every CU, and the call saves the tiled launches.
+  const bool decode_class = M <= geg::kDecodeAvgRows * (int64_t)E;
+  const int32_t auto_thresh = decode_class ? INT32_MAX
+                              : (M > geg::kLargeM ? geg::kSkinnyMaxRowsLargeM : geg::kSkinnyMaxRows);
   p.thresh = (force == 1 || force == 3 || force == 4) ? INT32_MAX : (force == 2 ? 0 : auto_thresh);
   // the narrow kernel serves the skinny range unless the skinny kernel is forced
   p.narrow = force != 1;

@@ -22,6 +22,7 @@ constexpr int kSkinnyRows = 32;   // activation rows per skinny unit (2 MFMA row
 constexpr int kSkinnyMaxRows = 64;
 constexpr int kSkinnyMaxRowsLargeM = 16;
 constexpr int64_t kLargeM = 2048;   // routed rows above which a batch counts as large
+constexpr int64_t kDecodeAvgRows = 32;   // batches with at most this many rows per expert: no tiles
 constexpr int kSkinnyCols = 16;   // weight rows (output columns) per skinny unit
 constexpr int kKStep = 128;       // K per skinny inner step
 

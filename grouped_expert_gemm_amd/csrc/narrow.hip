@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(GemmArgs g) {
   constexpr int RPU = 16 * RB;                     // activation rows per unit
   constexpr int CPU = 4 * 16 * CBW;                // weight rows per unit
   const int32_t n_cols = (int32_t)((g.N + CPU - 1) / CPU);
-  const int32_t lo = max(1, g.vec_rows + 1), hi = g.thresh;
+  const int64_t lo = max<int64_t>(1, (int64_t)g.vec_rows + 1), hi = g.thresh;
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
     return (s >= lo && s <= hi) ? ((s + RPU - 1) / RPU) * n_cols : 0;
   });

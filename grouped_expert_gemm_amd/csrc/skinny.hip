@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
   const int cols = kSkinnyCols * CB;
   const int n_chunks = (int)((g.N + cols - 1) / cols);
   const int32_t thresh = g.thresh;
-  const int32_t lo = max(1, g.vec_rows + 1);   // smaller experts take the vector path
+  const int64_t lo = max<int64_t>(1, (int64_t)g.vec_rows + 1);   // smaller experts take the vector path
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
     if (s < lo || s > thresh) return 0;
     return ((s + kSkinnyRows - 1) / kSkinnyRows) * n_chunks * S;

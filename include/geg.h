@@ -115,9 +115,11 @@ typedef struct {
  *   K % 64 == 0. Paths (automatic choice): in a batch of at most 64 rows every
  *   expert takes the vector path (packed dot products on the vector ALUs,
  *   weight rows read whole, up to 4 activation rows per pass); in a larger batch
- *   experts with up to 64 rows (16 when M > 2048) take the narrow kernel
- *   (weights streamed once per 16 or 32 rows, decoded into MFMA operands, each
- *   wavefront over the whole K range) and larger experts the tiled MFMA path.
+ *   of at most 32 rows per expert on average (M <= 32 E) every expert takes the
+ *   narrow kernel (weights streamed once per 16 or 32 rows, decoded into MFMA
+ *   operands, each wavefront over the whole K range); in a larger batch experts
+ *   with up to 64 rows (16 when M > 2048) take the narrow kernel and larger
+ *   experts the tiled MFMA path.
  *   The skinny kernel (K split over wavefronts and optionally over workgroups
  *   with a fixed-order reduction) serves the same rows when forced.
  */
