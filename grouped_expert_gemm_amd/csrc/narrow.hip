@@ -17,8 +17,19 @@
 //
 // MFMA k slots: MFMA j of a step takes codes 8j .. 8j+7 of every lane's piece, so
 // its 32 k are {32 g + 8 j + i : g = 0..3, i = 0..7}; the activation operand reads
-// the same k. NF4: the fp32 product table x absmax is rounded once to fp16
-// (mixed-precision fma). MXFP4: the gfx950 scaled fp4 -> bf16 conversion.
+// the same k. NF4, 16-row units: lane groups g = 0, 1 hold the step's first
+// 64-block and g = 2, 3 its second, so each MFMA is issued twice, once per
+// block, with the other block's activation lanes reading a zero chunk of LDS; the
+// codes go through one unscaled fp16 table shared by all lanes and the fp32
+// absmax of each block scales that block's fp32 partial sums (cheaper than a
+// per-lane scaled table: the MFMA pipe has room for the extra MFMAs, the vector
+// ALUs do not; measured 4-15% faster). NF4, 32-row units: each lane scales its
+// own copy of the table by its piece's absmax (one mixed-precision fma per
+// entry; with two row blocks the doubled MFMAs and operand reads cost more than
+// the table, measured 12%). MXFP4: the
+// gfx950 scaled fp4 -> bf16 conversion applies the block scale (a piece is one
+// 32-block). Staged activation rows are 256 B with 16-byte chunk c of row r at
+// chunk c ^ (r % 16), which keeps the operand reads free of bank conflicts.
 #include <algorithm>
 
 #include "geg_device.hpp"
@@ -29,7 +40,15 @@ namespace geg {
 namespace {
 
 constexpr int kNStep = 128;                    // K per step
-constexpr int kNALd = kNStep + 8;              // staged activation row stride (halves, 272 B)
+
+// A stage buffer holds RB blocks of 16 activation rows (256 B each), each block
+// followed by a zero chunk: block r starts at r * kRBlk halves.
+constexpr int kRBlk = 16 * kNStep + 8;
+
+// Half offset of 16-byte chunk c of staged activation row r.
+__device__ __forceinline__ int nswz(int r, int c) {
+  return (r >> 4) * kRBlk + (r & 15) * kNStep + ((c ^ (r & 15)) << 3);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t nrsrc(const void* base, int64_t bytes) {
   const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int32_t)bytes);
@@ -38,15 +57,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t nrsrc(const void* base, int64_
 
 // Raw data of one K step held in registers: this thread's share of the
 // activation stage and the wavefront's weight pieces.
-template <int RB, int CBW>
+template <int RB, int CBW, int NSC>
 struct StepRaw {
   u32x4 a[RB];          // activations: rows 16r + t/16, k chunk t%16 (8 values)
   u32x4 w[CBW];         // codes of weight row n0 + 16 cb + l%16, k in [32 (l/16), +32)
-  uint32_t s[CBW];      // NF4: fp32 absmax bits; MXFP4: e8m0 byte
+  uint32_t s[CBW][NSC]; // NF4: fp32 absmax bits (of the step's two 64-blocks when
+                        // NSC = 2, else of the lane's piece); MXFP4: e8m0 byte
 };
 
-template <Fmt F, int RB, int CBW>
-__device__ __forceinline__ void load_step(StepRaw<RB, CBW>& d, const __amdgpu_buffer_rsrc_t& A,
+template <Fmt F, int RB, int CBW, int NSC>
+__device__ __forceinline__ void load_step(StepRaw<RB, CBW, NSC>& d, const __amdgpu_buffer_rsrc_t& A,
                                           const __amdgpu_buffer_rsrc_t& W,
                                           const __amdgpu_buffer_rsrc_t& S, int64_t K, int64_t N,
                                           int64_t n0, int st, int lane) {
@@ -69,17 +89,29 @@ __device__ __forceinline__ void load_step(StepRaw<RB, CBW>& d, const __amdgpu_bu
   for (int cb = 0; cb < CBW; ++cb) {
     const int64_t n = n0 + 16 * cb + (lane & 15);  // rows past N read as zero (buffer bounds)
     d.w[cb] = __builtin_amdgcn_raw_buffer_load_b128(W, (uint32_t)(n * (K >> 1) + (kc >> 1)) | mask, 0, 0);
-    if constexpr (F == NF4)
-      d.s[cb] = __builtin_amdgcn_raw_buffer_load_b32(S, (uint32_t)((n * (K >> 6) + (kc >> 6)) * 4) | mask, 0, 0);
-    else
-      d.s[cb] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, (uint32_t)(n * (K >> 5) + (kc >> 5)) | mask, 0, 0);
+    if constexpr (F == NF4 && NSC == 2) {
+      // both 64-blocks of the step for the lane's weight row (a block past K reads 0)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t kb = k0 + 64 * h;
+        d.s[cb][h] = __builtin_amdgcn_raw_buffer_load_b32(
+            S, (uint32_t)((n * (K >> 6) + (kb >> 6)) * 4) | (kb < K ? 0u : 0xFFFFFFF0u), 0, 0);
+      }
+    } else if constexpr (F == NF4) {
+      d.s[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(S, (uint32_t)((n * (K >> 6) + (kc >> 6)) * 4) | mask, 0, 0);
+    } else {
+      d.s[cb][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, (uint32_t)(n * (K >> 5) + (kc >> 5)) | mask, 0, 0);
+    }
   }
 }
 
 template <Fmt F, int RB, int CBW, int NS>
-__global__ __launch_bounds__(kThreads) void narrow_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   __shared__ Plan plan;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][RB * 16 * kNALd];
+  // two stage buffers; the zero chunk after each row block is what the
+  // activation lanes of the other 64-block read (NF4)
+  constexpr int kBuf = RB * kRBlk;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBuf];
   constexpr int RPU = 16 * RB;                     // activation rows per unit
   constexpr int CPU = 4 * 16 * CBW;                // weight rows per unit
   const int32_t n_cols = (int32_t)((g.N + CPU - 1) / CPU);
@@ -93,6 +125,25 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(GemmArgs g) {
   const int64_t K = g.K, N = g.N;
   const int nst = (int)((K + kNStep - 1) / kNStep);
   uint32_t range = 0;
+  uint32_t m4, base;
+  nf4_selector_consts(m4, base);
+  constexpr bool kSplit = F == NF4 && RB == 1;   // per-block MFMA partials, shared table
+  constexpr int kNsc = kSplit ? 2 : 1;
+  Lut16 lut{};
+  if constexpr (kSplit) lut = nf4_scaled_lut(1.0f);
+  if (t < 2 * RB)
+    *reinterpret_cast<u32x4*>(&As[t / RB][(t % RB) * kRBlk + kRBlk - 8]) = u32x4{0u, 0u, 0u, 0u};
+  // A operand offsets within a stage buffer for MFMA j of row block 0 (row
+  // l%16, chunk 4 (l/16) + j; block r adds r * kRBlk): NF4 splits them by
+  // 64-block, `ab[h]` reading the zero chunk on the lanes of the other block
+  const int am = lane & 15, ag = lane >> 4;
+  int ab[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int real = nswz(am, 4 * ag + j);
+    ab[0][j] = (!kSplit || ag < 2) ? real : kRBlk - 8;
+    ab[1][j] = ag >= 2 ? real : kRBlk - 8;
+  }
 
   for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
     const int e = find_expert(plan, g.E, u);
@@ -113,19 +164,19 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(GemmArgs g) {
       for (int cb = 0; cb < CBW; ++cb) acc[r][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // stage the activations of step st (registers -> LDS buffer st % 2)
-    auto stage = [&](const StepRaw<RB, CBW>& r, int st) {
+    auto stage = [&](const StepRaw<RB, CBW, kNsc>& r, int st) {
       uint16_t* Ab = As[st & 1];
 #pragma unroll
       for (int q = 0; q < RB; ++q) {
         u32x4 v = r.a[q];
         if constexpr (F == NF4) v = bf16x8_to_f16_slots(v, range);
-        *reinterpret_cast<u32x4*>(&Ab[(16 * q + (t >> 4)) * kNALd + 8 * (t & 15)]) = v;
+        *reinterpret_cast<u32x4*>(&Ab[nswz(16 * q + (t >> 4), t & 15)]) = v;
       }
     };
-    StepRaw<RB, CBW> raw[NS];
+    StepRaw<RB, CBW, kNsc> raw[NS];
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
-      if (i < nst) load_step<F, RB, CBW>(raw[i], A, W, S, K, N, n0, i, lane);
+      if (i < nst) load_step<F, RB, CBW, kNsc>(raw[i], A, W, S, K, N, n0, i, lane);
     __syncthreads();   // the previous unit is done with both LDS buffers
     stage(raw[0], 0);
     __syncthreads();
@@ -138,38 +189,56 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(GemmArgs g) {
       for (int jn = 0; jn < NS; ++jn) {
         const int st = s0 + jn;
         if (st < nst) {
-          StepRaw<RB, CBW>& cur = raw[jn];
+          StepRaw<RB, CBW, kNsc>& cur = raw[jn];
           if (st + 1 < nst) stage(raw[(jn + 1) % NS], st + 1);
-          if (st + NS - 1 < nst) load_step<F, RB, CBW>(raw[(jn + NS - 1) % NS], A, W, S, K, N, n0, st + NS - 1, lane);
+          if (st + NS - 1 < nst)
+            load_step<F, RB, CBW, kNsc>(raw[(jn + NS - 1) % NS], A, W, S, K, N, n0, st + NS - 1, lane);
           const uint16_t* Ab = As[st & 1];
-          // A operand of MFMA j, row block r: row 16r + l%16, k = 32 (l/16) + 8 j
-          u32x4 af[RB][4];
-#pragma unroll
-          for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              af[r][j] = *reinterpret_cast<const u32x4*>(
-                  &Ab[(16 * r + (lane & 15)) * kNALd + 32 * (lane >> 4) + 8 * j]);
 #pragma unroll
           for (int cb = 0; cb < CBW; ++cb) {
-            if constexpr (F == NF4) {
-              Lut16 lut;
-              const float sc = __builtin_bit_cast(float, cur.s[cb]);
+            if constexpr (F == NF4 && !kSplit) {
+              // 32-row units: a per-lane table scaled by the absmax of the lane's
+              // piece (one mixed-precision fma per entry), one MFMA per row block
+              Lut16 sl;
+              const float sc = __builtin_bit_cast(float, cur.s[cb][0]);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) nf4_scaled_lut_quarter_mix(sc, q, lut);
+              for (int q = 0; q < 4; ++q) nf4_scaled_lut_quarter_mix(sc, q, sl);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const u32x4 b = nf4_decode8(lut, cur.w[cb][j]);
+                const u32x4 b = nf4_decode8(sl, cur.w[cb][j]);
 #pragma unroll
-                for (int r = 0; r < RB; ++r) acc[r][cb] = mfma16<NF4>(af[r][j], b, acc[r][cb]);
+                for (int r = 0; r < RB; ++r)
+                  acc[r][cb] = mfma16<NF4>(*reinterpret_cast<const u32x4*>(&Ab[ab[0][j] + r * kRBlk]), b, acc[r][cb]);
               }
+            } else if constexpr (kSplit) {
+              // 16-row units: the step's two 64-blocks as separate MFMA partial
+              // sums, each scaled by its absmax
+              f32x4 part[2][RB];
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) part[h][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u32x4 b = nf4_decode8(lut, cur.w[cb][j], m4, base);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                  for (int r = 0; r < RB; ++r)
+                    part[h][r] = mfma16<NF4>(*reinterpret_cast<const u32x4*>(&Ab[ab[h][j] + r * kRBlk]), b, part[h][r]);
+              }
+              const float s0 = __builtin_bit_cast(float, cur.s[cb][0]);
+              const float s1 = __builtin_bit_cast(float, cur.s[cb][1]);
+#pragma unroll
+              for (int r = 0; r < RB; ++r) acc[r][cb] += s0 * part[0][r] + s1 * part[1][r];
             } else {
-              const float sc = e8m0_to_f32(cur.s[cb]);
+              const float sc = e8m0_to_f32(cur.s[cb][0]);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const u32x4 b = mxfp4_decode8(cur.w[cb][j], sc);
 #pragma unroll
-                for (int r = 0; r < RB; ++r) acc[r][cb] = mfma16<MXFP4>(af[r][j], b, acc[r][cb]);
+                for (int r = 0; r < RB; ++r)
+                  acc[r][cb] = mfma16<MXFP4>(*reinterpret_cast<const u32x4*>(&Ab[ab[0][j] + r * kRBlk]), b, acc[r][cb]);
               }
             }
           }
