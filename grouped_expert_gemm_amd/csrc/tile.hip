@@ -180,16 +180,16 @@ __device__ __forceinline__ void load_b(RawB& r, const TileSrc& t, int st, bool o
     r.s = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(S, t.s_off, (uint32_t)st * t.s_step, 0));
 }
 
-// One row chunk of raw activations -> LDS. Chunks past the contraction length
-// C are zeroed (NF4 forward has C % 64 == 0; MXFP4 can have a 32-wide tail and
-// dgrad an 8-aligned one).
-template <Fmt F, bool DG>
+// One row chunk of raw activations -> LDS. With TAIL, chunks past the
+// contraction length C are zeroed (NF4 forward has C % 64 == 0; MXFP4 can have a
+// 32-wide tail and dgrad an 8-aligned one).
+template <Fmt F, bool DG, bool TAIL>
 __device__ __forceinline__ void store_a_piece(const RawA& r, int i, uint16_t* As, int64_t k0,
                                               int64_t C, int wave, int lane) {
   const int chunk = lane & 7;
   const int row = 32 * wave + 8 * i + (lane >> 3);
   u32x4 v = r.v[i];
-  if constexpr (F == MXFP4 || DG) v = k0 + 8 * chunk < C ? v : u32x4{0u, 0u, 0u, 0u};
+  if constexpr (TAIL) v = k0 + 8 * chunk < C ? v : u32x4{0u, 0u, 0u, 0u};
   *reinterpret_cast<u32x4*>(&As[swz(row, chunk)]) = v;
 }
 
@@ -323,7 +323,7 @@ struct Ops {
 //   stage after it (entries 0-7, from the raw scale already in registers)
 //   barrier X at the end frees the current buffers.
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
-template <Fmt F, bool DG, int H, int P>
+template <Fmt F, bool DG, bool TAIL, int H, int P>
 __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
                                            int st, int nst, int wave, int lane, int bcol,
                                            RawA& ra, RawB (&rb)[2], BDec<F>& dec, Ops& ops,
@@ -372,7 +372,7 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
     // staging of the next stage (on the last stage it writes stale data into the
     // free buffer, which nothing reads; this keeps the groups free of branches)
     if (g < 4) {
-      store_a_piece<F, DG>(ra, g, L.a[nxt], k1, C, wave, lane);
+      store_a_piece<F, DG, TAIL>(ra, g, L.a[nxt], k1, C, wave, lane);
       load_a_piece(ra, g, src, st + 2, st + 2 < nst);
     }
     if (g == 0 || g == 1) b_setup<F>(dec, g + 2, rb[P ^ 1], k1, K);
@@ -396,7 +396,7 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
 
 // Main loop over the K stages of one tile (H = the wavefront's active 64-row
 // halves; every wavefront runs the same barriers whatever its H).
-template <Fmt F, bool DG, int H>
+template <Fmt F, bool DG, bool TAIL, int H>
 __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
                                            int wave, int lane, f32x4 (&acc)[8][4]) {
   const int wm = wave >> 2, wn = wave & 3;
@@ -419,7 +419,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   load_b<F>(rb[0], src, 0, true);
   load_b<F>(rb[1], src, 1, nst > 1);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_a_piece<F, DG>(ra, q, L.a[0], 0, C, wave, lane);
+  for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], 0, C, wave, lane);
   {
     NF4Half h;
     u32x2 even;
@@ -442,15 +442,18 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
   for (int st = 0; st < nst; st += 2) {
-    tile_stage<F, DG, H, 0>(L, src, C, K, st, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff, m4, base);
+    tile_stage<F, DG, TAIL, H, 0>(L, src, C, K, st, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff, m4, base);
     if (st + 1 < nst)
-      tile_stage<F, DG, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff, m4, base);
+      tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff,
+                                    m4, base);
   }
 }
 
 // Forward (DG = false): out[M, N] = a . W^T per expert. dgrad (DG = true, NF4):
 // out[M, K] = dY . W per expert, with `a16` holding dY as fp16.
-template <Fmt F, bool DG>
+// TAIL: the contraction length is not a multiple of 64, so the last stage's
+// activation chunks past it must be zeroed (MXFP4 K, dgrad N).
+template <Fmt F, bool DG, bool TAIL>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) TileLds<DG> L;
@@ -493,11 +496,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, DG, 2>(L, src, C, g.K, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 2>(L, src, C, g.K, wave, lane, acc);
     else if (vrows > 0)
-      run_tile_h<F, DG, 1>(L, src, C, g.K, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 1>(L, src, C, g.K, wave, lane, acc);
     else
-      run_tile_h<F, DG, 0>(L, src, C, g.K, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 0>(L, src, C, g.K, wave, lane, acc);
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores
@@ -543,14 +546,19 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
   if (fmt == NF4)
-    hipLaunchKernelGGL((tile_kernel<NF4, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+    hipLaunchKernelGGL((tile_kernel<NF4, false, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+  else if (g.K % BK)
+    hipLaunchKernelGGL((tile_kernel<MXFP4, false, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
   else
-    hipLaunchKernelGGL((tile_kernel<MXFP4, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+    hipLaunchKernelGGL((tile_kernel<MXFP4, false, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((tile_kernel<NF4, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
+  if (g.N % BK)
+    hipLaunchKernelGGL((tile_kernel<NF4, true, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((tile_kernel<NF4, true, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
   return hipGetLastError();
 }
 
