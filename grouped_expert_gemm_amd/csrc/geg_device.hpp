@@ -197,6 +197,55 @@ __device__ __forceinline__ void nf4_selector_consts(uint32_t& m4, uint32_t& base
   asm volatile("" : "+s"(m4));
 }
 
+// ------------------------------------------------------------------ NF4 byte table (LDS)
+// The decode-class kernels look codes up a byte at a time in LDS instead of in
+// registers. Entry v (a code byte) is the fp16 pair {T[v >> 4], T[v & 15]}, i.e.
+// the weights k = 2b and 2b + 1 of byte b in natural order. The 256 entries are
+// stored 64 times, interleaved (copy c of entry v is word 64 v + c), and lane l
+// reads copy l: the lanes of a lookup hit 64 different banks whatever the codes,
+// so a lookup is one conflict-free 32-bit LDS read, and its byte address
+// {4 l, code byte} is one v_perm. About 0.5 vector instruction per code against
+// about 3 for the register table.
+constexpr int kNf4ByteLutWords = 256 * 64;
+
+// Fill the table (every thread of a kThreads workgroup takes part; the caller
+// places a barrier before the first lookup). Word quad q = 256 i + t holds copies
+// 4 (t % 16) .. +3 of entry 16 i + t / 16, whose high nibble is i and low nibble
+// t / 16; the quads of a wavefront are contiguous, so the stores are
+// conflict-free.
+__device__ __forceinline__ void nf4_byte_lut_fill(uint32_t* lut) {
+  static_assert(kThreads == 256, "the fill covers 4096 word quads with 256 threads");
+  const int t = threadIdx.x;
+  const int lo = t >> 4;
+  _Float16 lv = (_Float16)0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (lo == j) lv = (_Float16)nf4_value(j);
+  const uint32_t high_half = (uint32_t)__builtin_bit_cast(uint16_t, lv) << 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t v = high_half | __builtin_bit_cast(uint16_t, (_Float16)nf4_value(i));
+    *reinterpret_cast<u32x4*>(lut + 4 * (256 * i + t)) = u32x4{v, v, v, v};
+  }
+}
+
+// Byte offset of the lane's copy: 4 * lane (kept in byte 0 of the address).
+__device__ __forceinline__ uint32_t nf4_byte_lut_lane(int lane) { return 4u * (uint32_t)lane; }
+
+// Decode 8 NF4 codes from one dword of packed bytes (byte b holds k = 2b in its
+// high nibble and k = 2b+1 in its low nibble) to 8 fp16 values in natural k
+// order: out[b] = {k 2b, k 2b+1}.
+__device__ __forceinline__ u32x4 nf4_byte_lut_decode8(const uint32_t* lut, uint32_t x, uint32_t lane_off) {
+  u32x4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // byte address {lane_off, byte b of x, 0, 0} = 256 * code byte + 4 * lane
+    const uint32_t addr = perm(x, lane_off, 0x0C0C0400u | ((uint32_t)b << 8));
+    r[b] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr);
+  }
+  return r;
+}
+
 // ------------------------------------------------------------------ MXFP4 decode
 // e8m0 byte -> fp32 scale 2^(x-127): normal for 1..254, 2^-127 (subnormal) for 0,
 // NaN for 255.
@@ -284,51 +333,67 @@ struct Plan {
   int32_t upre[kMaxExperts + 1];   // exclusive prefix of work units
 };
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-template <typename T>
-__device__ __forceinline__ T wave_inclusive_scan(T v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const T o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes of a wavefront, with unsigned adds
+// that saturate at 2^32 - 1. DPP row shifts by 1, 2, 4 and 8 scan each row of 16
+// lanes; row broadcast 15 then adds row 0's total to row 1 and row 2's to row 3,
+// and row broadcast 31 adds the total of rows 0-1 to rows 2-3. Lanes whose
+// source is outside the row (or rows the mask leaves out) add 0.
+__device__ __forceinline__ uint32_t wave_scan_sat(uint32_t v) {
+  auto step = [](uint32_t x, uint32_t t) { return __builtin_elementwise_add_sat(x, t); };
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
   return v;
 }
 
+struct NoOverlap {
+  __device__ void operator()() const {}
+};
+
 // Fill plan.off / plan.upre (wavefront 0 scans 64 experts at a time, the other
 // wavefronts wait at the barrier). `units(size)` gives the number of work units
-// of an expert with `size` (clamped) rows. Returns the total number of units.
-template <typename UnitFn>
+// of an expert with `size` (clamped) rows. `overlap()` runs on every thread while
+// the first 64 sizes are in flight (a kernel's LDS set-up, say). Returns the
+// total number of units. Row counts are clamped to M + 1 <= 2^31 before the
+// scan, so the saturating 32-bit sums are exact up to the point where they pass
+// M, and offsets are clamped to M after it.
+template <typename UnitFn, typename Overlap = NoOverlap>
 __device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E, int64_t M,
-                              uint32_t* err_word, UnitFn units) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int64_t run = 0;
-    int32_t urun = 0;
-    uint32_t err = 0;
+                              uint32_t* err_word, UnitFn units, Overlap overlap = Overlap{}) {
+  const int t = threadIdx.x;
+  int32_t first = 0;
+  if (t < 64 && t < E) first = sizes[t];
+  overlap();
+  if (t < 64) {
+    const int lane = t;
+    const uint32_t m = (uint32_t)M;
+    uint32_t run = 0, urun = 0, err = 0;
     for (int base = 0; base < E; base += 64) {
       const int e = base + lane;
-      int64_t s = e < E ? (int64_t)sizes[e] : 0;
-      if (s < 0) {
+      int32_t raw = base == 0 ? first : (e < E ? sizes[e] : 0);
+      if (raw < 0) {
         err |= kErrNegativeSize;
-        s = 0;
+        raw = 0;
       }
-      if (s > M) s = M + 1;  // keeps the running sum small; still exceeds M
-      const int64_t incl = wave_inclusive_scan<int64_t>(s, lane);
-      const int64_t lo = min(run + incl - s, M), hi = min(run + incl, M);
-      const int32_t uc = e < E ? units((int32_t)(hi - lo)) : 0;
-      const int32_t uincl = wave_inclusive_scan<int32_t>(uc, lane);
+      const uint32_t s = min((uint32_t)raw, m + 1u);
+      const uint32_t incl = __builtin_elementwise_add_sat(wave_scan_sat(s), run);
+      const uint32_t lo = min(incl - s, m), hi = min(incl, m);
+      const uint32_t uc = e < E ? (uint32_t)units((int32_t)(hi - lo)) : 0u;
+      const uint32_t uincl = wave_scan_sat(uc) + urun;
       if (e < E) {
         p.off[e] = (int32_t)lo;
-        p.upre[e] = urun + uincl - uc;
+        p.upre[e] = (int32_t)(uincl - uc);
       }
-      run += __shfl(incl, 63, 64);
-      urun += __shfl(uincl, 63, 64);
+      run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      urun = (uint32_t)__builtin_amdgcn_readlane((int)uincl, 63);
     }
     if (lane == 0) {
-      p.off[E] = (int32_t)min(run, M);
-      p.upre[E] = urun;
-      if (run > M) err |= kErrSizesExceedM;
+      p.off[E] = (int32_t)min(run, m);
+      p.upre[E] = (int32_t)urun;
+      if (run > m) err |= kErrSizesExceedM;
     }
     if (err) atomicOr(err_word, err);
   }
@@ -336,15 +401,21 @@ __device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E,
   return p.upre[E];
 }
 
-// Expert owning work unit u: the largest e with upre[e] <= u (experts with no
-// units are skipped because their upre equals the next expert's).
+// Expert owning work unit u (uniform over the wavefront, which must be whole):
+// the largest e with upre[e] <= u. upre is nondecreasing with upre[0] = 0, so
+// that e is the number of e' in [1, E) with upre[e'] <= u, counted 64 experts per
+// ballot (experts with no units share the next expert's upre and are passed).
 __device__ __forceinline__ int find_expert(const Plan& p, int E, int32_t u) {
-  int lo = 0, hi = E;  // invariant: upre[lo] <= u < upre[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (p.upre[mid] <= u) lo = mid; else hi = mid;
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int base = 1; base < E; base += 64) {
+    const int e = base + lane;
+    const bool le = e < E && p.upre[e] <= u;
+    const uint64_t b = __ballot(le);
+    cnt += __builtin_popcountll(b);
+    if (b != ~0ull) break;   // the rest lie past u
   }
-  return lo;
+  return cnt;
 }
 
 }  // namespace geg

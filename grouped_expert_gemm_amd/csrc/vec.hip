@@ -17,11 +17,13 @@
 // [32c, 32c + 32)); it decodes them in registers, takes packed fp32-accumulated
 // dot products with the activation rows' slice of that chunk, and the row group's
 // lanes add their partial sums with cross-lane shuffles. Wavefronts are
-// independent (no LDS beyond the routing plan, no barriers after it).
+// independent (LDS holds only the routing plan and the NF4 byte table, both
+// written before the one barrier).
 //
-// NF4: codes go through the unscaled fp16 table; the fp32 absmax of the chunk's
-// 64-block scales the chunk's fp32 dot product (activations as fp16 in the NF4
-// slot order, range-checked as in the other paths). MXFP4: the gfx950 scaled fp4
+// NF4: code bytes go through the unscaled fp16 byte table in LDS (one 32-bit
+// read per two codes, natural k order); the fp32 absmax of the chunk's 64-block
+// scales the chunk's fp32 dot product (activations as fp16, range-checked as in
+// the other paths). The 64 KiB table leaves room for two workgroups per CU. MXFP4: the gfx950 scaled fp4
 // -> bf16 conversion applies 2^(e8m0-127); bf16 activations pair with the decoded
 // bf16 values in natural order.
 #include <algorithm>
@@ -57,7 +59,7 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 template <Fmt F, int LPR, int RV, int U>
-__device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, int e, int64_t n0,
+__device__ __forceinline__ void vec_unit(const GemmArgs& g, const uint32_t* blut, int e, int64_t n0,
                                          int64_t row0, int rows, int lane, uint32_t& range) {
   constexpr int G = 64 / LPR;
   const int64_t N = g.N, K = g.K;
@@ -68,8 +70,7 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, in
       F == NF4 ? vrsrc(reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6), N * (K >> 6) * 4)
                : vrsrc(reinterpret_cast<const uint8_t*>(g.scales) + (int64_t)e * N * (K >> 5), N * (K >> 5));
   const __amdgpu_buffer_rsrc_t A = vrsrc(g.a + row0 * K, (int64_t)rows * K * 2);
-  uint32_t m4, base;
-  nf4_selector_consts(m4, base);
+  const uint32_t lane_off = nf4_byte_lut_lane(lane);
   float acc[U][RV];
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -114,7 +115,7 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, in
 #pragma unroll
       for (int m = 0; m < RV; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) av[m][j] = bf16x8_to_f16_slots(av[m][j], range);
+        for (int j = 0; j < 4; ++j) av[m][j] = bf16x8_to_f16(av[m][j], range);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -124,7 +125,7 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, in
         for (int m = 0; m < RV; ++m) d[m] = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4 w = nf4_decode8(lut, code[u][j], m4, base);   // codes k = 8j .. 8j+7, slot order
+          const u32x4 w = nf4_byte_lut_decode8(blut, code[u][j], lane_off);   // k = 8j .. 8j+7
 #pragma unroll
           for (int m = 0; m < RV; ++m)
             if (m < rows)
@@ -164,18 +165,19 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const Lut16& lut, in
 template <Fmt F, int LPR, int RV, int U>
 __global__ __launch_bounds__(kThreads) void vec_kernel(GemmArgs g) {
   __shared__ Plan plan;
+  __shared__ __attribute__((aligned(16))) uint32_t blut[F == NF4 ? kNf4ByteLutWords : 4];
   constexpr int RPU = U * (64 / LPR);   // weight rows per unit
   const int32_t n_units = (int32_t)((g.N + RPU - 1) / RPU);
   const int32_t vr = g.vec_rows;
   // an expert with s rows: ceil(s / RV) row chunks x n_units row blocks
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
     return (s >= 1 && s <= vr) ? ((s + RV - 1) / RV) * n_units : 0;
+  }, [&] {
+    if constexpr (F == NF4) nf4_byte_lut_fill(blut);   // ordered by the plan's barrier
   });
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t range = 0;
-  Lut16 lut{};
-  if constexpr (F == NF4) lut = nf4_scaled_lut(1.0f);
   const int stride = gridDim.x * (kThreads / 64);
   for (int32_t u = blockIdx.x * (kThreads / 64) + wave; u < total; u += stride) {
     const int e = find_expert(plan, g.E, u);
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void vec_kernel(GemmArgs g) {
     const int64_t n0 = (int64_t)(lu % n_units) * RPU;
     const int64_t row0 = plan.off[e] + (int64_t)(lu / n_units) * RV;
     const int rows = (int)min<int64_t>(RV, plan.off[e + 1] - row0);
-    vec_unit<F, LPR, RV, U>(g, lut, e, n0, row0, rows, lane, range);
+    vec_unit<F, LPR, RV, U>(g, blut, e, n0, row0, rows, lane, range);
   }
   if constexpr (F == NF4) {
     if (range_overflowed(range)) atomicOr(g.err, kErrFp16Range);
