@@ -201,46 +201,65 @@ __device__ __forceinline__ void nf4_selector_consts(uint32_t& m4, uint32_t& base
 // The decode-class kernels look codes up a byte at a time in LDS instead of in
 // registers. Entry v (a code byte) is the fp16 pair {T[v >> 4], T[v & 15]}, i.e.
 // the weights k = 2b and 2b + 1 of byte b in natural order. The 256 entries are
-// stored 64 times, interleaved (copy c of entry v is word 64 v + c), and lane l
-// reads copy l: the lanes of a lookup hit 64 different banks whatever the codes,
-// so a lookup is one conflict-free 32-bit LDS read, and its byte address
-// {4 l, code byte} is one v_perm. About 0.5 vector instruction per code against
-// about 3 for the register table.
+// stored C times, interleaved (copy c of entry v is word C v + c), and lane l
+// reads copy l % C. LDS serves a 32-bit read 32 lanes at a time, so with C = 32
+// or 64 the lanes of one pass hit 32 different banks whatever the codes: a
+// lookup is one conflict-free read. Its byte address {4 (l % C), code byte} is
+// one v_perm for C = 64 (a 64 KiB table) and a bit-field extract plus a
+// shift-or for C = 32 (32 KiB). About 0.5 or 1 vector instruction per code
+// against about 3 for the register table.
+template <int C>
+constexpr int nf4_byte_lut_words() { return 256 * C; }
 constexpr int kNf4ByteLutWords = 256 * 64;
 
-// Fill the table (every thread of a kThreads workgroup takes part; the caller
-// places a barrier before the first lookup). Word quad q = 256 i + t holds copies
-// 4 (t % 16) .. +3 of entry 16 i + t / 16, whose high nibble is i and low nibble
-// t / 16; the quads of a wavefront are contiguous, so the stores are
-// conflict-free.
+// Fill the table (every thread of an NT-thread workgroup takes part; the caller
+// places a barrier before the first lookup). Word quad q = NT i + t holds copies
+// 4 (q % (C / 4)) .. +3 of entry q / (C / 4); consecutive threads fill
+// consecutive quads, so the stores are conflict-free.
+template <int C = 64, int NT = kThreads>
 __device__ __forceinline__ void nf4_byte_lut_fill(uint32_t* lut) {
-  static_assert(kThreads == 256, "the fill covers 4096 word quads with 256 threads");
+  static_assert(C == 32 || C == 64, "32 or 64 copies");
+  constexpr int Q = C / 4;                    // quads per entry
+  constexpr int kQuads = 256 * Q;
+  static_assert(NT % (16 * Q) == 0 && kQuads % NT == 0, "threads must tile the entries evenly");
+  constexpr int R = NT / (16 * Q);            // high-nibble values per pass
   const int t = threadIdx.x;
-  const int lo = t >> 4;
+  // entry of quad NT i + t: (NT i + t) / Q = 16 R i + t / Q, so its low nibble is
+  // (t / Q) % 16 and its high nibble R i + t / (16 Q)
+  const int lo = (t / Q) & 15, sub = t / (16 * Q);
   _Float16 lv = (_Float16)0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     if (lo == j) lv = (_Float16)nf4_value(j);
   const uint32_t high_half = (uint32_t)__builtin_bit_cast(uint16_t, lv) << 16;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t v = high_half | __builtin_bit_cast(uint16_t, (_Float16)nf4_value(i));
-    *reinterpret_cast<u32x4*>(lut + 4 * (256 * i + t)) = u32x4{v, v, v, v};
+  for (int i = 0; i < kQuads / NT; ++i) {
+    uint32_t low_half = __builtin_bit_cast(uint16_t, (_Float16)nf4_value(R * i));
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+      if (sub == r) low_half = __builtin_bit_cast(uint16_t, (_Float16)nf4_value(R * i + r));
+    const uint32_t v = high_half | low_half;
+    *reinterpret_cast<u32x4*>(lut + 4 * (NT * i + t)) = u32x4{v, v, v, v};
   }
 }
 
-// Byte offset of the lane's copy: 4 * lane (kept in byte 0 of the address).
-__device__ __forceinline__ uint32_t nf4_byte_lut_lane(int lane) { return 4u * (uint32_t)lane; }
+// Byte offset of the lane's copy (kept in the low bits of the address).
+template <int C = 64>
+__device__ __forceinline__ uint32_t nf4_byte_lut_lane(int lane) { return 4u * (uint32_t)(lane % C); }
 
 // Decode 8 NF4 codes from one dword of packed bytes (byte b holds k = 2b in its
 // high nibble and k = 2b+1 in its low nibble) to 8 fp16 values in natural k
 // order: out[b] = {k 2b, k 2b+1}.
+template <int C = 64>
 __device__ __forceinline__ u32x4 nf4_byte_lut_decode8(const uint32_t* lut, uint32_t x, uint32_t lane_off) {
   u32x4 r;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    // byte address {lane_off, byte b of x, 0, 0} = 256 * code byte + 4 * lane
-    const uint32_t addr = perm(x, lane_off, 0x0C0C0400u | ((uint32_t)b << 8));
+    uint32_t addr;
+    if constexpr (C == 64)
+      addr = perm(x, lane_off, 0x0C0C0400u | ((uint32_t)b << 8));   // {lane_off, byte b of x, 0, 0}
+    else
+      addr = (__builtin_amdgcn_ubfe(x, 8 * b, 8) << 7) | lane_off;  // 128 * code byte + 4 (lane % 32)
     r[b] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr);
   }
   return r;
@@ -307,6 +326,12 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16(const u32x4& x, uint32_t& range) 
   return r;
 }
 
+// 4 bf16 (2 dwords) -> 4 fp16, natural order, with the same range tracking.
+__device__ __forceinline__ u32x2 bf16x4_to_f16(const u32x2& x, uint32_t& range) {
+  const u32x4 r = bf16x8_to_f16(u32x4{x[0], x[1], 0u, 0u}, range);
+  return u32x2{r[0], r[1]};
+}
+
 __device__ __forceinline__ bool range_overflowed(uint32_t range) {
   return (range & 0xFFFFu) >= 0x7C00u || (range >> 16) >= 0x7C00u;
 }
@@ -360,9 +385,10 @@ struct NoOverlap {
 // total number of units. Row counts are clamped to M + 1 <= 2^31 before the
 // scan, so the saturating 32-bit sums are exact up to the point where they pass
 // M, and offsets are clamped to M after it.
+// `off` and `upre` each hold E + 1 entries in LDS.
 template <typename UnitFn, typename Overlap = NoOverlap>
-__device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E, int64_t M,
-                              uint32_t* err_word, UnitFn units, Overlap overlap = Overlap{}) {
+__device__ int32_t build_plan(int32_t* off, int32_t* upre, const int32_t* __restrict__ sizes, int E,
+                              int64_t M, uint32_t* err_word, UnitFn units, Overlap overlap = Overlap{}) {
   const int t = threadIdx.x;
   int32_t first = 0;
   if (t < 64 && t < E) first = sizes[t];
@@ -384,38 +410,46 @@ __device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E,
       const uint32_t uc = e < E ? (uint32_t)units((int32_t)(hi - lo)) : 0u;
       const uint32_t uincl = wave_scan_sat(uc) + urun;
       if (e < E) {
-        p.off[e] = (int32_t)lo;
-        p.upre[e] = (int32_t)(uincl - uc);
+        off[e] = (int32_t)lo;
+        upre[e] = (int32_t)(uincl - uc);
       }
       run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       urun = (uint32_t)__builtin_amdgcn_readlane((int)uincl, 63);
     }
     if (lane == 0) {
-      p.off[E] = (int32_t)min(run, m);
-      p.upre[E] = (int32_t)urun;
+      off[E] = (int32_t)min(run, m);
+      upre[E] = (int32_t)urun;
       if (run > m) err |= kErrSizesExceedM;
     }
     if (err) atomicOr(err_word, err);
   }
   __syncthreads();
-  return p.upre[E];
+  return upre[E];
+}
+
+template <typename UnitFn, typename Overlap = NoOverlap>
+__device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E, int64_t M,
+                              uint32_t* err_word, UnitFn units, Overlap overlap = Overlap{}) {
+  return build_plan(p.off, p.upre, sizes, E, M, err_word, units, overlap);
 }
 
 // Expert owning work unit u (uniform over the wavefront, which must be whole):
 // the largest e with upre[e] <= u. upre is nondecreasing with upre[0] = 0, so
 // that e is the number of e' in [1, E) with upre[e'] <= u, counted 64 experts per
 // ballot (experts with no units share the next expert's upre and are passed).
-__device__ __forceinline__ int find_expert(const Plan& p, int E, int32_t u) {
+__device__ __forceinline__ int find_expert(const int32_t* upre, int E, int32_t u) {
   const int lane = threadIdx.x & 63;
   int cnt = 0;
   for (int base = 1; base < E; base += 64) {
     const int e = base + lane;
-    const bool le = e < E && p.upre[e] <= u;
+    const bool le = e < E && upre[e] <= u;
     const uint64_t b = __ballot(le);
     cnt += __builtin_popcountll(b);
     if (b != ~0ull) break;   // the rest lie past u
   }
   return cnt;
 }
+
+__device__ __forceinline__ int find_expert(const Plan& p, int E, int32_t u) { return find_expert(p.upre, E, u); }
 
 }  // namespace geg

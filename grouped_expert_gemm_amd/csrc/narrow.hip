@@ -107,6 +107,8 @@ __device__ __forceinline__ void load_step(StepRaw<RB, CBW, NSC>& d, const __amdg
 
 template <Fmt F, int RB, int CBW, int NS>
 __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
+  // step st stages step st+1 from registers loaded two steps earlier
+  static_assert(NS >= 3, "the staged step must already be in registers");
   __shared__ Plan plan;
   // two stage buffers; the zero chunk after each row block is what the
   // activation lanes of the other 64-block read (NF4)
