@@ -65,7 +65,7 @@ struct StepRaw {
                         // NSC = 2, else of the lane's piece); MXFP4: e8m0 byte
 };
 
-template <Fmt F, int RB, int CBW, int NSC>
+template <Fmt F, int RB, int CBW, int NSC, bool SSC>
 __device__ __forceinline__ void load_step(StepRaw<RB, CBW, NSC>& d, const __amdgpu_buffer_rsrc_t& A,
                                           const __amdgpu_buffer_rsrc_t& W,
                                           const __amdgpu_buffer_rsrc_t& S, int64_t K, int64_t N,
@@ -90,12 +90,15 @@ __device__ __forceinline__ void load_step(StepRaw<RB, CBW, NSC>& d, const __amdg
     const int64_t n = n0 + 16 * cb + (lane & 15);  // rows past N read as zero (buffer bounds)
     d.w[cb] = __builtin_amdgcn_raw_buffer_load_b128(W, (uint32_t)(n * (K >> 1) + (kc >> 1)) | mask, 0, 0);
     if constexpr (F == NF4 && NSC == 2) {
-      // both 64-blocks of the step for the lane's weight row (a block past K reads 0)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t kb = k0 + 64 * h;
-        d.s[cb][h] = __builtin_amdgcn_raw_buffer_load_b32(
-            S, (uint32_t)((n * (K >> 6) + (kb >> 6)) * 4) | (kb < K ? 0u : 0xFFFFFFF0u), 0, 0);
+      // both 64-blocks of the step for the lane's weight row in one load, unless
+      // the unit's scales are staged in LDS. When K % 128 == 64 the second value
+      // of the last step is the next row's first scale (or zero past the buffer);
+      // it multiplies a partial sum of zero activations.
+      if constexpr (!SSC) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(
+            S, (uint32_t)((n * (K >> 6) + (k0 >> 6)) * 4) | (k0 < K ? 0u : 0xFFFFFFF0u), 0, 0);
+        d.s[cb][0] = v[0];
+        d.s[cb][1] = v[1];
       }
     } else if constexpr (F == NF4) {
       d.s[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(S, (uint32_t)((n * (K >> 6) + (kc >> 6)) * 4) | mask, 0, 0);
@@ -105,7 +108,11 @@ __device__ __forceinline__ void load_step(StepRaw<RB, CBW, NSC>& d, const __amdg
   }
 }
 
-template <Fmt F, int RB, int CBW, int NS>
+// SSC: the unit's NF4 absmax values (K <= 2048: at most 32 blocks per row) are
+// staged in LDS once per unit instead of being loaded with every step; per-step
+// loads of 4-byte values from 16 rows cost as many memory requests as the
+// weights themselves.
+template <Fmt F, int RB, int CBW, int NS, bool SSC>
 __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   // step st stages step st+1 from registers loaded two steps earlier
   static_assert(NS >= 3, "the staged step must already be in registers");
@@ -131,6 +138,9 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   nf4_selector_consts(m4, base);
   constexpr bool kSplit = F == NF4 && RB == 1;   // per-block MFMA partials, shared table
   constexpr int kNsc = kSplit ? 2 : 1;
+  static_assert(!SSC || kSplit, "staged scales serve the 16-row NF4 units");
+  constexpr int kSscLd = 34;                       // floats per staged row (even, bank-spreading)
+  __shared__ __attribute__((aligned(16))) float Ssc[SSC ? 64 * CBW * kSscLd : 2];
   Lut16 lut{};
   if constexpr (kSplit) lut = nf4_scaled_lut(1.0f);
   if (t < 2 * RB)
@@ -175,26 +185,44 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
         *reinterpret_cast<u32x4*>(&Ab[nswz(16 * q + (t >> 4), t & 15)]) = v;
       }
     };
+    // staged scales: thread t loads 8 absmax values (blocks 8 (t%4) .. +7) of
+    // unit row t/4 (rows past N read as zero; blocks past the row read the next
+    // row's values, which only meet zero partial sums)
+    u32x4 sraw[2];
+    if constexpr (SSC) {
+      static_assert(kThreads == 256 && CBW == 1, "one thread per 8 blocks of 64 rows");
+      const int64_t nrow = (int64_t)(lu % n_cols) * CPU + (t >> 2);
+      const uint32_t off = (uint32_t)((nrow * (K >> 6) + 8 * (t & 3)) * 4);
+      sraw[0] = __builtin_amdgcn_raw_buffer_load_b128(S, off, 0, 0);
+      sraw[1] = __builtin_amdgcn_raw_buffer_load_b128(S, off + 16, 0, 0);
+    }
     StepRaw<RB, CBW, kNsc> raw[NS];
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      if (i < nst) load_step<F, RB, CBW, kNsc>(raw[i], A, W, S, K, N, n0, i, lane);
-    __syncthreads();   // the previous unit is done with both LDS buffers
+    for (int i = 0; i < NS - 1; ++i) load_step<F, RB, CBW, kNsc, SSC>(raw[i], A, W, S, K, N, n0, i, lane);
+    __syncthreads();   // the previous unit is done with both LDS buffers and the scales
     stage(raw[0], 0);
+    if constexpr (SSC) {
+      float* dst = &Ssc[(t >> 2) * kSscLd + 8 * (t & 3)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2*>(dst + 2 * q) = u32x2{sraw[q >> 1][2 * (q & 1)], sraw[q >> 1][2 * (q & 1) + 1]};
+    }
     __syncthreads();
 
     // Step st: stage st+1, load st+NS-1, compute st from LDS buffer st % 2 and
     // the step's weight registers. raw[] rotates through NS slots (compile-time
-    // indices: the loop body covers NS steps).
-    for (int s0 = 0; s0 < nst; s0 += NS) {
-#pragma unroll
-      for (int jn = 0; jn < NS; ++jn) {
-        const int st = s0 + jn;
-        if (st < nst) {
+    // indices: the loop body covers NS steps). Loads of steps past the last read
+    // zeros (their offsets lie past every buffer) and the stage they fill is never
+    // read, so every step issues the same loads and the waits for them are
+    // counted exactly; full groups of NS steps run without branches, and the last
+    // nst % NS steps follow.
+    auto step = [&](int jn, int st) {
+          // the scheduler would otherwise pull the next steps' decode ahead of
+          // this step's, and with it waits for loads that are still in flight
+          __builtin_amdgcn_sched_barrier(0);
           StepRaw<RB, CBW, kNsc>& cur = raw[jn];
-          if (st + 1 < nst) stage(raw[(jn + 1) % NS], st + 1);
-          if (st + NS - 1 < nst)
-            load_step<F, RB, CBW, kNsc>(raw[(jn + NS - 1) % NS], A, W, S, K, N, n0, st + NS - 1, lane);
+          stage(raw[(jn + 1) % NS], st + 1);
+          load_step<F, RB, CBW, kNsc, SSC>(raw[(jn + NS - 1) % NS], A, W, S, K, N, n0, st + NS - 1, lane);
           const uint16_t* Ab = As[st & 1];
 #pragma unroll
           for (int cb = 0; cb < CBW; ++cb) {
@@ -229,8 +257,16 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
                   for (int r = 0; r < RB; ++r)
                     part[h][r] = mfma16<NF4>(*reinterpret_cast<const u32x4*>(&Ab[ab[h][j] + r * kRBlk]), b, part[h][r]);
               }
-              const float s0 = __builtin_bit_cast(float, cur.s[cb][0]);
-              const float s1 = __builtin_bit_cast(float, cur.s[cb][1]);
+              float s0, s1;
+              if constexpr (SSC) {
+                const float2 sv = *reinterpret_cast<const float2*>(
+                    &Ssc[(16 * (CBW * wave + cb) + (lane & 15)) * kSscLd + 2 * st]);
+                s0 = sv.x;
+                s1 = sv.y;
+              } else {
+                s0 = __builtin_bit_cast(float, cur.s[cb][0]);
+                s1 = __builtin_bit_cast(float, cur.s[cb][1]);
+              }
 #pragma unroll
               for (int r = 0; r < RB; ++r) acc[r][cb] += s0 * part[0][r] + s1 * part[1][r];
             } else {
@@ -245,9 +281,15 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
             }
           }
           __syncthreads();   // buffer st+1 complete; buffer st free for step st+2
-        }
-      }
+    };
+    const int full = nst - nst % NS;
+    for (int s0 = 0; s0 < full; s0 += NS) {
+#pragma unroll
+      for (int jn = 0; jn < NS; ++jn) step(jn, s0 + jn);
     }
+#pragma unroll
+    for (int jn = 0; jn < NS - 1; ++jn)
+      if (full + jn < nst) step(jn, full + jn);
     // acc[r][cb][q]: activation row 16r + 4 (l/16) + q, weight row n0 + 16 cb + l%16
 #pragma unroll
     for (int cb = 0; cb < CBW; ++cb) {
@@ -268,9 +310,9 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   }
 }
 
-template <Fmt F, int RB, int CBW, int NS>
+template <Fmt F, int RB, int CBW, int NS, bool SSC = false>
 hipError_t launch_n(const GemmArgs& g, int cus, hipStream_t s) {
-  auto k = narrow_kernel<F, RB, CBW, NS>;
+  auto k = narrow_kernel<F, RB, CBW, NS, SSC>;
   static int per_cu = 0;
   if (per_cu == 0) {
     int b = 0;
@@ -285,13 +327,20 @@ hipError_t launch_n(const GemmArgs& g, int cus, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef NARROW_NS1
+#define NARROW_NS1 4
+#endif
+
 template <Fmt F>
 hipError_t launch_narrow_fmt(const GemmArgs& g, int cus, hipStream_t s) {
   // 32-row units (two 16-row blocks per wavefront, 128 weight rows per unit) when
   // the batch's experts are expected to hold more than 16 rows; otherwise 16-row
   // units over 64 weight rows (more, smaller units keep more wavefronts busy).
-  return g.thresh > 16 && g.M > 16 * (int64_t)std::min<int64_t>(g.E, g.M) ? launch_n<F, 2, 2, 3>(g, cus, s)
-                                                                           : launch_n<F, 1, 1, 3>(g, cus, s);
+  if (g.thresh > 16 && g.M > 16 * (int64_t)std::min<int64_t>(g.E, g.M)) return launch_n<F, 2, 2, 3>(g, cus, s);
+  if constexpr (F == NF4) {
+    if (g.K <= 2048) return launch_n<F, 1, 1, NARROW_NS1, true>(g, cus, s);
+  }
+  return launch_n<F, 1, 1, NARROW_NS1>(g, cus, s);
 }
 
 }  // namespace
