@@ -188,13 +188,15 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
     // staged scales: thread t loads 8 absmax values (blocks 8 (t%4) .. +7) of
     // unit row t/4 (rows past N read as zero; blocks past the row read the next
     // row's values, which only meet zero partial sums)
-    u32x4 sraw[2];
+    constexpr int kSscTpr = 4 / CBW;                 // threads per staged row
+    constexpr int kSscQ = 2 * CBW;                   // 16-byte loads per thread
+    u32x4 sraw[kSscQ];
     if constexpr (SSC) {
-      static_assert(kThreads == 256 && CBW == 1, "one thread per 8 blocks of 64 rows");
-      const int64_t nrow = (int64_t)(lu % n_cols) * CPU + (t >> 2);
-      const uint32_t off = (uint32_t)((nrow * (K >> 6) + 8 * (t & 3)) * 4);
-      sraw[0] = __builtin_amdgcn_raw_buffer_load_b128(S, off, 0, 0);
-      sraw[1] = __builtin_amdgcn_raw_buffer_load_b128(S, off + 16, 0, 0);
+      static_assert(kThreads == 256 && (CBW == 1 || CBW == 2), "256 threads cover 64 CBW rows of 32 blocks");
+      const int64_t nrow = (int64_t)(lu % n_cols) * CPU + t / kSscTpr;
+      const uint32_t off = (uint32_t)((nrow * (K >> 6) + 8 * CBW * (t % kSscTpr)) * 4);
+#pragma unroll
+      for (int q = 0; q < kSscQ; ++q) sraw[q] = __builtin_amdgcn_raw_buffer_load_b128(S, off + 16 * q, 0, 0);
     }
     StepRaw<RB, CBW, kNsc> raw[NS];
 #pragma unroll
@@ -202,9 +204,9 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
     __syncthreads();   // the previous unit is done with both LDS buffers and the scales
     stage(raw[0], 0);
     if constexpr (SSC) {
-      float* dst = &Ssc[(t >> 2) * kSscLd + 8 * (t & 3)];
+      float* dst = &Ssc[(t / kSscTpr) * kSscLd + 8 * CBW * (t % kSscTpr)];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 2 * kSscQ; ++q)
         *reinterpret_cast<u32x2*>(dst + 2 * q) = u32x2{sraw[q >> 1][2 * (q & 1)], sraw[q >> 1][2 * (q & 1) + 1]};
     }
     __syncthreads();
@@ -337,8 +339,11 @@ hipError_t launch_narrow_fmt(const GemmArgs& g, int cus, hipStream_t s) {
   // the batch's experts are expected to hold more than 16 rows; otherwise 16-row
   // units over 64 weight rows (more, smaller units keep more wavefronts busy).
   if (g.thresh > 16 && g.M > 16 * (int64_t)std::min<int64_t>(g.E, g.M)) return launch_n<F, 2, 2, 3>(g, cus, s);
+#ifndef NARROW_CBW1
+#define NARROW_CBW1 1
+#endif
   if constexpr (F == NF4) {
-    if (g.K <= 2048) return launch_n<F, 1, 1, NARROW_NS1, true>(g, cus, s);
+    if (g.K <= 2048) return launch_n<F, 1, NARROW_CBW1, NARROW_NS1, true>(g, cus, s);
   }
   return launch_n<F, 1, 1, NARROW_NS1>(g, cus, s);
 }
