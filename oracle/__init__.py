@@ -23,6 +23,9 @@ section):
 * "grouped-nf4-gemm capability index" (index.json), `system_manifest.owns`: the
   package owns the input gradient of the grouped GEMM, dX = dY . W, computed on
   the same packed bytes.
+* "grouped-nf4-gemm releases", v0.2.5 section (arena_experts), and the capability
+  index's `entrypoints` (`swiglu_rows`): the fused expert block, gate_up -> SwiGLU
+  -> down (oracle.block, with its readings stated there).
 
 Two public specifications that the pages rely on but do not print supply the
 value tables: the NF4 data type (QLoRA, Dettmers et al. 2023, appendix E) and
@@ -38,6 +41,8 @@ from .pack import (quantize_pack_nf4, dequant_nf4, unpack_nf4_codes, pack_nf4_co
 from .grouped import (offsets, grouped_ref, loop_ref, dgrad_ref,
                       sampled_fwd_ref, sampled_dgrad_ref, brute_force_ref,
                       brute_force_dgrad)
+from .block import (silu, swiglu_ref, bf16_rne_from_f64, expert_block_ref,
+                    sampled_block_ref, brute_force_block)
 
 PARITY = {
     "NF4_TABLE_F32": "pinned: published decimal values and closed-form quantiles",
@@ -50,6 +55,12 @@ PARITY = {
                     "are available); pinned only by the stated convention",
     "grouped_ref": "pinned: pure-Python brute force, exact integer cases, loop_ref",
     "dgrad_ref": "pinned: adjoint identity with grouped_ref, pure-Python brute force",
+    "silu / swiglu_ref": "pinned: closed forms (silu(0), silu(ln 3), the odd-part "
+                         "identity silu(x) - silu(-x) = x), interleaved pair order",
+    "bf16_rne_from_f64": "pinned: equals the bit-pattern rounding on fp32 inputs, "
+                         "a double-rounding case, subnormals, ties to even",
+    "expert_block_ref": "pinned: pure-Python brute force (math.fsum, math.exp), "
+                        "zero up rows give zero output, exact integer case",
 }
 
 __all__ = [n for n in dir() if not n.startswith("_")]
