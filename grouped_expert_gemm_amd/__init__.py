@@ -19,9 +19,10 @@ import threading
 __all__ = [
     "GegError", "Opts", "Workspace", "lib", "header_functions",
     "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
+    "gnf4_expert_block", "gmxfp4_expert_block",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
     "geg_version", "geg_launch_count", "GEG_OP_NF4_FWD", "GEG_OP_MXFP4_FWD", "GEG_OP_NF4_DGRAD",
-    "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
+    "GEG_OP_NF4_BLOCK", "GEG_OP_MXFP4_BLOCK", "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libgeg.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "geg.h")
 
 GEG_OP_NF4_FWD, GEG_OP_MXFP4_FWD, GEG_OP_NF4_DGRAD = 0, 1, 2
+GEG_OP_NF4_BLOCK, GEG_OP_MXFP4_BLOCK = 3, 4
 DEVERR_NEGATIVE_SIZE, DEVERR_SIZES_EXCEED_M, DEVERR_FP16_RANGE = 0x1, 0x2, 0x4
 
 _STATUS = {0: "GEG_OK", 1: "GEG_ERR_NULL_POINTER", 2: "GEG_ERR_BAD_SHAPE", 3: "GEG_ERR_MISALIGNED",
@@ -72,6 +74,10 @@ def lib() -> ctypes.CDLL:
             for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad"):
                 f = getattr(L, name)
                 f.argtypes, f.restype = gemm_args, ctypes.c_int
+            block_args = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P, _P]
+            for name in ("gnf4_expert_block", "gmxfp4_expert_block"):
+                f = getattr(L, name)
+                f.argtypes, f.restype = block_args, ctypes.c_int
             L.geg_workspace_bytes.argtypes = [_I32, _I64, _I64, _I64, _I32, _P]
             L.geg_workspace_bytes.restype = _SZ
             L.geg_workspace_init.argtypes, L.geg_workspace_init.restype = [_P, _SZ, _P], ctypes.c_int
@@ -258,6 +264,42 @@ def gnf4_grouped_dgrad(dy, sizes, w, absmax, dx=None, workspace: Workspace | Non
                                     _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None,
                                     _stream(stream)))
     return dx
+
+
+def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream):
+    import torch
+    _require_gpu(a, sizes, w13, s13, w2, s2, out)
+    M, H = a.shape
+    E, I = w13.shape[0], w13.shape[1] // 2
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=a.device)
+    need = geg_workspace_bytes(op, M, H, I, E, opts)
+    ws = _workspace(workspace, need, a.device, stream)
+    _check(getattr(lib(), fn_name)(_ptr(a), _ptr(sizes), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                                   _ptr(out), M, H, I, E, _ptr(ws.buf), ws.nbytes,
+                                   ctypes.byref(opts) if opts else None, _stream(stream)))
+    return out
+
+
+def gnf4_expert_block(a, sizes, w13, absmax13, w2, absmax2, out=None,
+                      workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+    """Fused SwiGLU expert MLP: a bf16 [M,H], w13 uint8 [E,2I,H/2] (rows 2i gate,
+    2i+1 up), absmax13 fp32 [E,2I,H/64], w2 uint8 [E,H,I/2], absmax2 fp32
+    [E,H,I/64] -> out bf16 [M,H]."""
+    return _block("gnf4_expert_block", GEG_OP_NF4_BLOCK, a, sizes, w13, absmax13, w2, absmax2, out,
+                  workspace, opts, stream)
+
+
+def gmxfp4_expert_block(a, sizes, blocks13, scales13, blocks2, scales2, out=None,
+                        workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+    """The same block on MXFP4: blocks13 uint8 [E,2I,H/2], scales13 uint8
+    [E,2I,H/32], blocks2 uint8 [E,H,I/2], scales2 uint8 [E,H,I/32]."""
+    if blocks13.dim() == 4:
+        blocks13 = blocks13.reshape(blocks13.shape[0], blocks13.shape[1], -1)
+    if blocks2.dim() == 4:
+        blocks2 = blocks2.reshape(blocks2.shape[0], blocks2.shape[1], -1)
+    return _block("gmxfp4_expert_block", GEG_OP_MXFP4_BLOCK, a, sizes, blocks13, scales13, blocks2,
+                  scales2, out, workspace, opts, stream)
 
 
 def _dequant(fn_name, wq, scales, bf16, f16, stream):

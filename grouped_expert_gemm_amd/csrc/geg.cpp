@@ -208,11 +208,16 @@ geg_status check_shape(int64_t M, int64_t N, int64_t K, int32_t E, int64_t kmult
   return GEG_OK;
 }
 
+// glu = 1: the fused expert block's first projection (out is [M, N/2], see GemmArgs).
 geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8_t* wq,
                        const void* scales, void* out, int64_t M, int64_t N, int64_t K, int32_t E,
-                       void* ws, size_t ws_bytes, const geg_opts* opts, hipStream_t stream) {
+                       void* ws, size_t ws_bytes, const geg_opts* opts, hipStream_t stream,
+                       int32_t glu = 0) {
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
+  if (glu && (N % 2)) return fail(GEG_ERR_BAD_SHAPE, "the fused gate/up width must be even");
+  if (glu && opts && opts->force_path == 1)
+    return fail(GEG_ERR_BAD_OPTION, "the expert block does not run on the skinny kernel (force_path 1)");
   Plan p;
   st = make_plan(fmt == geg::NF4 ? GEG_OP_NF4_FWD : GEG_OP_MXFP4_FWD, M, N, K, E, opts, p);
   if (st != GEG_OK) return st;
@@ -250,6 +255,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
+  g.glu = glu;
 
   if (p.run_tile) {
     if (fmt == geg::NF4) {
@@ -291,6 +297,57 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   return GEG_OK;
 }
 
+// Workspace layout of the fused expert block: both projections' own regions
+// (they run one after the other and share the error word), then the bf16
+// intermediate act [M, I].
+geg_status block_layout(int fmt, int64_t M, int64_t H, int64_t I, int32_t E, const geg_opts* o,
+                        size_t& act_off, size_t& total) {
+  const int op = fmt == geg::NF4 ? GEG_OP_NF4_FWD : GEG_OP_MXFP4_FWD;
+  Plan p1, p2;
+  geg_status st;
+  if ((st = make_plan(op, M, 2 * I, H, E, o, p1)) != GEG_OK) return st;
+  if ((st = make_plan(op, M, H, I, E, o, p2)) != GEG_OK) return st;
+  act_off = round256(std::max(p1.total_bytes, p2.total_bytes));
+  total = act_off + round256((size_t)M * (size_t)I * 2);
+  return GEG_OK;
+}
+
+geg_status block_common(int fmt, const void* a, const int32_t* sizes, const uint8_t* w13,
+                        const void* s13, const uint8_t* w2, const void* s2, void* out, int64_t M,
+                        int64_t H, int64_t I, int32_t E, void* ws, size_t ws_bytes,
+                        const geg_opts* opts, hipStream_t stream) {
+  const int64_t kmult = fmt == geg::NF4 ? 64 : 32;
+  geg_status st;
+  if ((st = check_shape(M, 2 * I, H, E, kmult)) != GEG_OK) return st;
+  if (I <= 0 || I % kmult) return fail(GEG_ERR_BAD_SHAPE, "I must be a positive multiple of " + std::to_string(kmult));
+  if (opts && opts->force_path == 1)
+    return fail(GEG_ERR_BAD_OPTION, "the expert block does not run on the skinny kernel (force_path 1)");
+  size_t act_off = 0, total = 0;
+  if ((st = block_layout(fmt, M, H, I, E, opts, act_off, total)) != GEG_OK) return st;
+  if (M == 0) return GEG_OK;
+  if (!w2 || !s2) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!ws) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < total)
+    return fail(GEG_ERR_WORKSPACE, "workspace smaller than geg_workspace_bytes(): need " + std::to_string(total));
+  if (!aligned(w2, 16) || (fmt == geg::NF4 && !aligned(s2, 4)))
+    return fail(GEG_ERR_MISALIGNED, "w2/blocks2 must be 16-byte aligned");
+  if ((st = check_device_ptr(w2, "w2")) != GEG_OK) return st;
+  if ((st = check_device_ptr(s2, "scales2")) != GEG_OK) return st;
+  geg_opts inner{};
+  if (opts) inner = *opts;
+  inner.kernel_events = nullptr;
+  hipError_t e = record_event(opts, 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "event record");
+  void* act = reinterpret_cast<uint8_t*>(ws) + act_off;
+  st = gemm_common(fmt, a, sizes, w13, s13, act, M, 2 * I, H, E, ws, act_off, &inner, stream, 1);
+  if (st != GEG_OK) return st;
+  st = gemm_common(fmt, act, sizes, w2, s2, out, M, H, I, E, ws, act_off, &inner, stream, 0);
+  if (st != GEG_OK) return st;
+  e = record_event(opts, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "event record");
+  return GEG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +366,24 @@ geg_status gmxfp4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_
                                const geg_opts* opts, hipStream_t stream) {
   return gemm_common(geg::MXFP4, a, sizes, blocks, scales, out, M, N, K, E, workspace,
                      workspace_bytes, opts, stream);
+}
+
+geg_status gnf4_expert_block(const void* a, const int32_t* sizes, const uint8_t* w13,
+                             const float* absmax13, const uint8_t* w2, const float* absmax2,
+                             void* out, int64_t M, int64_t H, int64_t I, int32_t E,
+                             void* workspace, size_t workspace_bytes, const geg_opts* opts,
+                             hipStream_t stream) {
+  return block_common(geg::NF4, a, sizes, w13, absmax13, w2, absmax2, out, M, H, I, E, workspace,
+                      workspace_bytes, opts, stream);
+}
+
+geg_status gmxfp4_expert_block(const void* a, const int32_t* sizes, const uint8_t* blocks13,
+                               const uint8_t* scales13, const uint8_t* blocks2,
+                               const uint8_t* scales2, void* out, int64_t M, int64_t H, int64_t I,
+                               int32_t E, void* workspace, size_t workspace_bytes,
+                               const geg_opts* opts, hipStream_t stream) {
+  return block_common(geg::MXFP4, a, sizes, blocks13, scales13, blocks2, scales2, out, M, H, I, E,
+                      workspace, workspace_bytes, opts, stream);
 }
 
 geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_t* w,
@@ -362,7 +437,13 @@ geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_
 
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
                            const geg_opts* opts) {
-  if (op < 0 || op > 2 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  if (op < 0 || op > 4 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  if (op == GEG_OP_NF4_BLOCK || op == GEG_OP_MXFP4_BLOCK) {
+    size_t act_off = 0, total = 0;
+    if (block_layout(op == GEG_OP_NF4_BLOCK ? geg::NF4 : geg::MXFP4, M, N, K, E, opts, act_off, total) != GEG_OK)
+      return 0;
+    return total;
+  }
   Plan p;
   if (make_plan(op, M, N, K, E, opts, p) != GEG_OK) return 0;
   return p.total_bytes;

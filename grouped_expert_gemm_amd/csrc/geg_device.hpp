@@ -332,6 +332,15 @@ __device__ __forceinline__ u32x2 bf16x4_to_f16(const u32x2& x, uint32_t& range) 
   return u32x2{r[0], r[1]};
 }
 
+// Gated unit of the fused expert block: silu(g) * u with silu(x) = x / (1 + e^-x),
+// in fp32 (e^-x overflowing to inf for very negative g gives -0).
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// The value held by the neighbouring lane (l ^ 1): a DPP quad permutation.
+__device__ __forceinline__ float lane_pair_swap(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ bool range_overflowed(uint32_t range) {
   return (range & 0xFFFFu) >= 0x7C00u || (range >> 16) >= 0x7C00u;
 }

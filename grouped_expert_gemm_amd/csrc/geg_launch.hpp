@@ -57,6 +57,8 @@ struct GemmArgs {
   uint32_t* err;          // device error word
   int32_t* counters;      // split-K arrival counters
   float* partials;        // split-K partials [split, M, N]
+  int32_t glu;            // 1: columns 2i, 2i+1 are (gate, up) of unit i and out is
+                          // [M, N/2] with out[m, i] = bf16(silu(gate) * up)
 };
 
 // Each launcher returns the hipError_t of its launch.

@@ -293,6 +293,24 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
     for (int jn = 0; jn < NS - 1; ++jn)
       if (full + jn < nst) step(jn, full + jn);
     // acc[r][cb][q]: activation row 16r + 4 (l/16) + q, weight row n0 + 16 cb + l%16
+    if (g.glu) {
+      // fused expert block: weight rows 2c, 2c+1 (lanes l, l ^ 1) are the gate
+      // and up of unit c; the even lane writes out[row, c] of the [M, N/2] output
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb) {
+        const int64_t n = n0 + 16 * cb + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float up = lane_pair_swap(acc[r][cb][q]);
+            const int lr = 16 * r + 4 * (lane >> 4) + q;
+            if (!(lane & 1) && n < N && lr < rows)
+              g.out[(row0 + lr) * (N >> 1) + (n >> 1)] = to_bf16(swiglu(acc[r][cb][q], up));
+          }
+      }
+      continue;
+    }
 #pragma unroll
     for (int cb = 0; cb < CBW; ++cb) {
       const int64_t n = n0 + 16 * cb + (lane & 15);

@@ -508,6 +508,49 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     // column 16j + lane%16 of the block; every write offset is a constant from
     // the lane's base.
     uint16_t* E = L.epi[wave];
+    if (!DG && g.glu) {
+      // Fused expert block: columns 2c, 2c+1 (lanes l, l ^ 1) are the gate and
+      // up of unit c. Each lane of a pair computes two of the four rows' units:
+      // the even lane rows q = 0, 1, the odd lane rows q = 2, 3, trading the
+      // missing halves with its neighbour. The wavefront's 128 x 32 unit block
+      // goes through LDS like the plain epilogue.
+      const bool odd = lane & 1;
+      uint16_t* base = E + (4 * (lane >> 4) + (odd ? 2 : 0)) * kEpiLd + ((lane & 15) >> 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = acc[i][j];
+          const float r0 = lane_pair_swap(odd ? v[0] : v[2]);
+          const float r1 = lane_pair_swap(odd ? v[1] : v[3]);
+          const float a0 = odd ? swiglu(r0, v[2]) : swiglu(v[0], r0);
+          const float a1 = odd ? swiglu(r1, v[3]) : swiglu(v[1], r1);
+          base[(16 * i) * kEpiLd + 8 * j] = to_bf16(a0);
+          base[(16 * i + 1) * kEpiLd + 8 * j] = to_bf16(a1);
+        }
+      __syncthreads();
+      const int chunk = lane & 3;
+      const int64_t O2 = O >> 1;
+      const int64_t col = (n0 >> 1) + 32 * wn + 8 * chunk;
+      const bool vec = (O2 & 7) == 0 && col + 8 <= O2;
+      const uint16_t* src = E + (lane >> 2) * kEpiLd + 8 * chunk;
+      for (int rr = 0; rr < 128; rr += 16) {
+        const int lr = 128 * wm + rr + (lane >> 2);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + rr * kEpiLd);
+        if (lr < rows && col < O2) {
+          uint16_t* dst = g.out + (row0 + lr) * O2 + col;
+          if (vec) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              if (col + x < O2) dst[x] = (uint16_t)(v[x >> 1] >> (16 * (x & 1)));
+          }
+        }
+      }
+      __syncthreads();   // the stage buffers are reused by the next tile
+      continue;
+    }
     {
       uint16_t* base = E + (4 * (lane >> 4)) * kEpiLd + (lane & 15);
 #pragma unroll

@@ -149,6 +149,24 @@ __device__ __forceinline__ void vec_unit(const GemmArgs& g, const uint32_t* blut
       }
     }
   }
+  if (g.glu) {
+    // fused expert block: weight rows 2c, 2c+1 are the gate and up of unit c.
+    // With one row group per wavefront (G = 1) they are row groups u, u+1 of the
+    // same lanes; with two (G = 2) the same u of lane groups 0 and 1.
+#pragma unroll
+    for (int u = 0; u < U; u += (G == 1 ? 2 : 1)) {
+      const int64_t n = n0 + G * u + gl;
+#pragma unroll
+      for (int m = 0; m < RV; ++m) {
+        if (m < rows) {
+          const float v = group_sum<LPR>(acc[u][m]);
+          const float w = G == 1 ? group_sum<LPR>(acc[u + 1][m]) : __shfl_xor(v, 32, 64);
+          if (lane == 0 && n < N) g.out[(row0 + m) * (N >> 1) + (n >> 1)] = to_bf16(swiglu(v, w));
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t n = n0 + G * u + gl;

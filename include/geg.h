@@ -104,6 +104,8 @@ typedef struct {
 #define GEG_OP_NF4_FWD 0
 #define GEG_OP_MXFP4_FWD 1
 #define GEG_OP_NF4_DGRAD 2
+#define GEG_OP_NF4_BLOCK 3   /* N = H (hidden), K = I (intermediate) */
+#define GEG_OP_MXFP4_BLOCK 4 /* N = H (hidden), K = I (intermediate) */
 
 /*
  * gnf4_grouped_gemm — out[M, N] = per expert, a_e . W_e^T with W_e in NF4.
@@ -151,6 +153,45 @@ geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_
                               const float* absmax, void* dx, int64_t M, int64_t N, int64_t K,
                               int32_t E, void* workspace, size_t workspace_bytes,
                               const geg_opts* opts, hipStream_t stream);
+
+/*
+ * gnf4_expert_block — the routed experts' whole SwiGLU MLP in two grouped GEMMs,
+ * with the gated unit applied in the first one's epilogue ("grouped-nf4-gemm
+ * releases", v0.2.5: a MoE layer forward runs gate, GLU and down straight off
+ * the grouped GEMM's packed weights; "grouped-nf4-gemm capability index": the
+ * package owns the swiglu glue):
+ *   h   = a_e . W13_e^T                       (fp32 accumulation, never stored)
+ *   act = bf16( silu(h[:, 2i]) * h[:, 2i+1] )  silu(x) = x / (1 + e^-x)
+ *   out = act_e . W2_e^T
+ *   a       bf16 [M, H], rows grouped by expert, 16-B aligned
+ *   sizes   int32 [E] (device memory, not modified)
+ *   w13     u8 [E, 2I, H/2] NF4 codes of the fused gate/up weight; row 2i is the
+ *           gate and row 2i+1 the up projection of unit i (interleaved)
+ *   absmax13 fp32 [E, 2I, H/64]
+ *   w2      u8 [E, H, I/2], absmax2 fp32 [E, H, I/64]
+ *   out     bf16 [M, H], 16-B aligned
+ *   H % 64 == 0 and I % 64 == 0. The intermediate act [M, I] lives in the
+ *   workspace (size it with geg_workspace_bytes(GEG_OP_NF4_BLOCK, M, H, I, E)).
+ *   Both projections choose their paths as gnf4_grouped_gemm does; force_path 1
+ *   (skinny) is refused with GEG_ERR_BAD_OPTION. kernel_events, when given, are
+ *   recorded as {block_start, block_end, NULL, NULL}: around the whole block.
+ */
+geg_status gnf4_expert_block(const void* a, const int32_t* sizes, const uint8_t* w13,
+                             const float* absmax13, const uint8_t* w2, const float* absmax2,
+                             void* out, int64_t M, int64_t H, int64_t I, int32_t E,
+                             void* workspace, size_t workspace_bytes, const geg_opts* opts,
+                             hipStream_t stream);
+
+/*
+ * gmxfp4_expert_block — the same block on MXFP4 weights: blocks13 u8 [E, 2I, H/2]
+ * with scales13 u8 [E, 2I, H/32], blocks2 u8 [E, H, I/2] with scales2 u8
+ * [E, H, I/32]; H % 32 == 0 and I % 32 == 0.
+ */
+geg_status gmxfp4_expert_block(const void* a, const int32_t* sizes, const uint8_t* blocks13,
+                               const uint8_t* scales13, const uint8_t* blocks2,
+                               const uint8_t* scales2, void* out, int64_t M, int64_t H, int64_t I,
+                               int32_t E, void* workspace, size_t workspace_bytes,
+                               const geg_opts* opts, hipStream_t stream);
 
 /* Workspace bytes needed by one call of operation `op` with these sizes and options. */
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
