@@ -20,6 +20,10 @@ Prints ONE JSON line:
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same case
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+
+The *_block workloads time the fused expert block (gate_up -> SwiGLU -> down in
+one call) at prefill and decode shapes; their value is the block's TFLOP/s over
+both projections, next to the two plain GEMMs of the same shapes.
 """
 from __future__ import annotations
 
@@ -53,6 +57,13 @@ WORKLOADS = {
     # decode-class only (no prefill leg): value is packed-weight GB/s
     "qwen3_t64": (None, "qwen3_gate_up_t64"),
     "qwen3_down_t64": (None, "qwen3_down_t64"),
+}
+# Fused expert block (gate_up -> SwiGLU -> down in one call): the gate_up and down
+# cases of one model share their routing; (prefill gate_up, prefill down, decode
+# gate_up, decode down).
+BLOCK_WORKLOADS = {
+    "qwen3_block": ("qwen3_gate_up_t4096", "qwen3_down_t4096", "qwen3_gate_up_t1", "qwen3_down_t1"),
+    "gptoss_block": ("gptoss_gate_up_t2048", "gptoss_down_t2048", "gptoss_gate_up_t1", "gptoss_down_t1"),
 }
 KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip",
                   "geg.cpp"]
@@ -206,12 +217,138 @@ def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s"):
             "host_cpus": os.cpu_count()}
 
 
+def cpu_baseline_block(cg, cdn, seed, budget_s=12.0):
+    """The fp64 oracle of the fused expert block on as many routed experts as fit
+    in about budget_s seconds, as TFLOP/s (both projections' flops)."""
+    import oracle
+    import synthetic
+    from oracle import cases as C
+    a_bits, sizes = synthetic.rows_bf16(cg, seed)
+    off = oracle.offsets(sizes)
+    experts = [e for e in range(cg.E) if sizes[e]][:16]
+    H, I = cg.K, cg.N // 2
+    flops, secs, used = 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    i = 0
+    while True:
+        e = experts[i % len(experts)]
+        i += 1
+        if cg.fmt == "nf4":
+            p13, p2 = C.nf4_expert(cg, seed, e), C.nf4_expert(cdn, seed, e)
+            dq = oracle.dequant_nf4
+        else:
+            p13, p2 = synthetic.mxfp4_bytes(cg, seed, e), synthetic.mxfp4_bytes(cdn, seed, e)
+            dq = oracle.dequant_mxfp4
+        t0 = time.perf_counter()
+        W13, W2 = dq(*p13), dq(*p2)
+        rows = a_bits[off[e]:off[e + 1]]
+        oracle.expert_block_ref(rows, np.array([len(rows)], np.int32), lambda _e: W13, lambda _e: W2, H, I)
+        secs += time.perf_counter() - t0
+        flops += 2.0 * len(rows) * 3 * H * I
+        used += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0]) or os.cpu_count()
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{cg.name} block: {used} expert blocks (cycling over {len(experts)} routed experts), "
+                      "fp64 decode + numpy matmuls + SwiGLU", "seconds": secs, "host_cpus": os.cpu_count()}
+
+
+def main_block(args, torch, geg, synthetic):
+    """Fused expert block workloads: prefill and decode calls of gnf4/gmxfp4_expert_block."""
+    dev = torch.device("cuda", 0)
+    pg, pdn, dg, ddn = (synthetic.case(n) for n in BLOCK_WORKLOADS[args.workload])
+    blk = geg.gnf4_expert_block if pg.fmt == "nf4" else geg.gmxfp4_expert_block
+    gemm = geg.gnf4_grouped_gemm if pg.fmt == "nf4" else geg.gmxfp4_grouped_gemm
+    a, sz, sizes, c13, s13 = make_inputs(pg, args.seed, torch, geg, dev)
+    _, _, sizes2, c2, s2 = make_inputs(pdn, args.seed, torch, geg, dev)
+    assert (sizes == sizes2).all(), "gate_up and down cases must share their routing"
+    H, I = pg.K, pg.N // 2
+    assert pdn.K == I and pdn.N == H
+    stack = sum(t.numel() * t.element_size() for t in (c13, s13, c2, s2))
+    ncopies = max(1, int(np.ceil(ROTATE_BYTES / stack)))
+    wcopies = [(c13, s13, c2, s2)] + [tuple(t.clone() for t in (c13, s13, c2, s2)) for _ in range(ncopies - 1)]
+    ws = geg.Workspace(geg.geg_workspace_bytes(3 if pg.fmt == "nf4" else 4, pg.M, H, I, pg.E))
+    out = torch.empty((pg.M, H), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((pg.M, 2 * I), dtype=torch.bfloat16, device=dev)
+    act = torch.zeros((pg.M, I), dtype=torch.bfloat16, device=dev)
+
+    def prefill(wc, opts=None):
+        blk(a, sz, wc[0], wc[1], wc[2], wc[3], out=out, workspace=ws, opts=opts)
+
+    def unfused(wc, opts=None):
+        # the two plain GEMMs of the same shapes (timing only: the down GEMM reads
+        # a zero intermediate; an unfused block would also need a SwiGLU pass)
+        gemm(a, sz, wc[0], wc[1], out=h, workspace=ws)
+        gemm(act, sz, wc[2], wc[3], out=out, workspace=ws)
+
+    da_bits, dsizes = synthetic.rows_bf16(dg, args.seed)
+    da = torch.from_numpy(da_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    dsz = torch.from_numpy(dsizes).to(dev)
+    dout = torch.empty((dg.M, H), dtype=torch.bfloat16, device=dev)
+    dws = geg.Workspace(geg.geg_workspace_bytes(3 if pg.fmt == "nf4" else 4, dg.M, H, I, dg.E))
+
+    def decode(wc, opts=None):
+        blk(da, dsz, wc[0], wc[1], wc[2], wc[3], out=dout, workspace=dws, opts=opts)
+
+    prefill(wcopies[0])
+    decode(wcopies[0])
+    torch.cuda.synchronize()
+    assert ws.read_error() == 0 and dws.read_error() == 0, "device error word set"
+    for i in range(args.warmup):
+        prefill(wcopies[i % ncopies]); decode(wcopies[i % ncopies])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        prefill(wcopies[i % ncopies]); decode(wcopies[i % ncopies])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    flops = 2.0 * pg.M * 3 * H * I
+    pre_ms, pre_how = time_calls(prefill, wcopies, args.steps, args.warmup, torch)
+    pre_avg = float(np.mean(pre_ms))
+    un_ms, _ = time_calls(unfused, wcopies, args.steps, args.warmup, torch)
+    blk_ms = time_kernel(prefill, wcopies, args.steps, args.warmup, geg, torch, 0)
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    ktflops = flops / (blk_ms * 1e-3) / 1e12
+    dbytes = touched_weight_bytes(dg, dsizes) + touched_weight_bytes(ddn, dsizes)
+    dec_ms, dec_how = time_calls(decode, wcopies, max(args.steps, 50), args.warmup, torch)
+    dec_avg = float(np.mean(dec_ms))
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16" if pg.fmt == "nf4" else "bf16", "data": "synthetic",
+        "config": {"workload": f"{pg.name} + {pdn.name} fused block, {dg.name} + {ddn.name} fused block",
+                   "format": pg.fmt, "E": pg.E, "H": H, "I": I, "prefill_rows": pg.M,
+                   "decode_rows": dg.M, "top_k": pg.top_k, "weight_copies_rotated": ncopies},
+        "prefill": {"ms": round(pre_avg, 5), "gflop": flops / 1e9, "tflops": round(tflops, 2),
+                    "timing": pre_how, "two_plain_gemms_ms": round(float(np.mean(un_ms)), 5),
+                    "block_events_ms": round(blk_ms, 5)},
+        "decode": {"value": round(dbytes / (dec_avg * 1e-3) / 1e9, 1), "unit": "GB/s",
+                   "ms": round(dec_avg, 5), "weight_bytes": dbytes, "timing": dec_how},
+        "roofline": {"bound": "mfma", "achieved": round(ktflops, 2), "peak": round(PEAK_MFMA_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(ktflops / PEAK_MFMA_TFLOPS, 4),
+                     "kernel": f"fused expert block ({pg.fmt}): both projections' kernels, {pg.name}",
+                     "per_launch_gflop": round(flops / 1e9, 3), "kernel_ms": round(blk_ms, 5),
+                     "traffic": None},
+        "kernel_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_block(pg, pdn, args.seed, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="olmoe", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="olmoe", choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -240,6 +377,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.workload in BLOCK_WORKLOADS:
+        main_block(args, torch, geg, synthetic)
+        return
     pre_name, dec_name = WORKLOADS[args.workload]
     cp = synthetic.case(pre_name or dec_name)
     fn = geg.gnf4_grouped_gemm if cp.fmt == "nf4" else geg.gmxfp4_grouped_gemm

@@ -112,13 +112,14 @@ class KernelTimer:
         return self._opts
 
     def _ms(self, a, b):
-        if self._hip.hipEventSynchronize(ctypes.c_void_p(self._ev[b])) != 0:
-            return None
         ms = ctypes.c_float(0.0)
-        if self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._ev[a]),
-                                         ctypes.c_void_p(self._ev[b])) != 0:
-            return None
-        return ms.value
+        ok = (self._hip.hipEventSynchronize(ctypes.c_void_p(self._ev[b])) == 0 and
+              self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._ev[a]),
+                                            ctypes.c_void_p(self._ev[b])) == 0)
+        # events the call did not record fail here; leave no error behind for
+        # the next launch on this thread
+        self._hip.hipGetLastError()
+        return ms.value if ok else None
 
     def elapsed_ms(self):
         return self._ms(0, 1), self._ms(2, 3)

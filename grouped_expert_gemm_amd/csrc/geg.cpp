@@ -49,7 +49,11 @@ geg_status check_device() {
       g_last_error = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950";
     }
   }
-  return known[dev] == 1 ? GEG_OK : fail(GEG_ERR_UNSUPPORTED_DEVICE, "current device is not gfx950");
+  if (known[dev] != 1) return fail(GEG_ERR_UNSUPPORTED_DEVICE, "current device is not gfx950");
+  // Launch errors are read with hipGetLastError right after each launch; clear
+  // what an unrelated earlier call on this thread may have left there.
+  (void)hipGetLastError();
+  return GEG_OK;
 }
 
 // Device (or managed) memory of the current device; host memory is refused.

@@ -333,8 +333,12 @@ __device__ __forceinline__ u32x2 bf16x4_to_f16(const u32x2& x, uint32_t& range) 
 }
 
 // Gated unit of the fused expert block: silu(g) * u with silu(x) = x / (1 + e^-x),
-// in fp32 (e^-x overflowing to inf for very negative g gives -0).
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// in fp32 with the hardware exponential and reciprocal (about 1 ulp each; the
+// result is rounded to bf16). e^-x overflowing to inf for very negative g gives
+// a reciprocal of 0 and a result of -0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // The value held by the neighbouring lane (l ^ 1): a DPP quad permutation.
 __device__ __forceinline__ float lane_pair_swap(float v) {
