@@ -19,10 +19,11 @@ import threading
 __all__ = [
     "GegError", "Opts", "Workspace", "lib", "header_functions",
     "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
-    "gnf4_expert_block", "gmxfp4_expert_block",
+    "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
     "geg_version", "geg_launch_count", "GEG_OP_NF4_FWD", "GEG_OP_MXFP4_FWD", "GEG_OP_NF4_DGRAD",
     "GEG_OP_NF4_BLOCK", "GEG_OP_MXFP4_BLOCK", "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
+    "DEVERR_BAD_EXPERT_ID",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +33,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "geg.h")
 GEG_OP_NF4_FWD, GEG_OP_MXFP4_FWD, GEG_OP_NF4_DGRAD = 0, 1, 2
 GEG_OP_NF4_BLOCK, GEG_OP_MXFP4_BLOCK = 3, 4
 DEVERR_NEGATIVE_SIZE, DEVERR_SIZES_EXCEED_M, DEVERR_FP16_RANGE = 0x1, 0x2, 0x4
+DEVERR_BAD_EXPERT_ID = 0x8
 
 _STATUS = {0: "GEG_OK", 1: "GEG_ERR_NULL_POINTER", 2: "GEG_ERR_BAD_SHAPE", 3: "GEG_ERR_MISALIGNED",
            4: "GEG_ERR_NOT_DEVICE_MEMORY", 5: "GEG_ERR_WORKSPACE", 6: "GEG_ERR_UNSUPPORTED_DEVICE",
@@ -74,6 +76,12 @@ def lib() -> ctypes.CDLL:
             for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad"):
                 f = getattr(L, name)
                 f.argtypes, f.restype = gemm_args, ctypes.c_int
+            L.geg_route_sort.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
+            L.geg_route_sort.restype = ctypes.c_int
+            L.geg_route_workspace_bytes.argtypes = [_I64, _I32, _I32]
+            L.geg_route_workspace_bytes.restype = _SZ
+            L.geg_route_combine.argtypes = [_P, _P, _P, _I64, _I32, _I64, _P, _P]
+            L.geg_route_combine.restype = ctypes.c_int
             block_args = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P, _P]
             for name in ("gnf4_expert_block", "gmxfp4_expert_block"):
                 f = getattr(L, name)
@@ -301,6 +309,44 @@ def gmxfp4_expert_block(a, sizes, blocks13, scales13, blocks2, scales2, out=None
         blocks2 = blocks2.reshape(blocks2.shape[0], blocks2.shape[1], -1)
     return _block("gmxfp4_expert_block", GEG_OP_MXFP4_BLOCK, a, sizes, blocks13, scales13, blocks2,
                   scales2, out, workspace, opts, stream)
+
+
+def route_sort(topk_ids, E: int, x=None, workspace: Workspace | None = None, stream=None):
+    """Device-side routing sort of topk_ids int32 [T, k] over E experts.
+
+    Returns (sizes int32 [E], row_of int32 [T*k], src_of int32 [T*k], x_sorted):
+    entries ordered by expert, then by t*k + slot; x_sorted bf16 [T*k, H] holds
+    x[src_of[r] // k] in sorted row r when x (bf16 [T, H]) is given, else None."""
+    import torch
+    _require_gpu(topk_ids, x)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    sizes = torch.empty((E,), dtype=torch.int32, device=dev)
+    row_of = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    src_of = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    xs = None
+    H = 0
+    if x is not None:
+        H = x.shape[1]
+        xs = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    need = lib().geg_route_workspace_bytes(T, k, E)
+    ws = _workspace(workspace, need, dev, stream)
+    _check(lib().geg_route_sort(_ptr(topk_ids), T, k, E, _ptr(x), H, _ptr(sizes), _ptr(row_of),
+                                _ptr(src_of), _ptr(xs), _ptr(ws.buf), ws.nbytes, _stream(stream)))
+    return sizes, row_of, src_of, xs
+
+
+def route_combine(y, row_of, weights, k: int, out=None, stream=None):
+    """out bf16 [T, N] = sum over slots of weights[t, s] * y[row_of[t*k + s]] (fp32 in
+    slot order); y bf16 [T*k, N] in routing-sort order, weights fp32 [T, k] or None."""
+    import torch
+    _require_gpu(y, row_of, weights, out)
+    T = row_of.numel() // k
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=y.device)
+    _check(lib().geg_route_combine(_ptr(y), _ptr(row_of), _ptr(weights), T, k, N, _ptr(out), _stream(stream)))
+    return out
 
 
 def _dequant(fn_name, wq, scales, bf16, f16, stream):

@@ -439,6 +439,71 @@ geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_
   return GEG_OK;
 }
 
+size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k <= 0 || E <= 0 || E > geg::kMaxExperts) return 0;
+  const int64_t nchunks = (T * k + geg::kThreads - 1) / geg::kThreads;
+  return kHeader + round256((size_t)std::max<int64_t>(nchunks, 1) * (size_t)E * 4);
+}
+
+geg_status geg_route_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
+                          int64_t H, int32_t* sizes, int32_t* row_of, int32_t* src_of, void* x_sorted,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || k <= 0 || E <= 0) return fail(GEG_ERR_BAD_SHAPE, "need T >= 0, k > 0, E > 0");
+  if (E > geg::kMaxExperts) return fail(GEG_ERR_BAD_SHAPE, "E exceeds 1024 experts");
+  if (T * (int64_t)k >= (int64_t)INT32_MAX) return fail(GEG_ERR_BAD_SHAPE, "T * k must be below 2^31");
+  const bool gather = x || x_sorted;
+  if (gather && (!x || !x_sorted)) return fail(GEG_ERR_NULL_POINTER, "x and x_sorted go together");
+  if (gather && (H <= 0 || H % 8)) return fail(GEG_ERR_BAD_SHAPE, "the gather needs H > 0, H % 8 == 0");
+  if (!sizes || !workspace) return fail(GEG_ERR_NULL_POINTER, "sizes and workspace are required");
+  if (T > 0 && (!topk_ids || !row_of || !src_of))
+    return fail(GEG_ERR_NULL_POINTER, "topk_ids, row_of and src_of are required");
+  if ((gather && (!aligned(x, 16) || !aligned(x_sorted, 16))) || !aligned(topk_ids, 4) ||
+      !aligned(sizes, 4) || !aligned(row_of, 4) || !aligned(src_of, 4))
+    return fail(GEG_ERR_MISALIGNED, "x and x_sorted must be 16-byte aligned, index arrays 4-byte");
+  if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < geg_route_workspace_bytes(T, k, E))
+    return fail(GEG_ERR_WORKSPACE, "workspace smaller than geg_route_workspace_bytes()");
+  geg_status st;
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{topk_ids, "topk_ids"}, {sizes, "sizes"},
+                           {row_of, "row_of"}, {src_of, "src_of"}, {x, "x"}, {x_sorted, "x_sorted"},
+                           {workspace, "workspace"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  const int64_t n = T * k;
+  hipError_t e = geg::launch_route_sort(topk_ids, n, E, reinterpret_cast<int32_t*>(wsb + kHeader), sizes,
+                                        row_of, src_of, reinterpret_cast<uint32_t*>(wsb), stream);
+  if (e != hipSuccess) return hip_fail(e, "routing sort launch");
+  g_launches += n > 0 ? 3 : 1;
+  if (gather && n > 0) {
+    e = geg::launch_route_gather(reinterpret_cast<const uint16_t*>(x), H, k, src_of, n,
+                                 reinterpret_cast<uint16_t*>(x_sorted), cu_count(), stream);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    ++g_launches;
+  }
+  return GEG_OK;
+}
+
+geg_status geg_route_combine(const void* y, const int32_t* row_of, const float* weights, int64_t T,
+                             int32_t k, int64_t N, void* out, hipStream_t stream) {
+  if (T < 0 || k <= 0 || N <= 0 || N % 8) return fail(GEG_ERR_BAD_SHAPE, "need T >= 0, k > 0, N > 0, N % 8 == 0");
+  if (T * (int64_t)k >= (int64_t)INT32_MAX) return fail(GEG_ERR_BAD_SHAPE, "T * k must be below 2^31");
+  if (T == 0) return GEG_OK;
+  if (!y || !row_of || !out) return fail(GEG_ERR_NULL_POINTER, "y, row_of and out are required");
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(row_of, 4) || (weights && !aligned(weights, 4)))
+    return fail(GEG_ERR_MISALIGNED, "y and out must be 16-byte aligned");
+  geg_status st;
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{y, "y"}, {row_of, "row_of"},
+                           {weights, "weights"}, {out, "out"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  hipError_t e = geg::launch_route_combine(reinterpret_cast<const uint16_t*>(y), N, row_of, weights, T, k,
+                                           reinterpret_cast<uint16_t*>(out), cu_count(), stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
                            const geg_opts* opts) {
   if (op < 0 || op > 4 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;

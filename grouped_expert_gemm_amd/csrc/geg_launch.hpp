@@ -72,6 +72,12 @@ hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float*
 hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,
                                int64_t K, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_route_sort(const int32_t* ids, int64_t n, int32_t E, int32_t* counts, int32_t* sizes,
+                             int32_t* row_of, int32_t* src_of, uint32_t* err, hipStream_t s);
+hipError_t launch_route_gather(const uint16_t* x, int64_t H, int32_t k, const int32_t* src_of, int64_t n,
+                               uint16_t* xs, int cus, hipStream_t s);
+hipError_t launch_route_combine(const uint16_t* y, int64_t N, const int32_t* row_of, const float* w, int64_t T,
+                                int32_t k, uint16_t* out, int cus, hipStream_t s);
 hipError_t launch_to_f16_slots(const uint16_t* a, uint16_t* a16, int64_t elems, uint32_t* err,
                                hipStream_t s);
 

@@ -83,6 +83,7 @@ typedef enum {
 #define GEG_DEVERR_NEGATIVE_SIZE 0x1u /* some sizes[e] < 0: treated as 0                     */
 #define GEG_DEVERR_SIZES_EXCEED_M 0x2u /* sum(sizes) > M: rows past M are not computed        */
 #define GEG_DEVERR_FP16_RANGE 0x4u    /* an NF4-path operand overflowed fp16 (|x| > 65504)   */
+#define GEG_DEVERR_BAD_EXPERT_ID 0x8u /* geg_route_sort: a top-k id outside [0, E) (entry dropped) */
 
 /* Optional knobs (NULL = automatic). Used by tests to pin a path. */
 typedef struct {
@@ -192,6 +193,45 @@ geg_status gmxfp4_expert_block(const void* a, const int32_t* sizes, const uint8_
                                const uint8_t* scales2, void* out, int64_t M, int64_t H, int64_t I,
                                int32_t E, void* workspace, size_t workspace_bytes,
                                const geg_opts* opts, hipStream_t stream);
+
+/*
+ * geg_route_sort — the routing step in front of the grouped GEMM, on the device
+ * ("grouped-nf4-gemm releases", v0.2.6 "The patch point": the kernel replaces a
+ * per-expert loop over rows grouped by expert; capability index, entrypoints:
+ * `router_epilogue`). The T*k (token, slot) entries of `topk_ids` are ordered by
+ * expert and, within an expert, by flat index t*k + slot (a stable sort):
+ *   topk_ids int32 [T, k], ids in [0, E) (device memory, not modified)
+ *   sizes    int32 [E] out: entries per expert (the GEMM's `sizes`)
+ *   row_of   int32 [T*k] out: sorted row of entry t*k + slot (-1 for an id
+ *            outside [0, E), which is dropped and flags GEG_DEVERR_BAD_EXPERT_ID)
+ *   src_of   int32 [T*k] out: entry of sorted row r (-1 for rows past sum(sizes))
+ *   x        bf16 [T, H] token activations, and x_sorted bf16 [T*k, H] out: the
+ *            GEMM's grouped rows, x_sorted[r] = x[src_of[r] / k]. Both NULL to
+ *            skip the gather; else H % 8 == 0 and both 16-B aligned. Rows past
+ *            sum(sizes) are left untouched.
+ *   workspace: at least geg_route_workspace_bytes(T, k, E) bytes, initialised
+ *            once with geg_workspace_init (its error word receives the flag).
+ * Deterministic: no order depends on atomics.
+ */
+geg_status geg_route_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
+                          int64_t H, int32_t* sizes, int32_t* row_of, int32_t* src_of, void* x_sorted,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of geg_route_sort. */
+size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E);
+
+/*
+ * geg_route_combine — the top-k weighted combine after the expert GEMMs, back in
+ * token order (capability index, entrypoints: `combine_rows`):
+ *   out[t, :] = bf16( sum over slots s of weights[t, s] * y[row_of[t*k + s], :] )
+ * with fp32 products and sums in slot order; entries with row_of < 0 are skipped.
+ *   y        bf16 [T*k, N], rows in the order of geg_route_sort, 16-B aligned
+ *   row_of   int32 [T*k] from geg_route_sort (values in [-1, T*k))
+ *   weights  fp32 [T, k] router weights, or NULL for all ones
+ *   out      bf16 [T, N], 16-B aligned; N % 8 == 0
+ */
+geg_status geg_route_combine(const void* y, const int32_t* row_of, const float* weights, int64_t T,
+                             int32_t k, int64_t N, void* out, hipStream_t stream);
 
 /* Workspace bytes needed by one call of operation `op` with these sizes and options. */
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,

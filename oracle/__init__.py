@@ -26,6 +26,9 @@ section):
 * "grouped-nf4-gemm releases", v0.2.5 section (arena_experts), and the capability
   index's `entrypoints` (`swiglu_rows`): the fused expert block, gate_up -> SwiGLU
   -> down (oracle.block, with its readings stated there).
+* The capability index's `entrypoints` (`router_epilogue`, `combine_rows`) and
+  releases v0.2.6 "The patch point": the routing sort in front of the grouped
+  GEMM and the top-k combine after it (oracle.route).
 
 Two public specifications that the pages rely on but do not print supply the
 value tables: the NF4 data type (QLoRA, Dettmers et al. 2023, appendix E) and
@@ -43,6 +46,7 @@ from .grouped import (offsets, grouped_ref, loop_ref, dgrad_ref,
                       brute_force_dgrad)
 from .block import (silu, swiglu_ref, bf16_rne_from_f64, expert_block_ref,
                     sampled_block_ref, brute_force_block)
+from .route import route_sort_ref, gather_ref, combine_ref, brute_force_route
 
 PARITY = {
     "NF4_TABLE_F32": "pinned: published decimal values and closed-form quantiles",
@@ -61,6 +65,10 @@ PARITY = {
                          "a double-rounding case, subnormals, ties to even",
     "expert_block_ref": "pinned: pure-Python brute force (math.fsum, math.exp), "
                         "zero up rows give zero output, exact integer case",
+    "route_sort_ref": "pinned: pure-Python brute force, permutation and sortedness "
+                      "invariants, the order loop_ref meets rows in",
+    "combine_ref": "pinned: one-hot weights give the routed row exactly, "
+                   "linearity in the weights, dropped slots",
 }
 
 __all__ = [n for n in dir() if not n.startswith("_")]
