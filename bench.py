@@ -295,10 +295,35 @@ def main_block(args, torch, geg, synthetic):
     def decode(wc, opts=None):
         blk(da, dsz, wc[0], wc[1], wc[2], wc[3], out=dout, workspace=dws, opts=opts)
 
+    # A whole MoE layer around the block: the router's top-k ids -> device sort and
+    # row gather -> fused block -> weighted combine back to token order.
+    ids = torch.from_numpy(synthetic.topk_ids(pg, args.seed).astype(np.int32)).to(dev)
+    xtok = torch.from_numpy(synthetic.activations_bf16(pg, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    wr = torch.full((pg.T, pg.top_k), 1.0 / pg.top_k, dtype=torch.float32, device=dev)
+    rws = geg.Workspace(geg.lib().geg_route_workspace_bytes(pg.T, pg.top_k, pg.E))
+    lsz, lro, lso, lxs = geg.route_sort(ids, pg.E, x=xtok, workspace=rws)
+    torch.cuda.synchronize()
+    assert (lsz.cpu().numpy() == sizes).all(), "device routing sort disagrees with the workload's sizes"
+    assert torch.equal(lxs.view(torch.int16), a.view(torch.int16)), "device gather disagrees with the grouped rows"
+    ly = torch.empty((pg.M, H), dtype=torch.bfloat16, device=dev)
+    lout = torch.empty((pg.T, H), dtype=torch.bfloat16, device=dev)
+
+    def route(wc, opts=None):
+        geg.route_sort(ids, pg.E, x=xtok, workspace=rws)
+
+    def combine(wc, opts=None):
+        geg.route_combine(ly, lro, wr, pg.top_k, out=lout)
+
+    def layer(wc, opts=None):
+        s_, ro_, so_, xs_ = geg.route_sort(ids, pg.E, x=xtok, workspace=rws)
+        blk(xs_, s_, wc[0], wc[1], wc[2], wc[3], out=ly, workspace=ws)
+        geg.route_combine(ly, ro_, wr, pg.top_k, out=lout)
+
     prefill(wcopies[0])
     decode(wcopies[0])
+    layer(wcopies[0])
     torch.cuda.synchronize()
-    assert ws.read_error() == 0 and dws.read_error() == 0, "device error word set"
+    assert ws.read_error() == 0 and dws.read_error() == 0 and rws.read_error() == 0, "device error word set"
     for i in range(args.warmup):
         prefill(wcopies[i % ncopies]); decode(wcopies[i % ncopies])
     torch.cuda.synchronize()
@@ -315,6 +340,9 @@ def main_block(args, torch, geg, synthetic):
     blk_ms = time_kernel(prefill, wcopies, args.steps, args.warmup, geg, torch, 0)
     tflops = flops / (pre_avg * 1e-3) / 1e12
     ktflops = flops / (blk_ms * 1e-3) / 1e12
+    route_ms, _ = time_calls(route, wcopies, args.steps, args.warmup, torch)
+    comb_ms, _ = time_calls(combine, wcopies, args.steps, args.warmup, torch)
+    layer_ms, _ = time_calls(layer, wcopies, args.steps, args.warmup, torch)
     dbytes = touched_weight_bytes(dg, dsizes) + touched_weight_bytes(ddn, dsizes)
     dec_ms, dec_how = time_calls(decode, wcopies, max(args.steps, 50), args.warmup, torch)
     dec_avg = float(np.mean(dec_ms))
@@ -329,6 +357,10 @@ def main_block(args, torch, geg, synthetic):
         "prefill": {"ms": round(pre_avg, 5), "gflop": flops / 1e9, "tflops": round(tflops, 2),
                     "timing": pre_how, "two_plain_gemms_ms": round(float(np.mean(un_ms)), 5),
                     "block_events_ms": round(blk_ms, 5)},
+        "moe_layer": {"tokens": pg.T, "route_sort_gather_ms": round(float(np.mean(route_ms)), 5),
+                      "combine_ms": round(float(np.mean(comb_ms)), 5),
+                      "layer_ms": round(float(np.mean(layer_ms)), 5),
+                      "timing": "hip graphs; sort + gather, block, combine on the device"},
         "decode": {"value": round(dbytes / (dec_avg * 1e-3) / 1e9, 1), "unit": "GB/s",
                    "ms": round(dec_avg, 5), "weight_bytes": dbytes, "timing": dec_how},
         "roofline": {"bound": "mfma", "achieved": round(ktflops, 2), "peak": round(PEAK_MFMA_TFLOPS, 1),

@@ -51,13 +51,19 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int32_t* __restric
   __shared__ int32_t tot[kMaxExperts];
   __shared__ int32_t base[kMaxExperts + 1];
   const int t = threadIdx.x;
+  // chunks 16 at a time: their loads are all in flight before the running sum
+  constexpr int B = 16;
   for (int e = t; e < E; e += kThreads) {
     int32_t run = 0;
-    for (int64_t c = 0; c < nchunks; ++c) {
-      int32_t* p = counts + c * E + e;
-      const int32_t v = *p;
-      *p = run;
-      run += v;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = c0 + j < nchunks ? counts[(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (c0 + j < nchunks) counts[(c0 + j) * E + e] = run;
+        run += v[j];
+      }
     }
     tot[e] = run;
     sizes[e] = run;
@@ -75,7 +81,14 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int32_t* __restric
   __syncthreads();
   for (int e = t; e < E; e += kThreads) {
     const int32_t b = base[e];
-    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += b;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = c0 + j < nchunks ? counts[(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        if (c0 + j < nchunks) counts[(c0 + j) * E + e] = v[j] + b;
+    }
   }
 }
 
@@ -112,13 +125,22 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* 
 __global__ __launch_bounds__(kThreads) void route_gather_kernel(const uint16_t* __restrict__ x, int64_t H, int32_t k,
                                                                 const int32_t* __restrict__ src_of, int64_t n,
                                                                 uint16_t* __restrict__ xs) {
+  // four rows per pass, their loads all in flight before the stores
+  constexpr int R = 4;
   const int64_t chunks = H >> 3;   // 16-byte pieces per row
-  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
-    const int32_t s = src_of[r];
-    if (s < 0) continue;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)(s / k) * H);
-    u32x4* dst = reinterpret_cast<u32x4*>(xs + r * H);
-    for (int64_t c = threadIdx.x; c < chunks; c += kThreads) dst[c] = src[c];
+  for (int64_t r0 = (int64_t)blockIdx.x * R; r0 < n; r0 += (int64_t)gridDim.x * R) {
+    int32_t s[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) s[u] = r0 + u < n ? src_of[r0 + u] : -1;
+    for (int64_t c = threadIdx.x; c < chunks; c += kThreads) {
+      u32x4 v[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (s[u] >= 0) v[u] = reinterpret_cast<const u32x4*>(x + (int64_t)(s[u] / k) * H)[c];
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (s[u] >= 0) reinterpret_cast<u32x4*>(xs + (r0 + u) * H)[c] = v[u];
+    }
   }
 }
 
@@ -172,7 +194,7 @@ hipError_t launch_route_sort(const int32_t* ids, int64_t n, int32_t E, int32_t* 
 
 hipError_t launch_route_gather(const uint16_t* x, int64_t H, int32_t k, const int32_t* src_of, int64_t n,
                                uint16_t* xs, int cus, hipStream_t s) {
-  const int64_t grid = std::min<int64_t>(n, (int64_t)cus * 8);
+  const int64_t grid = std::min<int64_t>((n + 3) / 4, (int64_t)cus * 8);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, H, k, src_of, n, xs);
   return hipGetLastError();
