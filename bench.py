@@ -54,6 +54,7 @@ WORKLOADS = {
     "mixtral_w2": ("mixtral_w2_t4096", None),
     "mixtral_dgrad": ("mixtral_dgrad_w13", None),
     "mixtral_dgrad_w2": ("mixtral_dgrad_w2", None),
+    "gptoss_dgrad": ("gptoss_dgrad_gate_up", None),
     # decode-class only (no prefill leg): value is packed-weight GB/s
     "qwen3_t64": (None, "qwen3_gate_up_t64"),
     "qwen3_down_t64": (None, "qwen3_down_t64"),
@@ -429,8 +430,10 @@ def main():
             dy = torch.from_numpy(synthetic.dgrad_dy_bf16(cp, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
             dx = torch.empty((cp.M, cp.K), dtype=torch.bfloat16, device=dev)
 
+            dfn = geg.gnf4_grouped_dgrad if cp.fmt == "nf4" else geg.gmxfp4_grouped_dgrad
+
             def prefill(wc, opts=None):
-                geg.gnf4_grouped_dgrad(dy, sz, wc[0], wc[1], dx=dx, workspace=ws, opts=opts)
+                dfn(dy, sz, wc[0], wc[1], dx=dx, workspace=ws, opts=opts)
         else:
             out = torch.empty((cp.M, cp.N), dtype=torch.bfloat16, device=dev)
 

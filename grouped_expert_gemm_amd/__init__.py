@@ -18,11 +18,11 @@ import threading
 
 __all__ = [
     "GegError", "Opts", "Workspace", "lib", "header_functions",
-    "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
-    "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
+    "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad", "gmxfp4_grouped_dgrad",
+    "grouped_linear", "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
     "geg_version", "geg_launch_count", "GEG_OP_NF4_FWD", "GEG_OP_MXFP4_FWD", "GEG_OP_NF4_DGRAD",
-    "GEG_OP_NF4_BLOCK", "GEG_OP_MXFP4_BLOCK", "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
+    "GEG_OP_NF4_BLOCK", "GEG_OP_MXFP4_BLOCK", "GEG_OP_MXFP4_DGRAD", "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
     "DEVERR_BAD_EXPERT_ID",
 ]
 
@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libgeg.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "geg.h")
 
 GEG_OP_NF4_FWD, GEG_OP_MXFP4_FWD, GEG_OP_NF4_DGRAD = 0, 1, 2
-GEG_OP_NF4_BLOCK, GEG_OP_MXFP4_BLOCK = 3, 4
+GEG_OP_NF4_BLOCK, GEG_OP_MXFP4_BLOCK, GEG_OP_MXFP4_DGRAD = 3, 4, 5
 DEVERR_NEGATIVE_SIZE, DEVERR_SIZES_EXCEED_M, DEVERR_FP16_RANGE = 0x1, 0x2, 0x4
 DEVERR_BAD_EXPERT_ID = 0x8
 
@@ -73,7 +73,8 @@ def lib() -> ctypes.CDLL:
                     "(hipcc, gfx950). There is no fallback implementation.")
             L = ctypes.CDLL(LIB_PATH)
             gemm_args = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P, _P]
-            for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad"):
+            for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
+                         "gmxfp4_grouped_dgrad"):
                 f = getattr(L, name)
                 f.argtypes, f.restype = gemm_args, ctypes.c_int
             L.geg_route_sort.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
@@ -258,21 +259,76 @@ def gmxfp4_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace
                  opts, stream)
 
 
-def gnf4_grouped_dgrad(dy, sizes, w, absmax, dx=None, workspace: Workspace | None = None,
-                       opts: Opts | None = None, stream=None):
-    """dy bf16 [M,N], w uint8 [E,N,K/2], absmax fp32 [E,N,K/64] -> dx bf16 [M,K]."""
+def _dgrad(fn_name, op, dy, sizes, w, scales, dx, workspace, opts, stream):
     import torch
-    _require_gpu(dy, sizes, w, absmax, dx)
+    _require_gpu(dy, sizes, w, scales, dx)
     M, N = dy.shape
     E, K = w.shape[0], w.shape[2] * 2
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
-    need = geg_workspace_bytes(GEG_OP_NF4_DGRAD, M, N, K, E, opts)
+    need = geg_workspace_bytes(op, M, N, K, E, opts)
     ws = _workspace(workspace, need, dy.device, stream)
-    _check(lib().gnf4_grouped_dgrad(_ptr(dy), _ptr(sizes), _ptr(w), _ptr(absmax), _ptr(dx), M, N, K, E,
-                                    _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None,
-                                    _stream(stream)))
+    _check(getattr(lib(), fn_name)(_ptr(dy), _ptr(sizes), _ptr(w), _ptr(scales), _ptr(dx), M, N, K, E,
+                                   _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None,
+                                   _stream(stream)))
     return dx
+
+
+def gnf4_grouped_dgrad(dy, sizes, w, absmax, dx=None, workspace: Workspace | None = None,
+                       opts: Opts | None = None, stream=None):
+    """dy bf16 [M,N], w uint8 [E,N,K/2], absmax fp32 [E,N,K/64] -> dx bf16 [M,K]."""
+    return _dgrad("gnf4_grouped_dgrad", GEG_OP_NF4_DGRAD, dy, sizes, w, absmax, dx, workspace, opts, stream)
+
+
+def gmxfp4_grouped_dgrad(dy, sizes, blocks, scales, dx=None, workspace: Workspace | None = None,
+                         opts: Opts | None = None, stream=None):
+    """dy bf16 [M,N], blocks uint8 [E,N,K/2], scales uint8 [E,N,K/32] -> dx bf16 [M,K]."""
+    if blocks.dim() == 4:
+        blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
+    return _dgrad("gmxfp4_grouped_dgrad", GEG_OP_MXFP4_DGRAD, dy, sizes, blocks, scales, dx, workspace, opts,
+                  stream)
+
+
+def grouped_linear(a, sizes, w, scales, fmt: str = "nf4"):
+    """The grouped 4-bit GEMM as a differentiable op (torch autograd): out = per
+    expert a_e W_e^T; the backward returns dA = per expert dOut_e W_e through the
+    library's dgrad kernel on the same packed bytes. The 4-bit weights are frozen
+    (no gradient), as in 4-bit adapter training."""
+    return _GroupedLinear.apply(a, sizes, w, scales, fmt)
+
+
+def _make_grouped_linear():
+    import torch
+
+    class GroupedLinear(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, a, sizes, w, scales, fmt):
+            ctx.save_for_backward(sizes, w, scales)
+            ctx.fmt = fmt
+            fn = gnf4_grouped_gemm if fmt == "nf4" else gmxfp4_grouped_gemm
+            return fn(a, sizes, w, scales)
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            sizes, w, scales = ctx.saved_tensors
+            fn = gnf4_grouped_dgrad if ctx.fmt == "nf4" else gmxfp4_grouped_dgrad
+            da = fn(grad_out.contiguous().to(torch.bfloat16), sizes, w, scales) if ctx.needs_input_grad[0] else None
+            return da, None, None, None, None
+
+    return GroupedLinear
+
+
+class _LazyFn:
+    def __init__(self):
+        self._f = None
+
+    def apply(self, *args):
+        if self._f is None:
+            self._f = _make_grouped_linear()
+        return self._f.apply(*args)
+
+
+_GroupedLinear = _LazyFn()
 
 
 def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream):

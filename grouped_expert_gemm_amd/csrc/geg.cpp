@@ -135,6 +135,11 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
+  if (op == GEG_OP_MXFP4_DGRAD) {   // bf16 dY feeds the MFMAs as it is
+    p.run_tile = M > 0;
+    p.total_bytes = kHeader;
+    return GEG_OK;
+  }
   // A decode-class batch (at most kDecodeAvgRows routed rows per expert on
   // average) keeps every expert off the tiled path: its few tiles would run one
   // per CU over the whole K range, slower than streaming the weights once per
@@ -352,6 +357,59 @@ geg_status block_common(int fmt, const void* a, const int32_t* sizes, const uint
   return GEG_OK;
 }
 
+geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uint8_t* w, const void* absmax,
+                        void* dx, int64_t M, int64_t N, int64_t K, int32_t E, void* workspace,
+                        size_t workspace_bytes, const geg_opts* opts, hipStream_t stream) {
+  geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
+  if (st != GEG_OK) return st;
+  if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");
+  Plan p;
+  if ((st = make_plan(fmt == geg::NF4 ? GEG_OP_NF4_DGRAD : GEG_OP_MXFP4_DGRAD, M, N, K, E, opts, p)) != GEG_OK)
+    return st;
+  if (M == 0) return GEG_OK;
+  if (!dy || !sizes || !w || !absmax || !dx) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!workspace) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(dy, 16) || !aligned(w, 16) || !aligned(dx, 16) || (fmt == geg::NF4 && !aligned(absmax, 4)) ||
+      !aligned(sizes, 4))
+    return fail(GEG_ERR_MISALIGNED, "dy, w and dx must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.total_bytes) return fail(GEG_ERR_WORKSPACE, "workspace too small");
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{dy, "dy"}, {sizes, "sizes"},
+                           {w, "w"}, {absmax, "absmax"}, {dx, "dx"}, {workspace, "workspace"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  geg::GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.a = reinterpret_cast<const uint16_t*>(dy);
+  g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
+  g.sizes = sizes;
+  g.wq = w;
+  g.scales = absmax;
+  g.out = reinterpret_cast<uint16_t*>(dx);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.E = E;
+  g.thresh = 0;   // every expert with rows goes through the tiled kernel
+  g.split = 1;
+  g.err = reinterpret_cast<uint32_t*>(wsb);
+  hipError_t e = hipSuccess;
+  if (fmt == geg::NF4) {
+    e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * N, g.err, stream);
+    if (e != hipSuccess) return hip_fail(e, "dY conversion launch");
+    ++g_launches;
+  }
+  const int64_t k_tiles = (K + geg::kTileN - 1) / geg::kTileN;
+  const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + std::min<int64_t>(E, M)) * k_tiles;
+  e = record_event(opts, 0, stream);
+  if (e == hipSuccess) e = geg::launch_tile_dgrad(fmt, g, persistent_grid(bound, 1), stream);
+  if (e == hipSuccess) e = record_event(opts, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -394,49 +452,15 @@ geg_status gnf4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_
                               const float* absmax, void* dx, int64_t M, int64_t N, int64_t K,
                               int32_t E, void* workspace, size_t workspace_bytes,
                               const geg_opts* opts, hipStream_t stream) {
-  geg_status st = check_shape(M, N, K, E, 64);
-  if (st != GEG_OK) return st;
-  if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");
-  Plan p;
-  if ((st = make_plan(GEG_OP_NF4_DGRAD, M, N, K, E, opts, p)) != GEG_OK) return st;
-  if (M == 0) return GEG_OK;
-  if (!dy || !sizes || !w || !absmax || !dx) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
-  if (!workspace) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(dy, 16) || !aligned(w, 16) || !aligned(dx, 16) || !aligned(absmax, 4) || !aligned(sizes, 4))
-    return fail(GEG_ERR_MISALIGNED, "dy, w and dx must be 16-byte aligned");
-  if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (workspace_bytes < p.total_bytes) return fail(GEG_ERR_WORKSPACE, "workspace too small");
-  if ((st = check_device()) != GEG_OK) return st;
-  for (auto [ptr, name] : {std::pair<const void*, const char*>{dy, "dy"}, {sizes, "sizes"},
-                           {w, "w"}, {absmax, "absmax"}, {dx, "dx"}, {workspace, "workspace"}})
-    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
-  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
-  geg::GemmArgs g;
-  std::memset(&g, 0, sizeof(g));
-  g.a = reinterpret_cast<const uint16_t*>(dy);
-  g.a16 = reinterpret_cast<const uint16_t*>(wsb + p.a16_off);
-  g.sizes = sizes;
-  g.wq = w;
-  g.scales = absmax;
-  g.out = reinterpret_cast<uint16_t*>(dx);
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.E = E;
-  g.thresh = 0;   // every expert with rows goes through the tiled kernel
-  g.split = 1;
-  g.err = reinterpret_cast<uint32_t*>(wsb);
-  hipError_t e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * N, g.err, stream);
-  if (e != hipSuccess) return hip_fail(e, "dY conversion launch");
-  ++g_launches;
-  const int64_t k_tiles = (K + geg::kTileN - 1) / geg::kTileN;
-  const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + std::min<int64_t>(E, M)) * k_tiles;
-  e = record_event(opts, 0, stream);
-  if (e == hipSuccess) e = geg::launch_tile_dgrad(g, persistent_grid(bound, 1), stream);
-  if (e == hipSuccess) e = record_event(opts, 1, stream);
-  if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
-  ++g_launches;
-  return GEG_OK;
+  return dgrad_common(geg::NF4, dy, sizes, w, absmax, dx, M, N, K, E, workspace, workspace_bytes, opts, stream);
+}
+
+geg_status gmxfp4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_t* blocks,
+                                const uint8_t* scales, void* dx, int64_t M, int64_t N, int64_t K,
+                                int32_t E, void* workspace, size_t workspace_bytes,
+                                const geg_opts* opts, hipStream_t stream) {
+  return dgrad_common(geg::MXFP4, dy, sizes, blocks, scales, dx, M, N, K, E, workspace, workspace_bytes, opts,
+                      stream);
 }
 
 size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
@@ -506,7 +530,7 @@ geg_status geg_route_combine(const void* y, const int32_t* row_of, const float* 
 
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
                            const geg_opts* opts) {
-  if (op < 0 || op > 4 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  if (op < 0 || op > 5 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
   if (op == GEG_OP_NF4_BLOCK || op == GEG_OP_MXFP4_BLOCK) {
     size_t act_off = 0, total = 0;
     if (block_layout(op == GEG_OP_NF4_BLOCK ? geg::NF4 : geg::MXFP4, M, N, K, E, opts, act_off, total) != GEG_OK)

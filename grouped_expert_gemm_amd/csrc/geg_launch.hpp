@@ -66,7 +66,7 @@ hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_vec(int fmt, const GemmArgs& g, int cus, hipStream_t s);      // sizes its own grid
 hipError_t launch_narrow(int fmt, const GemmArgs& g, int cus, hipStream_t s);   // sizes its own grid
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
-hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s);
+hipError_t launch_tile_dgrad(int fmt, const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,
                           uint16_t* bf16, uint16_t* f16, int64_t rows, int64_t K, hipStream_t s);
 hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,

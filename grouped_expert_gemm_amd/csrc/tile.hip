@@ -122,14 +122,22 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& g, int e, int64_t ro
   if constexpr (DG) {
     t.w = g.wq + (int64_t)e * N * (K >> 1);
     t.nw = clamp_bytes(N * (K >> 1));
-    t.s = reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6);
-    t.ns = clamp_bytes(N * (K >> 6) * 4);
     const int n = tid & 63, kc = tid >> 6;
     const int64_t kcol = o0 + 32 * kc;    // past K: never stored
     t.w_off = (uint32_t)(n * (K >> 1) + (kcol >> 1));
     t.w_step = (uint32_t)(BK * (K >> 1));
-    t.s_off = (uint32_t)((n * (K >> 6) + (kcol >> 6)) * 4);
-    t.s_step = (uint32_t)(BK * (K >> 6) * 4);
+    if constexpr (F == NF4) {
+      t.s = reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6);
+      t.ns = clamp_bytes(N * (K >> 6) * 4);
+      t.s_off = (uint32_t)((n * (K >> 6) + (kcol >> 6)) * 4);
+      t.s_step = (uint32_t)(BK * (K >> 6) * 4);
+    } else {
+      // the thread's 32 columns are exactly one 32-block of the weight row
+      t.s = reinterpret_cast<const uint8_t*>(g.scales) + (int64_t)e * N * (K >> 5);
+      t.ns = clamp_bytes(N * (K >> 5));
+      t.s_off = (uint32_t)(n * (K >> 5) + (kcol >> 5));
+      t.s_step = (uint32_t)(BK * (K >> 5));
+    }
   } else {
     const int64_t nrows = min<int64_t>(BN, N - o0);
     const int64_t wrow0 = (int64_t)e * N + o0;
@@ -201,12 +209,14 @@ template <> struct BDec<MXFP4> { float sc; };
 
 // Part j (0..3) of the decode state of stage k0 from the raw scale: NF4 builds
 // table entries 4j .. 4j+3; MXFP4 converts the block scale at j = 0.
-template <Fmt F>
+// dgrad (MXFP4): the thread's columns are one 32-block; columns past K are
+// never stored and weight rows past N read zero codes and a zero scale byte.
+template <Fmt F, bool DG = false>
 __device__ __forceinline__ void b_setup(BDec<F>& d, int j, const RawB& r, int64_t k0, int64_t K) {
   if constexpr (F == NF4) {
     nf4_scaled_lut_quarter_mix(r.s, j, d.lut);
   } else if (j == 0) {
-    const bool ok = k0 + 32 * (threadIdx.x & 1) < K;
+    const bool ok = DG || k0 + 32 * (threadIdx.x & 1) < K;
     d.sc = ok ? e8m0_to_f32(__builtin_bit_cast(uint32_t, r.s)) : 0.f;
   }
 }
@@ -286,7 +296,15 @@ __device__ __forceinline__ void b_step(int q, int r, const RawB& rb, const BDec<
         *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = u32x4{even[0], even[1], odd[0], odd[1]};
     }
   } else if (r == 0) {
-    *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = mxfp4_decode8(rb.c[q], d.sc);
+    const u32x4 v = mxfp4_decode8(rb.c[q], d.sc);   // k = 8q + j, natural order
+    if constexpr (DG) {
+      // column n of rows k = 32 (t/64) + 8 q + j (2-byte stores)
+      uint16_t* p = Bs + (32 * (t >> 6) + 8 * q) * kLdT + bcol;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j * kLdT] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+    } else {
+      *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = v;
+    }
   }
 }
 
@@ -375,13 +393,13 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
       store_a_piece<F, DG, TAIL>(ra, g, L.a[nxt], k1, C, wave, lane);
       load_a_piece(ra, g, src, st + 2, st + 2 < nst);
     }
-    if (g == 0 || g == 1) b_setup<F>(dec, g + 2, rb[P ^ 1], k1, K);
+    if (g == 0 || g == 1) b_setup<F, DG>(dec, g + 2, rb[P ^ 1], k1, K);
     if (g >= 2 && g < 14) {
       b_step<F, DG>((g - 2) / 3, (g - 2) % 3, rb[P ^ 1], dec, h, even, L.b[nxt], bcol, m4, base);
       if (g == 13) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
     }
     if (g == 13) __syncthreads();   // Y: the next stage's buffers are complete
-    if (g == 14 || g == 15) b_setup<F>(dec, g - 14, rb[P], k1 + BK, K);
+    if (g == 14 || g == 15) b_setup<F, DG>(dec, g - 14, rb[P], k1 + BK, K);
     // one MFMA, then up to two VALU instructions, four times
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -403,7 +421,9 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
   const uint32_t boff = (uint32_t)bpos<DG>(64 * wn + r16, lane >> 4);
-  const int bcol = ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7);   // dgrad staging column
+  // dgrad staging column: the weight row's contraction slot (NF4 slot order, or
+  // natural order for MXFP4's bf16 operands)
+  const int bcol = F == NF4 ? ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7) : (threadIdx.x & 63);
   constexpr int BR = 16 * (DG ? kLdT : BK);
   const int nst = (int)((C + BK - 1) / BK);
   uint32_t m4 = 0x04040404u, base = 0x03020100u;
@@ -424,7 +444,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
     NF4Half h;
     u32x2 even;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b_setup<F>(dec, j, rb[0], 0, K);
+    for (int j = 0; j < 4; ++j) b_setup<F, DG>(dec, j, rb[0], 0, K);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -432,8 +452,8 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   }
   load_a(ra, src, 1, nst > 1);
   load_b<F>(rb[0], src, 2, nst > 2);
-  b_setup<F>(dec, 0, rb[1], BK, K);
-  b_setup<F>(dec, 1, rb[1], BK, K);
+  b_setup<F, DG>(dec, 0, rb[1], BK, K);
+  b_setup<F, DG>(dec, 1, rb[1], BK, K);
   __syncthreads();
   if constexpr (H > 0) {
 #pragma unroll
@@ -449,8 +469,9 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   }
 }
 
-// Forward (DG = false): out[M, N] = a . W^T per expert. dgrad (DG = true, NF4):
-// out[M, K] = dY . W per expert, with `a16` holding dY as fp16.
+// Forward (DG = false): out[M, N] = a . W^T per expert. dgrad (DG = true):
+// out[M, K] = dY . W per expert (NF4: `a16` holds dY as fp16 in the slot order;
+// MXFP4 reads the bf16 dY directly).
 // TAIL: the contraction length is not a multiple of 64, so the last stage's
 // activation chunks past it must be zeroed (MXFP4 K, dgrad N).
 template <Fmt F, bool DG, bool TAIL>
@@ -597,8 +618,13 @@ hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_tile_dgrad(const GemmArgs& g, int grid, hipStream_t s) {
-  if (g.N % BK)
+hipError_t launch_tile_dgrad(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
+  if (fmt == MXFP4) {
+    if (g.N % BK)
+      hipLaunchKernelGGL((tile_kernel<MXFP4, true, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
+    else
+      hipLaunchKernelGGL((tile_kernel<MXFP4, true, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+  } else if (g.N % BK)
     hipLaunchKernelGGL((tile_kernel<NF4, true, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
   else
     hipLaunchKernelGGL((tile_kernel<NF4, true, false>), dim3(grid), dim3(kTileThreads), 0, s, g);

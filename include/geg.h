@@ -107,6 +107,7 @@ typedef struct {
 #define GEG_OP_NF4_DGRAD 2
 #define GEG_OP_NF4_BLOCK 3   /* N = H (hidden), K = I (intermediate) */
 #define GEG_OP_MXFP4_BLOCK 4 /* N = H (hidden), K = I (intermediate) */
+#define GEG_OP_MXFP4_DGRAD 5
 
 /*
  * gnf4_grouped_gemm — out[M, N] = per expert, a_e . W_e^T with W_e in NF4.
@@ -232,6 +233,17 @@ size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E);
  */
 geg_status geg_route_combine(const void* y, const int32_t* row_of, const float* weights, int64_t T,
                              int32_t k, int64_t N, void* out, hipStream_t stream);
+
+/*
+ * gmxfp4_grouped_dgrad — the input gradient of gmxfp4_grouped_gemm on the
+ * released MXFP4 bytes: dx[rows of e, :] = dy[rows of e, :] . W_e (contracts over
+ * N); blocks u8 [E, N, K/2], scales u8 [E, N, K/32], K % 32 == 0, N % 8 == 0.
+ * bf16 MFMA operands (dY as given; the decoded weights are exact in bf16).
+ */
+geg_status gmxfp4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint8_t* blocks,
+                                const uint8_t* scales, void* dx, int64_t M, int64_t N, int64_t K,
+                                int32_t E, void* workspace, size_t workspace_bytes,
+                                const geg_opts* opts, hipStream_t stream);
 
 /* Workspace bytes needed by one call of operation `op` with these sizes and options. */
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,

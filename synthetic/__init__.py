@@ -74,6 +74,8 @@ CASES = {c.name: c for c in [
     _mk("mixtral_w2_t4096", "nf4", 8, 14336, 4096, 4096, 2),
     _mk("mixtral_dgrad_w13", "nf4", 8, 4096, 28672, 4096, 2, op="dgrad"),
     _mk("mixtral_dgrad_w2", "nf4", 8, 14336, 4096, 4096, 2, op="dgrad"),
+    # input gradient of the gpt-oss gate_up projection on its released MXFP4 bytes
+    _mk("gptoss_dgrad_gate_up", "mxfp4", 32, 2880, 5760, 2048, 4, op="dgrad"),
 ]}
 
 
