@@ -171,6 +171,27 @@ def _require_gpu(*ts):
                               "(the CPU oracle under oracle/ is the reference for host data)")
 
 
+def _check_tensor(t, name, dtype, shape):
+    """dtype, shape and dense row-major layout of one operand: the C entry points
+    take bare pointers and sizes, so this is the only place they can be checked."""
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise GegError(2, f"{name}: expected a contiguous {dtype} tensor of shape {list(shape)}, got "
+                          f"{t.dtype} {list(t.shape)}{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _check_packed(nf4: bool, w, scales, E, N, K, wname, sname):
+    """Packed 4-bit weights [E, N, K/2] with fp32 absmax [E, N, K/64] (NF4) or
+    e8m0 bytes [E, N, K/32] (MXFP4)."""
+    import torch
+    _check_tensor(w, wname, torch.uint8, (E, N, K // 2))
+    if nf4:
+        _check_tensor(scales, sname, torch.float32, (E, N, K // 64))
+    else:
+        _check_tensor(scales, sname, torch.uint8, (E, N, K // 32))
+
+
 def geg_version() -> int:
     return lib().geg_version()
 
@@ -229,9 +250,13 @@ def _workspace(ws, need, device, stream):
 
 def _gemm(fn_name, op, a, sizes, wq, scales, out, workspace, opts, stream):
     import torch
-    _require_gpu(a, sizes, wq, scales, out)
     M, K = a.shape
     E, N = wq.shape[0], wq.shape[1]
+    _check_tensor(a, "a", torch.bfloat16, (M, K))
+    _check_tensor(sizes, "sizes", torch.int32, (E,))
+    _check_packed(op == GEG_OP_NF4_FWD, wq, scales, E, N, K, "weights", "scales")
+    _check_tensor(out, "out", torch.bfloat16, (M, N))
+    _require_gpu(a, sizes, wq, scales, out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     need = geg_workspace_bytes(op, M, N, K, E, opts)
@@ -261,9 +286,13 @@ def gmxfp4_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace
 
 def _dgrad(fn_name, op, dy, sizes, w, scales, dx, workspace, opts, stream):
     import torch
-    _require_gpu(dy, sizes, w, scales, dx)
     M, N = dy.shape
     E, K = w.shape[0], w.shape[2] * 2
+    _check_tensor(dy, "dy", torch.bfloat16, (M, N))
+    _check_tensor(sizes, "sizes", torch.int32, (E,))
+    _check_packed(op == GEG_OP_NF4_DGRAD, w, scales, E, N, K, "weights", "scales")
+    _check_tensor(dx, "dx", torch.bfloat16, (M, K))
+    _require_gpu(dy, sizes, w, scales, dx)
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
     need = geg_workspace_bytes(op, M, N, K, E, opts)
@@ -333,9 +362,15 @@ _GroupedLinear = _LazyFn()
 
 def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream):
     import torch
-    _require_gpu(a, sizes, w13, s13, w2, s2, out)
     M, H = a.shape
     E, I = w13.shape[0], w13.shape[1] // 2
+    nf4 = op == GEG_OP_NF4_BLOCK
+    _check_tensor(a, "a", torch.bfloat16, (M, H))
+    _check_tensor(sizes, "sizes", torch.int32, (E,))
+    _check_packed(nf4, w13, s13, E, 2 * I, H, "w13", "scales13")
+    _check_packed(nf4, w2, s2, E, H, I, "w2", "scales2")
+    _check_tensor(out, "out", torch.bfloat16, (M, H))
+    _require_gpu(a, sizes, w13, s13, w2, s2, out)
     if out is None:
         out = torch.empty((M, H), dtype=torch.bfloat16, device=a.device)
     need = geg_workspace_bytes(op, M, H, I, E, opts)
@@ -374,8 +409,11 @@ def route_sort(topk_ids, E: int, x=None, workspace: Workspace | None = None, str
     entries ordered by expert, then by t*k + slot; x_sorted bf16 [T*k, H] holds
     x[src_of[r] // k] in sorted row r when x (bf16 [T, H]) is given, else None."""
     import torch
-    _require_gpu(topk_ids, x)
     T, k = topk_ids.shape
+    _check_tensor(topk_ids, "topk_ids", torch.int32, (T, k))
+    if x is not None:
+        _check_tensor(x, "x", torch.bfloat16, (T, x.shape[1]))
+    _require_gpu(topk_ids, x)
     dev = topk_ids.device
     sizes = torch.empty((E,), dtype=torch.int32, device=dev)
     row_of = torch.empty((T * k,), dtype=torch.int32, device=dev)
@@ -396,9 +434,13 @@ def route_combine(y, row_of, weights, k: int, out=None, stream=None):
     """out bf16 [T, N] = sum over slots of weights[t, s] * y[row_of[t*k + s]] (fp32 in
     slot order); y bf16 [T*k, N] in routing-sort order, weights fp32 [T, k] or None."""
     import torch
-    _require_gpu(y, row_of, weights, out)
     T = row_of.numel() // k
     N = y.shape[1]
+    _check_tensor(row_of, "row_of", torch.int32, (T * k,))
+    _check_tensor(y, "y", torch.bfloat16, (T * k, N))
+    _check_tensor(weights, "weights", torch.float32, (T, k))
+    _check_tensor(out, "out", torch.bfloat16, (T, N))
+    _require_gpu(y, row_of, weights, out)
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=y.device)
     _check(lib().geg_route_combine(_ptr(y), _ptr(row_of), _ptr(weights), T, k, N, _ptr(out), _stream(stream)))
@@ -407,8 +449,9 @@ def route_combine(y, row_of, weights, k: int, out=None, stream=None):
 
 def _dequant(fn_name, wq, scales, bf16, f16, stream):
     import torch
-    _require_gpu(wq, scales)
     E, N, K = wq.shape[0], wq.shape[1], wq.shape[2] * 2
+    _check_packed(fn_name == "gnf4_dequant", wq, scales, E, N, K, "weights", "scales")
+    _require_gpu(wq, scales)
     f32 = torch.empty((E, N, K), dtype=torch.float32, device=wq.device)
     ob = torch.empty((E, N, K), dtype=torch.bfloat16, device=wq.device) if bf16 else None
     oh = torch.empty((E, N, K), dtype=torch.float16, device=wq.device) if f16 else None

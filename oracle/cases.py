@@ -79,6 +79,20 @@ def nf4_cols_fn(c: synthetic.Case, seed: int):
     return f
 
 
+def mxfp4_cols_fn(c: synthetic.Case, seed: int):
+    """weight_cols(e, k_idx) -> fp64 [N, len(k_idx)]: decodes only the 32-wide
+    blocks (16 code bytes and one scale byte per row) that hold the columns."""
+    def f(e, k_idx):
+        k_idx = np.asarray(k_idx)
+        codes, scales = synthetic.mxfp4_bytes(c, seed, e)
+        blocks = np.unique(k_idx // 32)
+        sub_c = np.concatenate([codes[:, 16 * b:16 * (b + 1)] for b in blocks], axis=1)
+        dq = dequant_mxfp4(np.ascontiguousarray(sub_c), np.ascontiguousarray(scales[:, blocks]))
+        pos = {int(b): i for i, b in enumerate(blocks)}
+        return dq[:, [32 * pos[int(k) // 32] + int(k) % 32 for k in k_idx]]
+    return f
+
+
 def mxfp4_rows_fn(c: synthetic.Case, seed: int):
     def f(e, n_idx):
         codes, scales = synthetic.mxfp4_bytes(c, seed, e)

@@ -110,3 +110,33 @@ def test_python_binding_refuses_cpu_tensors():
         geg.gnf4_grouped_gemm(a, torch.zeros(1, dtype=torch.int32),
                               torch.zeros((1, 8, 32), dtype=torch.uint8),
                               torch.zeros((1, 8, 1), dtype=torch.float32))
+
+
+def test_python_binding_checks_operand_types_and_shapes():
+    # the C entry points take bare pointers, so the binding checks every operand's
+    # dtype and shape before anything reaches the device: MXFP4 scale bytes handed
+    # to the NF4 entry point (or the reverse) are refused, not read as fp32
+    torch = pytest.importorskip("torch")
+    E, N, K, M = 2, 8, 128, 4
+    a = torch.zeros((M, K), dtype=torch.bfloat16)
+    sizes = torch.zeros(E, dtype=torch.int32)
+    w = torch.zeros((E, N, K // 2), dtype=torch.uint8)
+    nf4_s = torch.zeros((E, N, K // 64), dtype=torch.float32)
+    mx_s = torch.zeros((E, N, K // 32), dtype=torch.uint8)
+    dy = torch.zeros((M, N), dtype=torch.bfloat16)
+    for call in (lambda: geg.gnf4_grouped_gemm(a, sizes, w, mx_s),
+                 lambda: geg.gmxfp4_grouped_gemm(a, sizes, w, nf4_s),
+                 lambda: geg.gnf4_grouped_dgrad(dy, sizes, w, mx_s),
+                 lambda: geg.gmxfp4_grouped_dgrad(dy, sizes, w, nf4_s),
+                 lambda: geg.gnf4_grouped_gemm(a.float(), sizes, w, nf4_s),
+                 lambda: geg.gnf4_grouped_gemm(a, sizes.long(), w, nf4_s),
+                 lambda: geg.gnf4_grouped_gemm(a[:, :64], sizes, w, nf4_s),
+                 lambda: geg.gnf4_grouped_gemm(a, sizes, w.transpose(1, 2).contiguous().transpose(1, 2), nf4_s),
+                 lambda: geg.gnf4_dequant(w, mx_s),
+                 lambda: geg.route_combine(torch.zeros((6, 16), dtype=torch.bfloat16),
+                                           torch.zeros(8, dtype=torch.int32), None, 2)):
+        with pytest.raises(geg.GegError, match="GEG_ERR_BAD_SHAPE"):
+            call()
+    # well-formed operands get as far as the device check
+    with pytest.raises(geg.GegError, match="GPU"):
+        geg.gmxfp4_grouped_dgrad(dy, sizes, w, mx_s)

@@ -73,7 +73,8 @@ def test_dgrad_full_size(geg, name):
     log(f"case: {name} dgrad (M={c.M} N={c.N} K={c.K} E={c.E}) seed={seed}")
     a_bits, sizes, w, s = _inputs(c, seed)
     dy = synthetic.dgrad_dy_bf16(c, seed)
-    dx = geg.gnf4_grouped_dgrad(up_u16_as_bf16(dy), up(sizes), w, s)
+    fn = geg.gnf4_grouped_dgrad if c.fmt == "nf4" else geg.gmxfp4_grouped_dgrad
+    dx = fn(up_u16_as_bf16(dy), up(sizes), w, s)
     rows, cols = sample_positions(sizes, c.K, 600, seed=2)
     # keep the sampled columns inside a few 64-wide blocks (plus the last one) so
     # the oracle packs only those blocks of each expert
@@ -81,5 +82,6 @@ def test_dgrad_full_size(geg, name):
     blocks = np.append(rng.choice(c.K // 64 - 1, 3, replace=False), c.K // 64 - 1)
     cols = blocks[cols % 4] * 64 + cols % 64
     got = bf16_to_f64(dx)[rows, cols]
-    ref = oracle.sampled_dgrad_ref(dy, sizes, C.nf4_cols_fn(c, seed), rows, cols)
+    cols_fn = C.nf4_cols_fn(c, seed) if c.fmt == "nf4" else C.mxfp4_cols_fn(c, seed)
+    ref = oracle.sampled_dgrad_ref(dy, sizes, cols_fn, rows, cols)
     assert_close(got, ref, name + " dgrad")

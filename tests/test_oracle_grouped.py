@@ -154,3 +154,23 @@ def test_sampled_refs_match_full_refs():
     kcols = rng.integers(0, c.K, 50)
     gotd = oracle.sampled_dgrad_ref(dy, d["sizes"], C.nf4_cols_fn(c, 1), rows, kcols)
     np.testing.assert_allclose(gotd, fulld[rows, kcols], rtol=1e-12, atol=1e-14)
+
+
+def test_sampled_mxfp4_refs_match_full_refs():
+    # the MXFP4 row and column decoders used at full size against the whole-expert
+    # decode (K of 288: nine 32-blocks, an odd count of them)
+    c = synthetic.Case("t", "mxfp4", 3, 288, 96, 16, 2)
+    d = C.build(c, 2)
+    W = C.weight_fn(d)
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, c.M, 40)
+    cols = rng.integers(0, c.N, 40)
+    full = oracle.grouped_ref(d["a_bits"], d["sizes"], W, c.N)
+    got = oracle.sampled_fwd_ref(d["a_bits"], d["sizes"], C.mxfp4_rows_fn(c, 2), rows, cols)
+    np.testing.assert_allclose(got, full[rows, cols], rtol=1e-12, atol=1e-14)
+    dy = synthetic.dgrad_dy_bf16(c, 2)
+    fulld = oracle.dgrad_ref(dy, d["sizes"], W, c.K)
+    kcols = np.append(rng.integers(0, c.K, 40), [0, 31, 32, c.K - 1])
+    rows2 = np.append(rows, rows[:4])
+    gotd = oracle.sampled_dgrad_ref(dy, d["sizes"], C.mxfp4_cols_fn(c, 2), rows2, kcols)
+    np.testing.assert_allclose(gotd, fulld[rows2, kcols], rtol=1e-12, atol=1e-14)
