@@ -116,7 +116,10 @@ template <Fmt F, int RB, int CBW, int NS, bool SSC>
 __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   // step st stages step st+1 from registers loaded two steps earlier
   static_assert(NS >= 3, "the staged step must already be in registers");
-  __shared__ Plan plan;
+  // routing plan in dynamic LDS sized by the expert count: off[E + 1], upre[E + 1]
+  extern __shared__ __attribute__((aligned(16))) int32_t nplan[];
+  int32_t* const poff = nplan;
+  int32_t* const pupre = nplan + g.E + 1;
   // two stage buffers; the zero chunk after each row block is what the
   // activation lanes of the other 64-block read (NF4)
   constexpr int kBuf = RB * kRBlk;
@@ -125,9 +128,16 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   constexpr int CPU = 4 * 16 * CBW;                // weight rows per unit
   const int32_t n_cols = (int32_t)((g.N + CPU - 1) / CPU);
   const int64_t lo = max<int64_t>(1, (int64_t)g.vec_rows + 1), hi = g.thresh;
-  const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
-    return (s >= lo && s <= hi) ? ((s + RPU - 1) / RPU) * n_cols : 0;
-  });
+  constexpr bool kSplit = F == NF4 && RB == 1;   // per-block MFMA partials, shared table
+  // 16-row NF4 units decode through the 32-copy byte table in LDS (two VALU
+  // instructions and one conflict-free LDS read per code byte)
+  __shared__ __attribute__((aligned(16))) uint32_t blut[kSplit ? nf4_byte_lut_words<32>() : 4];
+  const int32_t total = build_plan(
+      poff, pupre, g.sizes, g.E, g.M, g.err,
+      [&](int32_t s) -> int32_t { return (s >= lo && s <= hi) ? ((s + RPU - 1) / RPU) * n_cols : 0; },
+      [&] {
+        if constexpr (kSplit) nf4_byte_lut_fill<32>(blut);   // ordered by the plan's barrier
+      });
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -136,13 +146,11 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   uint32_t range = 0;
   uint32_t m4, base;
   nf4_selector_consts(m4, base);
-  constexpr bool kSplit = F == NF4 && RB == 1;   // per-block MFMA partials, shared table
   constexpr int kNsc = kSplit ? 2 : 1;
   static_assert(!SSC || kSplit, "staged scales serve the 16-row NF4 units");
   constexpr int kSscLd = 34;                       // floats per staged row (even, bank-spreading)
   __shared__ __attribute__((aligned(16))) float Ssc[SSC ? 64 * CBW * kSscLd : 2];
-  Lut16 lut{};
-  if constexpr (kSplit) lut = nf4_scaled_lut(1.0f);
+  const uint32_t lane_off = nf4_byte_lut_lane<32>(lane);
   if (t < 2 * RB)
     *reinterpret_cast<u32x4*>(&As[t / RB][(t % RB) * kRBlk + kRBlk - 8]) = u32x4{0u, 0u, 0u, 0u};
   // A operand offsets within a stage buffer for MFMA j of row block 0 (row
@@ -158,10 +166,10 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
   }
 
   for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
-    const int e = find_expert(plan, g.E, u);
-    const int32_t lu = u - plan.upre[e];
-    const int64_t row0 = plan.off[e] + (int64_t)(lu / n_cols) * RPU;
-    const int rows = (int)min<int64_t>(RPU, plan.off[e + 1] - row0);
+    const int e = find_expert(pupre, g.E, u);
+    const int32_t lu = u - pupre[e];
+    const int64_t row0 = poff[e] + (int64_t)(lu / n_cols) * RPU;
+    const int rows = (int)min<int64_t>(RPU, poff[e + 1] - row0);
     const int64_t n0 = (int64_t)(lu % n_cols) * CPU + 16 * CBW * wave;
     const __amdgpu_buffer_rsrc_t A = nrsrc(g.a + row0 * K, (int64_t)rows * K * 2);
     const __amdgpu_buffer_rsrc_t W = nrsrc(g.wq + (int64_t)e * N * (K >> 1), N * (K >> 1));
@@ -181,7 +189,10 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < RB; ++q) {
         u32x4 v = r.a[q];
-        if constexpr (F == NF4) v = bf16x8_to_f16_slots(v, range);
+        if constexpr (kSplit)
+          v = bf16x8_to_f16(v, range);        // natural order, as the byte table decodes
+        else if constexpr (F == NF4)
+          v = bf16x8_to_f16_slots(v, range);
         *reinterpret_cast<u32x4*>(&Ab[nswz(16 * q + (t >> 4), t & 15)]) = v;
       }
     };
@@ -252,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
                 for (int r = 0; r < RB; ++r) part[h][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const u32x4 b = nf4_decode8(lut, cur.w[cb][j], m4, base);
+                const u32x4 b = nf4_byte_lut_decode8<32>(blut, cur.w[cb][j], lane_off);
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -333,17 +344,20 @@ __global__ __launch_bounds__(kThreads, 3) void narrow_kernel(GemmArgs g) {
 template <Fmt F, int RB, int CBW, int NS, bool SSC = false>
 hipError_t launch_n(const GemmArgs& g, int cus, hipStream_t s) {
   auto k = narrow_kernel<F, RB, CBW, NS, SSC>;
+  const size_t dyn = (size_t)2 * (g.E + 1) * sizeof(int32_t);
+  static size_t cached_dyn = 0;
   static int per_cu = 0;
-  if (per_cu == 0) {
+  if (per_cu == 0 || cached_dyn != dyn) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, kThreads, 0) != hipSuccess || b <= 0) b = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, kThreads, dyn) != hipSuccess || b <= 0) b = 1;
     per_cu = b;
+    cached_dyn = dyn;
   }
   constexpr int RPU = 16 * RB, CPU = 64 * CBW;
   const int64_t chunks = (g.M + RPU - 1) / RPU + std::min<int64_t>(g.E, g.M);
   const int64_t units = chunks * ((g.N + CPU - 1) / CPU);
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)per_cu * cus));
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), dyn, s, g);
   return hipGetLastError();
 }
 
