@@ -29,6 +29,9 @@ section):
 * The capability index's `entrypoints` (`router_epilogue`, `combine_rows`) and
   releases v0.2.6 "The patch point": the routing sort in front of the grouped
   GEMM and the top-k combine after it (oracle.route).
+* "bw24 releases, v0.9.0", "Changes since v0.8.0": the W4A8 variant, e4m3
+  activations times native e2m1 weights in one block-scaled matrix instruction
+  (oracle.w4a8, with its readings of the activation scaling stated there).
 
 Two public specifications that the pages rely on but do not print supply the
 value tables: the NF4 data type (QLoRA, Dettmers et al. 2023, appendix E) and
@@ -47,6 +50,8 @@ from .grouped import (offsets, grouped_ref, loop_ref, dgrad_ref,
 from .block import (silu, swiglu_ref, bf16_rne_from_f64, expert_block_ref,
                     sampled_block_ref, brute_force_block)
 from .route import route_sort_ref, gather_ref, combine_ref, brute_force_route
+from .w4a8 import (E4M3_TABLE, e4m3_value, e4m3_round, mxfp8_scale_bytes, quantize_mxfp8,
+                   dequant_mxfp8, w4a8_grouped_ref, sampled_w4a8_ref, brute_force_w4a8)
 
 PARITY = {
     "NF4_TABLE_F32": "pinned: published decimal values and closed-form quantiles",
@@ -69,6 +74,12 @@ PARITY = {
                       "invariants, the order loop_ref meets rows in",
     "combine_ref": "pinned: one-hot weights give the routed row exactly, "
                    "linearity in the weights, dropped slots",
+    "E4M3_TABLE / e4m3_round": "pinned: torch float8_e4m3fn values and conversion "
+                               "(every tie midpoint included), saturation at 448",
+    "quantize_mxfp8": "pinned: OCP scale rule on hand-worked blocks, block maximum in "
+                      "[256, 512), half-step error bound",
+    "w4a8_grouped_ref": "pinned: pure-Python brute force (exhaustive nearest e4m3 "
+                        "search, math.fsum), closeness to the bf16 product",
 }
 
 __all__ = [n for n in dir() if not n.startswith("_")]
