@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "grouped 4-bit GEMM TFLOP/s (prefill) + packed-weight HBM GB/s (decode), 1 GPU"
 PEAK_MFMA_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # dense fp16/bf16 MFMA, 2516.6
+PEAK_FP8_TFLOPS = 2 * PEAK_MFMA_TFLOPS   # dense fp8 MFMA (fp8 x fp4 runs at the fp8 rate): 5.0 PFLOP/s published
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 2.5e9
 
@@ -55,6 +56,9 @@ WORKLOADS = {
     "mixtral_dgrad": ("mixtral_dgrad_w13", None),
     "mixtral_dgrad_w2": ("mixtral_dgrad_w2", None),
     "gptoss_dgrad": ("gptoss_dgrad_gate_up", None),
+    # W4A8: activations quantised to MXFP8 on the device, block-scaled fp8 x fp4 MFMA
+    "gptoss_w4a8": ("gptoss_gate_up_t2048", None),
+    "gptoss_down_w4a8": ("gptoss_down_t2048", None),
     # decode-class only (no prefill leg): value is packed-weight GB/s
     "qwen3_t64": (None, "qwen3_gate_up_t64"),
     "qwen3_down_t64": (None, "qwen3_down_t64"),
@@ -62,11 +66,12 @@ WORKLOADS = {
 # Fused expert block (gate_up -> SwiGLU -> down in one call): the gate_up and down
 # cases of one model share their routing; (prefill gate_up, prefill down, decode
 # gate_up, decode down).
+W4A8_WORKLOADS = {"gptoss_w4a8", "gptoss_down_w4a8"}
 BLOCK_WORKLOADS = {
     "qwen3_block": ("qwen3_gate_up_t4096", "qwen3_down_t4096", "qwen3_gate_up_t1", "qwen3_down_t1"),
     "gptoss_block": ("gptoss_gate_up_t2048", "gptoss_down_t2048", "gptoss_gate_up_t1", "gptoss_down_t1"),
 }
-KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip", "route.hip",
+KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip", "route.hip", "w4a8.hip",
                   "geg.cpp"]
 
 
@@ -164,10 +169,12 @@ def time_kernel(fn, copies, steps, warmup, geg, torch, slot, force_path=0):
     return float(np.mean(ms)) if ms else None
 
 
-def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s"):
+def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s", w4a8=False):
     """The fp64 oracle (decode each expert to fp64, one matmul per expert) on as
     many of the case's experts as fit in about budget_s seconds (at least one),
-    as TFLOP/s or, for decode-class cases, packed-weight GB/s."""
+    as TFLOP/s or, for decode-class cases, packed-weight GB/s. With w4a8, the
+    oracle of that variant: each expert's rows quantised to MXFP8 first (timed
+    with the matmul)."""
     import oracle
     import synthetic
     from oracle import cases as C
@@ -193,7 +200,10 @@ def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s"):
         W = oracle.dequant_nf4(q, s) if c.fmt == "nf4" else oracle.dequant_mxfp4(q, s)
         t1 = time.perf_counter()
         rows = a_bits[off[e]:off[e + 1]]
-        out = oracle.grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, c.N)
+        if w4a8:
+            out = oracle.w4a8_grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, c.N)
+        else:
+            out = oracle.grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, c.N)
         t2 = time.perf_counter()
         t_dq += t1 - t0
         t_mm += t2 - t1
@@ -213,7 +223,7 @@ def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s"):
     return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
             "sample": f"{c.name}: {used} expert GEMMs (cycling over the first {len(packed)} of "
                       f"{int(np.count_nonzero(sizes))} routed experts, {int(flops / 2 / c.N / c.K)} rows), "
-                      "fp64 decode + numpy matmul",
+                      + ("MXFP8 activation quantisation + " if w4a8 else "") + "fp64 decode + numpy matmul",
             "seconds": secs, "dequant_s": t_dq, "matmul_s": t_mm,
             "host_cpus": os.cpu_count()}
 
@@ -415,7 +425,10 @@ def main():
         return
     pre_name, dec_name = WORKLOADS[args.workload]
     cp = synthetic.case(pre_name or dec_name)
+    w4a8 = args.workload in W4A8_WORKLOADS
     fn = geg.gnf4_grouped_gemm if cp.fmt == "nf4" else geg.gmxfp4_grouped_gemm
+    if w4a8:
+        fn = geg.gmxfp4_w4a8_grouped_gemm
 
     # The weight stack of the workload (the decode leg uses the same experts).
     a, sz, sizes, codes, scales = make_inputs(cp, args.seed, torch, geg, dev)
@@ -484,7 +497,7 @@ def main():
         "metric": METRIC, "value": None, "unit": None, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp16" if cp.fmt == "nf4" else "bf16", "data": "synthetic",
+        "dtype": "fp8xfp4" if w4a8 else ("fp16" if cp.fmt == "nf4" else "bf16"), "data": "synthetic",
         "config": {"workload": " + ".join(x for x in (pre_name, dec_name) if x),
                    "format": cp.fmt, "E": cp.E, "K": cp.K, "N": cp.N,
                    "prefill_rows": cp.M if pre_name else 0,
@@ -501,15 +514,17 @@ def main():
         tflops = flops / (pre_avg * 1e-3) / 1e12
         kern_ms = time_kernel(prefill, wcopies, args.steps, args.warmup, geg, torch, 0)
         ktflops = flops / (kern_ms * 1e-3) / 1e12
+        peak = PEAK_FP8_TFLOPS if w4a8 else PEAK_MFMA_TFLOPS
         result["value"], result["unit"] = round(tflops, 2), "TFLOP/s"
         result["prefill"] = {"ms": round(pre_avg, 5), "ms_min": round(float(np.min(pre_ms)), 5),
                              "gflop": flops / 1e9, "tflops": round(tflops, 2), "timing": pre_how,
                              "kernel_ms": round(kern_ms, 5), "kernel_tflops": round(ktflops, 2),
-                             "frac_of_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS, 4)}
-        roof = {"bound": "mfma", "achieved": round(ktflops, 2), "peak": round(PEAK_MFMA_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(ktflops / PEAK_MFMA_TFLOPS, 4),
-                "kernel": ("dgrad (tiled) kernel" if cp.op == "dgrad" else "tiled kernel")
-                          + f" ({cp.fmt}), {cp.name}",
+                             "frac_of_mfma_peak": round(tflops / peak, 4)}
+        kname = ("W4A8 kernel (block-scaled fp8 x fp4 MFMA)" if w4a8
+                 else "dgrad (tiled) kernel" if cp.op == "dgrad" else "tiled kernel")
+        roof = {"bound": "mfma", "achieved": round(ktflops, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(ktflops / peak, 4),
+                "kernel": kname + f" ({cp.fmt}), {cp.name}",
                 "per_launch_gflop": round(flops / 1e9, 3), "kernel_ms": round(kern_ms, 5)}
     if dec:
         cd, dsizes, decode = dec
@@ -532,7 +547,7 @@ def main():
                     "per_launch_bytes": dbytes, "kernel_ms": round(kern_ms, 5)}
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
-    tname = pre_name or dec_name
+    tname = (pre_name or dec_name) + (":w4a8" if w4a8 else "")
     if os.path.exists(tfile):
         try:
             rec = json.load(open(tfile)).get(tname)
@@ -543,7 +558,7 @@ def main():
     roof["traffic"] = traffic
     result["roofline"] = roof
     if not args.no_cpu_baseline and cp.op == "fwd":
-        result["cpu_baseline"] = cpu_baseline(cp, args.seed, args.cpu_budget, result["unit"])
+        result["cpu_baseline"] = cpu_baseline(cp, args.seed, args.cpu_budget, result["unit"], w4a8=w4a8)
     result["kernel_sha"] = kernel_sha()
     print(json.dumps(result), flush=True)
 

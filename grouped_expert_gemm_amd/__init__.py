@@ -21,6 +21,7 @@ __all__ = [
     "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad", "gmxfp4_grouped_dgrad",
     "grouped_linear", "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
+    "gmxfp4_w4a8_grouped_gemm", "gmxfp8_quantize", "GEG_OP_MXFP4_W4A8", "DEVERR_NON_FINITE",
     "geg_version", "geg_launch_count", "GEG_OP_NF4_FWD", "GEG_OP_MXFP4_FWD", "GEG_OP_NF4_DGRAD",
     "GEG_OP_NF4_BLOCK", "GEG_OP_MXFP4_BLOCK", "GEG_OP_MXFP4_DGRAD", "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
     "DEVERR_BAD_EXPERT_ID",
@@ -32,8 +33,9 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "geg.h")
 
 GEG_OP_NF4_FWD, GEG_OP_MXFP4_FWD, GEG_OP_NF4_DGRAD = 0, 1, 2
 GEG_OP_NF4_BLOCK, GEG_OP_MXFP4_BLOCK, GEG_OP_MXFP4_DGRAD = 3, 4, 5
+GEG_OP_MXFP4_W4A8 = 6
 DEVERR_NEGATIVE_SIZE, DEVERR_SIZES_EXCEED_M, DEVERR_FP16_RANGE = 0x1, 0x2, 0x4
-DEVERR_BAD_EXPERT_ID = 0x8
+DEVERR_BAD_EXPERT_ID, DEVERR_NON_FINITE = 0x8, 0x10
 
 _STATUS = {0: "GEG_OK", 1: "GEG_ERR_NULL_POINTER", 2: "GEG_ERR_BAD_SHAPE", 3: "GEG_ERR_MISALIGNED",
            4: "GEG_ERR_NOT_DEVICE_MEMORY", 5: "GEG_ERR_WORKSPACE", 6: "GEG_ERR_UNSUPPORTED_DEVICE",
@@ -74,9 +76,10 @@ def lib() -> ctypes.CDLL:
             L = ctypes.CDLL(LIB_PATH)
             gemm_args = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P, _P]
             for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad",
-                         "gmxfp4_grouped_dgrad"):
+                         "gmxfp4_grouped_dgrad", "gmxfp4_w4a8_grouped_gemm"):
                 f = getattr(L, name)
                 f.argtypes, f.restype = gemm_args, ctypes.c_int
+            L.gmxfp8_quantize.argtypes, L.gmxfp8_quantize.restype = [_P, _P, _P, _I64, _I64, _P], ctypes.c_int
             L.geg_route_sort.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
             L.geg_route_sort.restype = ctypes.c_int
             L.geg_route_workspace_bytes.argtypes = [_I64, _I32, _I32]
@@ -316,6 +319,29 @@ def gmxfp4_grouped_dgrad(dy, sizes, blocks, scales, dx=None, workspace: Workspac
         blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
     return _dgrad("gmxfp4_grouped_dgrad", GEG_OP_MXFP4_DGRAD, dy, sizes, blocks, scales, dx, workspace, opts,
                   stream)
+
+
+def gmxfp4_w4a8_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace | None = None,
+                             opts: Opts | None = None, stream=None):
+    """W4A8: a bf16 [M,K] quantised on the device to MXFP8 (e4m3, one e8m0 scale per
+    32 k) times MXFP4 blocks uint8 [E,N,K/2] (or [E,N,K/32,16]) with scales uint8
+    [E,N,K/32] on the block-scaled matrix instruction -> out bf16 [M,N]."""
+    if blocks.dim() == 4:
+        blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
+    return _gemm("gmxfp4_w4a8_grouped_gemm", GEG_OP_MXFP4_W4A8, a, sizes, blocks, scales, out, workspace,
+                 opts, stream)
+
+
+def gmxfp8_quantize(a, stream=None):
+    """a bf16 [M,K] (K % 32 == 0) -> (e4m3 codes uint8 [M,K], e8m0 scales uint8 [M,K/32])."""
+    import torch
+    M, K = a.shape
+    _check_tensor(a, "a", torch.bfloat16, (M, K))
+    _require_gpu(a)
+    codes = torch.empty((M, K), dtype=torch.uint8, device=a.device)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=a.device)
+    _check(lib().gmxfp8_quantize(_ptr(a), _ptr(codes), _ptr(scales), M, K, _stream(stream)))
+    return codes, scales
 
 
 def grouped_linear(a, sizes, w, scales, fmt: str = "nf4"):

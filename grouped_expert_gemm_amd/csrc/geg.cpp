@@ -135,6 +135,12 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
+  if (op == GEG_OP_MXFP4_W4A8) {   // e4m3 codes [M, K] and their scales [M, K/32]
+    p.a16_off = kHeader;
+    p.a16_bytes = round256((size_t)M * (size_t)K) + round256((size_t)M * (size_t)(K / 32));
+    p.total_bytes = p.a16_off + p.a16_bytes;
+    return GEG_OK;
+  }
   if (op == GEG_OP_MXFP4_DGRAD) {   // bf16 dY feeds the MFMAs as it is
     p.run_tile = M > 0;
     p.total_bytes = kHeader;
@@ -463,6 +469,64 @@ geg_status gmxfp4_grouped_dgrad(const void* dy, const int32_t* sizes, const uint
                       stream);
 }
 
+geg_status gmxfp4_w4a8_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* blocks,
+                                    const uint8_t* scales, void* out, int64_t M, int64_t N, int64_t K,
+                                    int32_t E, void* workspace, size_t workspace_bytes,
+                                    const geg_opts* opts, hipStream_t stream) {
+  geg_status st = check_shape(M, N, K, E, 32);
+  if (st != GEG_OK) return st;
+  // 32-bit buffer offsets within a 256-row tile of activation codes
+  if (K >= (int64_t)1 << 23) return fail(GEG_ERR_BAD_SHAPE, "K must be below 2^23");
+  Plan p;
+  if ((st = make_plan(GEG_OP_MXFP4_W4A8, M, N, K, E, opts, p)) != GEG_OK) return st;
+  if (M == 0) return GEG_OK;
+  if (!a || !sizes || !blocks || !scales || !out) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!workspace) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(a, 16) || !aligned(blocks, 16) || !aligned(out, 4) || !aligned(sizes, 4))
+    return fail(GEG_ERR_MISALIGNED, "a and blocks must be 16-byte aligned, out 4-byte");
+  if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.total_bytes)
+    return fail(GEG_ERR_WORKSPACE, "workspace smaller than geg_workspace_bytes(): need " +
+                                       std::to_string(p.total_bytes));
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{a, "a"}, {sizes, "sizes"}, {blocks, "blocks"},
+                           {scales, "scales"}, {out, "out"}, {workspace, "workspace"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  uint32_t* err = reinterpret_cast<uint32_t*>(wsb);
+  uint8_t* aq = wsb + p.a16_off;
+  uint8_t* as = aq + round256((size_t)M * (size_t)K);
+  const int cus = cu_count();
+  hipError_t e = geg::launch_mxfp8_quantize(reinterpret_cast<const uint16_t*>(a), M, K, aq, as, err, cus, stream);
+  if (e != hipSuccess) return hip_fail(e, "activation quantisation launch");
+  ++g_launches;
+  e = record_event(opts, 0, stream);
+  if (e == hipSuccess)
+    e = geg::launch_w4a8(aq, as, sizes, blocks, scales, reinterpret_cast<uint16_t*>(out), M, N, K, E, err, cus,
+                         stream);
+  if (e == hipSuccess) e = record_event(opts, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "W4A8 kernel launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
+geg_status gmxfp8_quantize(const void* a, uint8_t* codes, uint8_t* scales, int64_t M, int64_t K,
+                           hipStream_t stream) {
+  if (M < 0 || K <= 0 || K % 32) return fail(GEG_ERR_BAD_SHAPE, "need M >= 0, K > 0, K % 32 == 0");
+  if (M == 0) return GEG_OK;
+  if (!a || !codes || !scales) return fail(GEG_ERR_NULL_POINTER, "a, codes and scales are required");
+  if (!aligned(a, 16) || !aligned(codes, 16)) return fail(GEG_ERR_MISALIGNED, "a and codes must be 16-byte aligned");
+  geg_status st;
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{a, "a"}, {codes, "codes"}, {scales, "scales"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  hipError_t e = geg::launch_mxfp8_quantize(reinterpret_cast<const uint16_t*>(a), M, K, codes, scales, nullptr,
+                                            cu_count(), stream);
+  if (e != hipSuccess) return hip_fail(e, "activation quantisation launch");
+  ++g_launches;
+  return GEG_OK;
+}
+
 size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0 || E > geg::kMaxExperts) return 0;
   const int64_t nchunks = (T * k + geg::kThreads - 1) / geg::kThreads;
@@ -530,7 +594,7 @@ geg_status geg_route_combine(const void* y, const int32_t* row_of, const float* 
 
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
                            const geg_opts* opts) {
-  if (op < 0 || op > 5 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  if (op < 0 || op > 6 || M < 0 || N <= 0 || K <= 0 || E <= 0) return 0;
   if (op == GEG_OP_NF4_BLOCK || op == GEG_OP_MXFP4_BLOCK) {
     size_t act_off = 0, total = 0;
     if (block_layout(op == GEG_OP_NF4_BLOCK ? geg::NF4 : geg::MXFP4, M, N, K, E, opts, act_off, total) != GEG_OK)

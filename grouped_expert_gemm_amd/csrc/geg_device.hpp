@@ -34,6 +34,7 @@ constexpr uint32_t kErrNegativeSize = 0x1u;
 constexpr uint32_t kErrSizesExceedM = 0x2u;
 constexpr uint32_t kErrFp16Range = 0x4u;
 constexpr uint32_t kErrBadExpertId = 0x8u;
+constexpr uint32_t kErrNonFinite = 0x10u;   // W4A8: an activation is inf or NaN
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value {hi, lo}.

@@ -1,0 +1,370 @@
+// W4A8 variant of the MXFP4 grouped GEMM: the released e2m1 weight bytes and
+// their e8m0 scales feed gfx950's block-scaled matrix instruction
+// (v_mfma_scale_f32_16x16x128_f8f6f4) as they are, against activations
+// quantised to MXFP8 (e4m3 elements, one e8m0 scale per 32 k). Prior art: "bw24
+// releases, v0.9.0", "Changes since v0.8.0" (a W4A8-FP8 prefill tile: e4m3
+// activations times native e2m1 weights in one block-scaled MMA).
+//
+// Activation quantisation follows the OCP MX v1.0 conversion: per 32-block,
+// X = floor(log2 amax) - 8 + 127 clamped to [0, 254] (0 for an all-zero block),
+// elements round to nearest e4m3 (ties to even) after the exact division by
+// 2^(X - 127), saturating at 448, the sign kept.
+//
+// Operand layout of the instruction (measured with in-bounds probes on gfx950):
+// lane l works on row (A) or column (B) l % 16 and lane group g = l / 16.
+//   A (fp8, 8 VGPRs): bytes 0-15 hold k = 16 g + 0..15, bytes 16-31 hold
+//     k = 64 + 16 g + 0..15 of the 128-wide step.
+//   B (fp4, 4 VGPRs): 32 nibbles, k = 32 g + 0..31, the even k in the low nibble:
+//     exactly 16 consecutive bytes of a released MXFP4 row.
+//   Scales: lane 16 b + i carries the e8m0 byte of row / column i for k-block b
+//     (k = 32 b .. 32 b + 31), in byte 0 of its scale register.
+// So every operand loads straight from row-major storage: two 16-byte loads of
+// activation codes, one of weight bytes and one byte of each scale per lane and
+// 16x16 block. The instruction's dot product keeps about 12 bits below its
+// largest product (measured: error up to 3e-4 of max |a w| per instruction,
+// unbiased); its results then accumulate in fp32.
+#include <algorithm>
+
+#include "geg_device.hpp"
+#include "geg_launch.hpp"
+
+namespace geg {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int QBM = 256;   // rows per workgroup tile (4 wavefront rows of 64)
+constexpr int QBN = 128;   // columns per workgroup tile (2 wavefront columns of 64)
+constexpr int QBK = 128;   // k per instruction step
+// Offsets stay below 2^31; setting bit 31 moves an access past every buffer
+// record (it then reads 0). Arithmetic rather than a select, which the compiler
+// would turn into branches around the load.
+__device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)!ok << 31); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t qrsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// fp32 t (|t| < 512, the block's scale already divided out) -> e4m3 byte:
+// round to nearest, ties to even, saturating at 448; the sign bit is kept.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
+  const uint32_t s = (__float_as_uint(t) >> 24) & 0x80u;
+  const float a = fabsf(t);
+  uint32_t c;
+  if (a >= 448.f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {                       // below 2^-6: the 2^-9 grid
+    c = (uint32_t)__builtin_rintf(a * 512.f);       // 0..8 (8 is the smallest normal)
+  } else {
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;    // floor(log2 a)
+    const uint32_t r = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));   // 8..16
+    c = ((uint32_t)(e + 7) << 3) + (r - 8u);        // r = 16 carries into the exponent
+  }
+  return c | s;
+}
+
+// One thread per 32-element block of a row-major bf16 [M, K] (K % 32 == 0).
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const uint16_t* __restrict__ a, int64_t nblocks,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales, uint32_t* err) {
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * kThreads) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a + b * 32);
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = src[i];
+    // largest magnitude: bf16 magnitudes order as their low 15 bits
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = max(mx, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
+    if (mx >= 0x7F80u && err) atomicOr(err, kErrNonFinite);
+    // floor(log2 amax) = field - 127 for a normal amax; zero and subnormal blocks
+    // land below the clamp, as do their elements on the 2^-9 grid
+    const uint32_t field = mx >> 7;
+    const int X = field == 0 ? 0 : min(max((int)field - 8, 0), 254);
+    const int sh = 127 - X;
+    u32x4 out[2];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int el = 4 * w + h;   // element of the block
+        const uint32_t bits = (v[el >> 3][(el >> 1) & 3] >> (16 * (el & 1))) & 0xFFFFu;
+        const float t = __builtin_ldexpf(__uint_as_float(bits << 16), sh);
+        word |= e4m3_rne_sat(t) << (8 * h);
+      }
+      out[w >> 2][w & 3] = word;
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + b * 32);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    scales[b] = (uint8_t)X;
+  }
+}
+
+struct W4A8Args {
+  const uint8_t* aq;      // e4m3 activation codes [M, K]
+  const uint8_t* as;      // their e8m0 scales [M, K/32]
+  const int32_t* sizes;   // [E]
+  const uint8_t* wq;      // e2m1 weight bytes [E, N, K/2]
+  const uint8_t* ws;      // e8m0 weight scales [E, N, K/32]
+  uint16_t* out;          // bf16 [M, N]
+  int64_t M, N, K;
+  int32_t E;
+  uint32_t* err;
+};
+
+constexpr int QThreads = 512;                 // 8 wavefronts: 4 (rows) x 2 (columns)
+constexpr int kAStage = QBM * QBK;            // activation bytes per stage (256 rows x 128)
+constexpr int kBStage = QBN * (QBK / 2);      // weight bytes per stage (128 columns x 64)
+
+// LDS stage layout. Activation row r holds 8 chunks of 16 bytes, chunk c stored
+// at c ^ (r % 8); weight column n holds 4 chunks, chunk c stored at
+// c ^ ((n / 4) % 4). With those, the fragment reads (16 rows or columns at one
+// chunk each, serviced 8 lanes at a time over the 64 banks) touch 8 distinct
+// 16-byte bank groups, and the row-wise stores stay conflict-free too.
+__device__ __forceinline__ uint32_t a_lds(int r, int c) { return (uint32_t)(r * QBK + ((c ^ (r & 7)) << 4)); }
+__device__ __forceinline__ uint32_t b_lds(int n, int c) {
+  return (uint32_t)(n * (QBK / 2) + ((c ^ ((n >> 2) & 3)) << 4));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most N of this wavefront's loads (those into LDS included) are
+// still in flight; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);   // expcnt, lgkmcnt: no wait
+}
+
+// End of a pipelined step: this wavefront's LDS reads are done and at most N of
+// its loads are in flight, then the workgroup meets. (__syncthreads would also
+// wait for every load in flight: its fence orders global memory too.) The
+// memory clobber keeps the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void step_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0070);   // lgkmcnt(0), vmcnt(N)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Output tiles of 256x128 per workgroup (one workgroup per CU), persistent over
+// an XCD-aware order. Each 128-wide k step is staged through LDS by loads that
+// write LDS directly: 16 bytes per lane at consecutive slots from a
+// wavefront-uniform base, each lane fetching the chunk that belongs in its slot
+// under the swizzle. Three stage buffers, two steps of loads in flight while a
+// step computes, one barrier per step. The buffers are distinct LDS objects
+// and each step names its own at compile time (the step loop is unrolled by 3):
+// the compiler then knows a step's LDS reads do not touch the buffers that
+// loads are still filling, and adds no wait for those loads.
+// Wavefront (wm, wn) computes rows 64 wm .. +63 and columns 64 wn .. +63: 4 x 4
+// blocks of the 16x16x128 instruction per step. Scale bytes go straight from
+// memory to the lanes that use them.
+__global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
+  __shared__ Plan plan;
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kAStage + kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kAStage + kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kAStage + kBStage];
+  const int64_t K = g.K, N = g.N, KS = K >> 5;
+  const int n_tiles = (int)((N + QBN - 1) / QBN);
+  const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
+    return ((s + QBM - 1) / QBM) * n_tiles;
+  });
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int nst = (int)((K + QBK - 1) / QBK);
+  const int G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  // Stage copy: wavefront w fills activation rows 8 (w + 8 i) .. +7 (i < 4) and
+  // weight columns 16 w .. +15, 1 KB per load instruction; lane l
+  // lands in slot l % 8 of row l / 8 (activations) or slot l % 4 of column l / 4
+  // (weights) and fetches the chunk the swizzle puts there.
+  const int cp_ar = 8 * wave + (lane >> 3), cp_ac = (lane & 7) ^ (cp_ar & 7);   // row, chunk (i = 0)
+  const int cp_bn = 16 * wave + (lane >> 2), cp_bc = (lane & 3) ^ ((cp_bn >> 2) & 3);
+  // Fragment reads: rows 16 apart share their swizzle, and so do columns 16 apart,
+  // so fragment i of the wavefront's rows is read at rd_alo / rd_ahi + 2048 i,
+  // fragment j of its columns at rd_b + 1024 j.
+  const uint32_t rd_alo = a_lds(64 * wm + r16, grp), rd_ahi = a_lds(64 * wm + r16, 4 + grp);
+  const uint32_t rd_b = kAStage + b_lds(64 * wn + r16, grp);
+  // scale byte offsets of the lane's first row / column (16 i rows further: + 16 i KS)
+  const uint32_t sa0 = (uint32_t)((64 * wm + r16) * KS), sb0 = (uint32_t)((64 * wn + r16) * KS);
+
+  for (int32_t base = 0; base < total; base += G) {
+    const int32_t u = base + slot;
+    if (u >= total) break;
+    const int e = find_expert(plan, g.E, u);
+    const int32_t lu = u - plan.upre[e];
+    const int64_t row0 = plan.off[e] + (int64_t)(lu / n_tiles) * QBM;
+    const int rows = (int)min<int64_t>(QBM, plan.off[e + 1] - row0);
+    const int64_t n0 = (int64_t)(lu % n_tiles) * QBN;
+    const int ncols = (int)min<int64_t>(QBN, N - n0);
+    // rows past the expert's last row and columns past N read as zeros
+    const __amdgpu_buffer_rsrc_t RA = qrsrc(g.aq + row0 * K, (int64_t)rows * K);
+    const __amdgpu_buffer_rsrc_t RAS = qrsrc(g.as + row0 * KS, (int64_t)rows * KS);
+    const __amdgpu_buffer_rsrc_t RW = qrsrc(g.wq + ((int64_t)e * N + n0) * (K >> 1), (int64_t)ncols * (K >> 1));
+    const __amdgpu_buffer_rsrc_t RWS = qrsrc(g.ws + ((int64_t)e * N + n0) * KS, (int64_t)ncols * KS);
+
+    // Stage st into LDS buffer L. Chunks that start at or past K (the last step
+    // when K % 128 != 0, and every chunk of the steps past the last) read zeros,
+    // and so do their scale bytes (a scale byte of the next row must not reach
+    // the instruction: 0xFF would be NaN). Rows past the tile's rows and columns
+    // past N read zeros through the buffer bounds. Five loads per wavefront.
+    auto stage = [&](int st, uint8_t* L) {
+      const int64_t k0 = (int64_t)st * QBK;
+      const bool a_ok = k0 + 16 * cp_ac < K, b_ok = k0 + 32 * cp_bc < K;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)((cp_ar + 64 * i) * K + k0 + 16 * cp_ac);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(RA, (lds_ptr_t)(L + (8 * wave + 64 * i) * QBK), 16,
+                                                 oob_unless(a_ok, off), 0, 0, 0);
+      }
+      const uint32_t boff = (uint32_t)(cp_bn * (K >> 1) + (k0 >> 1) + 16 * cp_bc);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(RW, (lds_ptr_t)(L + kAStage + 16 * wave * (QBK / 2)), 16,
+                                               oob_unless(b_ok, boff), 0, 0, 0);
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // scale bytes of step st (row / column block of the lane, k-block grp):
+    // sc[i] for row block i, sc[4 + j] for column block j; 8 loads per wavefront
+    auto scales = [&](uint32_t (&sc)[8], int st) {
+      const int64_t k0 = (int64_t)st * QBK;
+      const bool s_ok = k0 + 32 * grp < K;
+      const uint32_t ks = (uint32_t)(k0 >> 5) + grp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sc[i] = __builtin_amdgcn_raw_buffer_load_b8(RAS, oob_unless(s_ok, sa0 + (uint32_t)(16 * i * KS) + ks), 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sc[4 + j] = __builtin_amdgcn_raw_buffer_load_b8(RWS, oob_unless(s_ok, sb0 + (uint32_t)(16 * j * KS) + ks), 0, 0);
+    };
+
+    // Step st (its stage in buffer `cur` and its scale bytes in `sc`, both loaded
+    // earlier): (1) load the scale bytes of step st + 1 into `sc1`, then start
+    // stage st + 2 into `nxt2` (the buffer step st - 1 read; every wavefront left
+    // it at the barrier that ended that step), (2) read the step's fragments,
+    // (3) run its 16 instructions from registers, (4) wait until stage st + 1 has
+    // landed (the 13 loads of (1) may still be in flight) and meet at the barrier.
+    // Loads complete in issue order, so the scale bytes go first: waiting for
+    // them in the next step does not wait for the stage issued after them. The
+    // three scale sets rotate with the buffers (no register copies, which would
+    // wait for the newest loads).
+    typedef uint32_t Sc[8];   // 4 row-block scales, then 4 column-block scales
+    auto step = [&](int st, const uint8_t* cur, uint8_t* nxt2, const Sc& sc, Sc& sc1) {
+      scales(sc1, st + 1);
+      stage(st + 2, nxt2);
+      v8i bf[4], af[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cur + rd_b + 1024 * j);
+        bf[j] = v8i{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + rd_alo + 2048 * i);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + rd_ahi + 2048 * i);
+        af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 0, 4, 0, (int)sc[i], 0,
+                                                                        (int)sc[4 + j]);
+      __builtin_amdgcn_sched_barrier(0);   // the instructions above overlap the loads
+      step_barrier<13>();
+    };
+
+    // prologue: scale bytes of step 0, stages 0 and 1 in flight; wait for the
+    // first two (the 5 loads of stage 1 may still be in flight)
+    Sc sc0, sc1, sc2;
+    scales(sc0, 0);
+    stage(0, lds0);
+    stage(1, lds1);
+    wait_vm<5>();
+    __syncthreads();
+    // whole groups of three steps in one branch-free block (a step's
+    // instructions must stay ahead of its wait and barrier; across a branch the
+    // compiler would sink them past), then the one or two steps left
+    int st = 0;
+    for (; st + 3 <= nst; st += 3) {
+      step(st, lds0, lds2, sc0, sc1);
+      step(st + 1, lds1, lds0, sc1, sc2);
+      step(st + 2, lds2, lds1, sc2, sc0);
+    }
+    if (st < nst) step(st, lds0, lds2, sc0, sc1);
+    if (st + 1 < nst) step(st + 1, lds1, lds0, sc1, sc2);
+    wait_vm<0>();         // loads past the last step (zeros) land before the buffers are reused
+    __syncthreads();
+
+    // Epilogue: acc[i][j][q] is row 16 i + 4 grp + q, column 16 j + r16 of the
+    // wavefront's block. Lanes l, l ^ 1 hold neighbouring columns; each trades two
+    // values with the other so that the even lane stores rows q = 0, 1 and the odd
+    // lane rows q = 2, 3 as bf16 pairs.
+    const bool odd = lane & 1;
+    const int64_t colp = n0 + 64 * wn + r16 - (odd ? 1 : 0);   // even column of the pair
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = acc[i][j];
+        const float x0 = lane_pair_swap(odd ? v[0] : v[2]);
+        const float x1 = lane_pair_swap(odd ? v[1] : v[3]);
+        const int lr = 64 * wm + 16 * i + 4 * grp + (odd ? 2 : 0);
+        const int64_t c = colp + 16 * j;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float p = odd ? (h ? x1 : x0) : (h ? v[1] : v[0]);
+          const float q = odd ? (h ? v[3] : v[2]) : (h ? x1 : x0);
+          if (lr + h < rows && c < N) {
+            uint16_t* dst = g.out + (row0 + lr + h) * N + c;
+            if ((N & 1) == 0 && c + 1 < N) {
+              *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(p, q);
+            } else {
+              dst[0] = to_bf16(p);
+              if (c + 1 < N) dst[1] = to_bf16(q);
+            }
+          }
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mxfp8_quantize(const uint16_t* a, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                                 uint32_t* err, int cus, hipStream_t s) {
+  const int64_t nblocks = M * (K >> 5);
+  if (nblocks <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((nblocks + kThreads - 1) / kThreads, (int64_t)cus * 16);
+  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a, nblocks, codes, scales,
+                     err);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8(const uint8_t* aq, const uint8_t* as, const int32_t* sizes, const uint8_t* wq,
+                       const uint8_t* ws, uint16_t* out, int64_t M, int64_t N, int64_t K, int32_t E, uint32_t* err,
+                       int cus, hipStream_t s) {
+  W4A8Args g{aq, as, sizes, wq, ws, out, M, N, K, E, err};
+  const int64_t n_tiles = (N + QBN - 1) / QBN;
+  const int64_t bound = ((M + QBM - 1) / QBM + std::min<int64_t>(E, M)) * n_tiles;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(bound, (int64_t)cus));
+  hipLaunchKernelGGL(w4a8_kernel, dim3((unsigned)grid), dim3(QThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace geg
