@@ -137,7 +137,8 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
   }
   if (op == GEG_OP_MXFP4_W4A8) {   // e4m3 codes [M, K] and their scales [M, K/32]
     p.a16_off = kHeader;
-    p.a16_bytes = round256((size_t)M * (size_t)K) + round256((size_t)M * (size_t)(K / 32));
+    // scales step-major, 4 per row and 128-wide k step
+    p.a16_bytes = round256((size_t)M * (size_t)K) + round256((size_t)M * (size_t)((K / 32 + 3) & ~3));
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
@@ -497,7 +498,7 @@ geg_status gmxfp4_w4a8_grouped_gemm(const void* a, const int32_t* sizes, const u
   uint8_t* aq = wsb + p.a16_off;
   uint8_t* as = aq + round256((size_t)M * (size_t)K);
   const int cus = cu_count();
-  hipError_t e = geg::launch_mxfp8_quantize(reinterpret_cast<const uint16_t*>(a), M, K, aq, as, err, cus, stream);
+  hipError_t e = geg::launch_mxfp8_quantize(reinterpret_cast<const uint16_t*>(a), M, K, aq, as, err, 1, cus, stream);
   if (e != hipSuccess) return hip_fail(e, "activation quantisation launch");
   ++g_launches;
   e = record_event(opts, 0, stream);
@@ -520,7 +521,7 @@ geg_status gmxfp8_quantize(const void* a, uint8_t* codes, uint8_t* scales, int64
   if ((st = check_device()) != GEG_OK) return st;
   for (auto [ptr, name] : {std::pair<const void*, const char*>{a, "a"}, {codes, "codes"}, {scales, "scales"}})
     if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
-  hipError_t e = geg::launch_mxfp8_quantize(reinterpret_cast<const uint16_t*>(a), M, K, codes, scales, nullptr,
+  hipError_t e = geg::launch_mxfp8_quantize(reinterpret_cast<const uint16_t*>(a), M, K, codes, scales, nullptr, 0,
                                             cu_count(), stream);
   if (e != hipSuccess) return hip_fail(e, "activation quantisation launch");
   ++g_launches;

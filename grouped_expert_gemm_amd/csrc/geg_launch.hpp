@@ -76,10 +76,12 @@ hipError_t launch_route_sort(const int32_t* ids, int64_t n, int32_t E, int32_t* 
                              int32_t* row_of, int32_t* src_of, uint32_t* err, hipStream_t s);
 hipError_t launch_route_gather(const uint16_t* x, int64_t H, int32_t k, const int32_t* src_of, int64_t n,
                                uint16_t* xs, int cus, hipStream_t s);
-// W4A8: bf16 [M, K] -> e4m3 codes [M, K] + e8m0 scales [M, K/32] (err may be
-// NULL), then the grouped GEMM of those with MXFP4 weights.
+// W4A8: bf16 [M, K] -> e4m3 codes [M, K] + e8m0 scales (err may be NULL), then
+// the grouped GEMM of those with MXFP4 weights. Scales row-major [M, K/32], or
+// with step_major as the W4A8 kernel reads them: [ceil(K/128)][M][4], blocks past
+// K / 32 zero.
 hipError_t launch_mxfp8_quantize(const uint16_t* a, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
-                                 uint32_t* err, int cus, hipStream_t s);
+                                 uint32_t* err, int step_major, int cus, hipStream_t s);
 hipError_t launch_w4a8(const uint8_t* aq, const uint8_t* as, const int32_t* sizes, const uint8_t* wq,
                        const uint8_t* ws, uint16_t* out, int64_t M, int64_t N, int64_t K, int32_t E, uint32_t* err,
                        int cus, hipStream_t s);

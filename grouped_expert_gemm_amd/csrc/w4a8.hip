@@ -66,11 +66,24 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
 }
 
 // One thread per 32-element block of a row-major bf16 [M, K] (K % 32 == 0).
-__global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const uint16_t* __restrict__ a, int64_t nblocks,
-                                                                  uint8_t* __restrict__ codes,
+// Scales go to [M, K/32] (row-major), or with STEP_MAJOR to the layout the W4A8
+// kernel stages: for each 128-wide k step st and row m, the 4 bytes of the
+// step's blocks at (st * M + m) * 4; blocks past K / 32 in the last step get 0.
+template <bool STEP_MAJOR>
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const uint16_t* __restrict__ a, int64_t M,
+                                                                  int64_t KS, uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales, uint32_t* err) {
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
-       b += (int64_t)gridDim.x * kThreads) {
+  const int64_t KS4 = STEP_MAJOR ? (KS + 3) & ~(int64_t)3 : KS;   // blocks per row, padded to whole steps
+  const int64_t nblocks = M * KS4;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < nblocks;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t m = idx / KS4, kb = idx - m * KS4;
+    const int64_t sidx = STEP_MAJOR ? ((kb >> 2) * M + m) * 4 + (kb & 3) : idx;
+    if (kb >= KS) {            // padding block of the last step
+      scales[sidx] = 0;
+      continue;
+    }
+    const int64_t b = m * KS + kb;
     const u32x4* src = reinterpret_cast<const u32x4*>(a + b * 32);
     u32x4 v[4];
 #pragma unroll
@@ -103,13 +116,13 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const uint16_t
     u32x4* dst = reinterpret_cast<u32x4*>(codes + b * 32);
     dst[0] = out[0];
     dst[1] = out[1];
-    scales[b] = (uint8_t)X;
+    scales[sidx] = (uint8_t)X;
   }
 }
 
 struct W4A8Args {
   const uint8_t* aq;      // e4m3 activation codes [M, K]
-  const uint8_t* as;      // their e8m0 scales [M, K/32]
+  const uint8_t* as;      // their e8m0 scales, step-major: [ceil(K/128)][M][4]
   const int32_t* sizes;   // [E]
   const uint8_t* wq;      // e2m1 weight bytes [E, N, K/2]
   const uint8_t* ws;      // e8m0 weight scales [E, N, K/32]
@@ -122,6 +135,9 @@ struct W4A8Args {
 constexpr int QThreads = 512;                 // 8 wavefronts: 4 (rows) x 2 (columns)
 constexpr int kAStage = QBM * QBK;            // activation bytes per stage (256 rows x 128)
 constexpr int kBStage = QBN * (QBK / 2);      // weight bytes per stage (128 columns x 64)
+constexpr int kSAOff = kAStage + kBStage;     // activation scales of the stage: [256 rows][4 blocks]
+constexpr int kSBOff = kSAOff + QBM * 4;      // weight scales of the stage: [128 columns][4 blocks]
+constexpr int kStage = kSBOff + QBN * 4;
 
 // LDS stage layout. Activation row r holds 8 chunks of 16 bytes, chunk c stored
 // at c ^ (r % 8); weight column n holds 4 chunks, chunk c stored at
@@ -168,10 +184,10 @@ __device__ __forceinline__ void step_barrier() {
 // memory to the lanes that use them.
 __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
   __shared__ Plan plan;
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kAStage + kBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[kAStage + kBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[kAStage + kBStage];
-  const int64_t K = g.K, N = g.N, KS = K >> 5;
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
+  const int64_t K = g.K, N = g.N, KS = K >> 5, M = g.M;
   const int n_tiles = (int)((N + QBN - 1) / QBN);
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
     return ((s + QBM - 1) / QBM) * n_tiles;
@@ -196,8 +212,12 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
   // fragment j of its columns at rd_b + 1024 j.
   const uint32_t rd_alo = a_lds(64 * wm + r16, grp), rd_ahi = a_lds(64 * wm + r16, 4 + grp);
   const uint32_t rd_b = kAStage + b_lds(64 * wn + r16, grp);
-  // scale byte offsets of the lane's first row / column (16 i rows further: + 16 i KS)
-  const uint32_t sa0 = (uint32_t)((64 * wm + r16) * KS), sb0 = (uint32_t)((64 * wn + r16) * KS);
+  // scale bytes in LDS: row 64 wm + 16 i + r16, block grp at rd_sa + 64 i; column
+  // 64 wn + 16 j + r16 at rd_sb + 64 j
+  const uint32_t rd_sa = kSAOff + (uint32_t)((64 * wm + r16) * 4 + grp);
+  const uint32_t rd_sb = kSBOff + (uint32_t)((64 * wn + r16) * 4 + grp);
+  // weight scale byte this thread stages: column t / 4, block t % 4 of the step
+  const int sb_col = t >> 2, sb_blk = t & 3;
 
   for (int32_t base = 0; base < total; base += G) {
     const int32_t u = base + slot;
@@ -210,15 +230,18 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
     const int ncols = (int)min<int64_t>(QBN, N - n0);
     // rows past the expert's last row and columns past N read as zeros
     const __amdgpu_buffer_rsrc_t RA = qrsrc(g.aq + row0 * K, (int64_t)rows * K);
-    const __amdgpu_buffer_rsrc_t RAS = qrsrc(g.as + row0 * KS, (int64_t)rows * KS);
+    // step-major activation scales: the whole array (rows of the next expert read
+    // real scale bytes, never 0xFF; their activation chunks read zeros)
+    const __amdgpu_buffer_rsrc_t RAS = qrsrc(g.as, (int64_t)nst * M * 4);
     const __amdgpu_buffer_rsrc_t RW = qrsrc(g.wq + ((int64_t)e * N + n0) * (K >> 1), (int64_t)ncols * (K >> 1));
     const __amdgpu_buffer_rsrc_t RWS = qrsrc(g.ws + ((int64_t)e * N + n0) * KS, (int64_t)ncols * KS);
 
-    // Stage st into LDS buffer L. Chunks that start at or past K (the last step
-    // when K % 128 != 0, and every chunk of the steps past the last) read zeros,
-    // and so do their scale bytes (a scale byte of the next row must not reach
-    // the instruction: 0xFF would be NaN). Rows past the tile's rows and columns
-    // past N read zeros through the buffer bounds. Five loads per wavefront.
+    // Stage st into LDS buffer L: activation and weight chunks, and (wavefront 0)
+    // the tile's 256 activation scale dwords of the step, 1 KB. Chunks that start
+    // at or past K (the last step when K % 128 != 0, and every chunk of the steps
+    // past the last) read zeros. Rows past the tile's rows and columns past N
+    // read zeros through the buffer bounds. Five loads per wavefront, six for
+    // wavefront 0.
     auto stage = [&](int st, uint8_t* L) {
       const int64_t k0 = (int64_t)st * QBK;
       const bool a_ok = k0 + 16 * cp_ac < K, b_ok = k0 + 32 * cp_bc < K;
@@ -231,83 +254,94 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
       const uint32_t boff = (uint32_t)(cp_bn * (K >> 1) + (k0 >> 1) + 16 * cp_bc);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(RW, (lds_ptr_t)(L + kAStage + 16 * wave * (QBK / 2)), 16,
                                                oob_unless(b_ok, boff), 0, 0, 0);
+      if (wave == 0) {
+        const uint32_t soff = (uint32_t)(((int64_t)st * M + row0) * 4 + 16 * lane);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(RAS, (lds_ptr_t)(L + kSAOff), 16, oob_unless(st < nst, soff), 0, 0, 0);
+      }
     };
-
+    // weight scale byte of step st for this thread (column sb_col, block sb_blk);
+    // blocks past K read 0 (a scale byte of the next row must not reach the
+    // instruction: 0xFF would be NaN)
+    auto wscale = [&](int st) -> uint32_t {
+      const int64_t kb = (int64_t)st * 4 + sb_blk;
+      return __builtin_amdgcn_raw_buffer_load_b8(RWS, oob_unless(kb < KS, (uint32_t)(sb_col * KS + kb)), 0, 0);
+    };
+    // MFMAs only for the wavefront rows that hold rows of the expert
+    const bool live = 64 * wm < rows;
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // scale bytes of step st (row / column block of the lane, k-block grp):
-    // sc[i] for row block i, sc[4 + j] for column block j; 8 loads per wavefront
-    auto scales = [&](uint32_t (&sc)[8], int st) {
-      const int64_t k0 = (int64_t)st * QBK;
-      const bool s_ok = k0 + 32 * grp < K;
-      const uint32_t ks = (uint32_t)(k0 >> 5) + grp;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sc[i] = __builtin_amdgcn_raw_buffer_load_b8(RAS, oob_unless(s_ok, sa0 + (uint32_t)(16 * i * KS) + ks), 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sc[4 + j] = __builtin_amdgcn_raw_buffer_load_b8(RWS, oob_unless(s_ok, sb0 + (uint32_t)(16 * j * KS) + ks), 0, 0);
-    };
-
-    // Step st (its stage in buffer `cur` and its scale bytes in `sc`, both loaded
-    // earlier): (1) load the scale bytes of step st + 1 into `sc1`, then start
-    // stage st + 2 into `nxt2` (the buffer step st - 1 read; every wavefront left
-    // it at the barrier that ended that step), (2) read the step's fragments,
-    // (3) run its 16 instructions from registers, (4) wait until stage st + 1 has
-    // landed (the 13 loads of (1) may still be in flight) and meet at the barrier.
-    // Loads complete in issue order, so the scale bytes go first: waiting for
-    // them in the next step does not wait for the stage issued after them. The
-    // three scale sets rotate with the buffers (no register copies, which would
-    // wait for the newest loads).
-    typedef uint32_t Sc[8];   // 4 row-block scales, then 4 column-block scales
-    auto step = [&](int st, const uint8_t* cur, uint8_t* nxt2, const Sc& sc, Sc& sc1) {
-      scales(sc1, st + 1);
+    // Step st (stage in buffer `cur`, loaded two steps earlier): (1) load this
+    // thread's weight scale byte of step st + 2 and start stage st + 2 into
+    // `nxt2` (the buffer step st - 1 read; every wavefront left it at the barrier
+    // that ended that step), (2) read the step's fragments and scale bytes,
+    // (3) run its 16 instructions from registers, (4) wait until stage st + 1 and
+    // the scale byte loaded in step st - 1 have landed (the loads of (1) may still
+    // be in flight), store that byte into stage st + 1's buffer `nxt1`, and meet at
+    // the barrier. `ws1` carries the byte of step st + 1 into this step and
+    // returns the one of step st + 2.
+    auto step = [&](int st, const uint8_t* cur, uint8_t* nxt1, uint8_t* nxt2, uint32_t& ws1) {
+      const uint32_t ws2 = wscale(st + 2);
       stage(st + 2, nxt2);
-      v8i bf[4], af[4];
+      if (live) {
+        v8i bf[4], af[4];
+        uint32_t sa[4], sb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(cur + rd_b + 1024 * j);
-        bf[j] = v8i{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(cur + rd_b + 1024 * j);
+          bf[j] = v8i{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          sb[j] = cur[rd_sb + 64 * j];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + rd_alo + 2048 * i);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + rd_ahi + 2048 * i);
+          af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          sa[i] = cur[rd_sa + 64 * i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 0, 4, 0, (int)sa[i],
+                                                                          0, (int)sb[j]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + rd_alo + 2048 * i);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + rd_ahi + 2048 * i);
-        af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 0, 4, 0, (int)sc[i], 0,
-                                                                        (int)sc[4 + j]);
       __builtin_amdgcn_sched_barrier(0);   // the instructions above overlap the loads
-      step_barrier<13>();
+      if (wave == 0)
+        wait_vm<7>();
+      else
+        wait_vm<6>();
+      nxt1[kSBOff + t] = (uint8_t)ws1;
+      ws1 = ws2;
+      step_barrier<7>();   // the byte store is done (lgkmcnt 0); loads: no further wait
     };
 
-    // prologue: scale bytes of step 0, stages 0 and 1 in flight; wait for the
-    // first two (the 5 loads of stage 1 may still be in flight)
-    Sc sc0, sc1, sc2;
-    scales(sc0, 0);
+    // prologue: stages 0 and 1 and the weight scale bytes of steps 0 and 1; wait
+    // for stage 0 and step 0's byte, store it, meet
+    uint32_t ws0 = wscale(0);
     stage(0, lds0);
+    uint32_t ws1 = wscale(1);
     stage(1, lds1);
-    wait_vm<5>();
+    if (wave == 0)
+      wait_vm<7>();
+    else
+      wait_vm<6>();
+    lds0[kSBOff + t] = (uint8_t)ws0;
     __syncthreads();
     // whole groups of three steps in one branch-free block (a step's
     // instructions must stay ahead of its wait and barrier; across a branch the
     // compiler would sink them past), then the one or two steps left
     int st = 0;
     for (; st + 3 <= nst; st += 3) {
-      step(st, lds0, lds2, sc0, sc1);
-      step(st + 1, lds1, lds0, sc1, sc2);
-      step(st + 2, lds2, lds1, sc2, sc0);
+      step(st, lds0, lds1, lds2, ws1);
+      step(st + 1, lds1, lds2, lds0, ws1);
+      step(st + 2, lds2, lds0, lds1, ws1);
     }
-    if (st < nst) step(st, lds0, lds2, sc0, sc1);
-    if (st + 1 < nst) step(st + 1, lds1, lds0, sc1, sc2);
+    if (st < nst) step(st, lds0, lds1, lds2, ws1);
+    if (st + 1 < nst) step(st + 1, lds1, lds2, lds0, ws1);
     wait_vm<0>();         // loads past the last step (zeros) land before the buffers are reused
     __syncthreads();
 
@@ -347,12 +381,17 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
 }  // namespace
 
 hipError_t launch_mxfp8_quantize(const uint16_t* a, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
-                                 uint32_t* err, int cus, hipStream_t s) {
-  const int64_t nblocks = M * (K >> 5);
+                                 uint32_t* err, int step_major, int cus, hipStream_t s) {
+  const int64_t KS = K >> 5;
+  const int64_t nblocks = M * (step_major ? (KS + 3) & ~(int64_t)3 : KS);
   if (nblocks <= 0) return hipSuccess;
   const int64_t grid = std::min<int64_t>((nblocks + kThreads - 1) / kThreads, (int64_t)cus * 16);
-  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a, nblocks, codes, scales,
-                     err);
+  if (step_major)
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, M, KS, codes,
+                       scales, err);
+  else
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, M, KS, codes,
+                       scales, err);
   return hipGetLastError();
 }
 
