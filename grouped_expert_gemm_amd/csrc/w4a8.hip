@@ -345,11 +345,47 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
     wait_vm<0>();         // loads past the last step (zeros) land before the buffers are reused
     __syncthreads();
 
-    // Epilogue: acc[i][j][q] is row 16 i + 4 grp + q, column 16 j + r16 of the
+    // Epilogue. acc[i][j][q] is row 16 i + 4 grp + q, column 16 j + r16 of the
     // wavefront's block. Lanes l, l ^ 1 hold neighbouring columns; each trades two
-    // values with the other so that the even lane stores rows q = 0, 1 and the odd
+    // values with the other so that the even lane holds rows q = 0, 1 and the odd
     // lane rows q = 2, 3 as bf16 pairs.
     const bool odd = lane & 1;
+    if ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0) {
+      // Through LDS (the stage buffers are idle: every load has landed and every
+      // wavefront passed the barrier above): rows 0-127 of the tile in lds0, rows
+      // 128-255 in lds1, 272-byte rows; then 16-byte row pieces, 16 threads per
+      // 256-byte row.
+      constexpr int kEpLd = 2 * QBN + 16;   // bytes per staged row
+      uint8_t* half = wm < 2 ? lds0 : lds1;
+      const int hr0 = 64 * (wm & 1);        // the wavefront's first row in its half
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = acc[i][j];
+          const float x0 = lane_pair_swap(odd ? v[0] : v[2]);
+          const float x1 = lane_pair_swap(odd ? v[1] : v[3]);
+          const int r = hr0 + 16 * i + 4 * grp + (odd ? 2 : 0);
+          const int cb = 2 * (64 * wn + 16 * j + r16 - (odd ? 1 : 0));   // byte of the even column
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float p = odd ? (h ? x1 : x0) : (h ? v[1] : v[0]);
+            const float q = odd ? (h ? v[3] : v[2]) : (h ? x1 : x0);
+            *reinterpret_cast<uint32_t*>(half + (r + h) * kEpLd + cb) = pack_bf16x2(p, q);
+          }
+        }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = t + QThreads * k;   // 16-byte piece: row c / 16, piece c % 16
+        const int r = c >> 4, pc = c & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>((r < 128 ? lds0 : lds1) + (r & 127) * kEpLd + 16 * pc);
+        const int64_t col = n0 + 8 * pc;
+        if (r < rows && col < N) *reinterpret_cast<u32x4*>(g.out + (row0 + r) * N + col) = v;
+      }
+      __syncthreads();   // the stage buffers are reused by the next tile
+      continue;
+    }
     const int64_t colp = n0 + 64 * wn + r16 - (odd ? 1 : 0);   // even column of the pair
 #pragma unroll
     for (int i = 0; i < 4; ++i)
