@@ -65,58 +65,62 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
   return c | s;
 }
 
-// One thread per 32-element block of a row-major bf16 [M, K] (K % 32 == 0).
-// Scales go to [M, K/32] (row-major), or with STEP_MAJOR to the layout the W4A8
-// kernel stages: for each 128-wide k step st and row m, the 4 bytes of the
-// step's blocks at (st * M + m) * 4; blocks past K / 32 in the last step get 0.
+// One thread per 16-byte chunk (8 elements) of a row-major bf16 [M, K]
+// (K % 32 == 0): the four lanes of a 32-block (consecutive lanes, the grid
+// stride being a multiple of 4) share its largest magnitude through two lane
+// exchanges, each converts its 8 elements, and the block's first lane writes
+// the scale byte. Scales go to [M, K/32] (row-major), or with STEP_MAJOR to the
+// layout the W4A8 kernel stages: for each 128-wide k step st and row m, the 4
+// bytes of the step's blocks at (st * M + m) * 4; blocks past K / 32 in the last
+// step get 0.
 template <bool STEP_MAJOR>
 __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const uint16_t* __restrict__ a, int64_t M,
                                                                   int64_t KS, uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales, uint32_t* err) {
-  const int64_t KS4 = STEP_MAJOR ? (KS + 3) & ~(int64_t)3 : KS;   // blocks per row, padded to whole steps
-  const int64_t nblocks = M * KS4;
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < nblocks;
-       idx += (int64_t)gridDim.x * kThreads) {
-    const int64_t m = idx / KS4, kb = idx - m * KS4;
-    const int64_t sidx = STEP_MAJOR ? ((kb >> 2) * M + m) * 4 + (kb & 3) : idx;
-    if (kb >= KS) {            // padding block of the last step
-      scales[sidx] = 0;
-      continue;
-    }
-    const int64_t b = m * KS + kb;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a + b * 32);
-    u32x4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = src[i];
+  const int64_t nchunks = M * KS * 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx - (threadIdx.x & 3) < nchunks;
+       idx += stride) {
+    // every lane of a 4-lane group enters together (nchunks is a multiple of 4)
+    const u32x4 v = reinterpret_cast<const u32x4*>(a)[idx];
     // largest magnitude: bf16 magnitudes order as their low 15 bits
     uint32_t mx = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = max(mx, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
-    if (mx >= 0x7F80u && err) atomicOr(err, kErrNonFinite);
+    for (int j = 0; j < 4; ++j) mx = max(mx, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
+    if (mx >= 0x7F80u && err && (idx & 3) == 0) atomicOr(err, kErrNonFinite);
     // floor(log2 amax) = field - 127 for a normal amax; zero and subnormal blocks
     // land below the clamp, as do their elements on the 2^-9 grid
     const uint32_t field = mx >> 7;
     const int X = field == 0 ? 0 : min(max((int)field - 8, 0), 254);
     const int sh = 127 - X;
-    u32x4 out[2];
+    u32x2 out;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int w = 0; w < 2; ++w) {
       uint32_t word = 0;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const int el = 4 * w + h;   // element of the block
-        const uint32_t bits = (v[el >> 3][(el >> 1) & 3] >> (16 * (el & 1))) & 0xFFFFu;
+        const int el = 4 * w + h;   // element of the chunk
+        const uint32_t bits = (v[el >> 1] >> (16 * (el & 1))) & 0xFFFFu;
         const float t = __builtin_ldexpf(__uint_as_float(bits << 16), sh);
         word |= e4m3_rne_sat(t) << (8 * h);
       }
-      out[w >> 2][w & 3] = word;
+      out[w] = word;
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(codes + b * 32);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    scales[sidx] = (uint8_t)X;
+    reinterpret_cast<u32x2*>(codes)[idx] = out;
+    if ((idx & 3) == 0) {
+      const int64_t b = idx >> 2, m = b / KS, kb = b - m * KS;
+      scales[STEP_MAJOR ? ((kb >> 2) * M + m) * 4 + (kb & 3) : b] = (uint8_t)X;
+    }
+  }
+  if constexpr (STEP_MAJOR) {
+    // zero the scale bytes of the padding blocks of the last step
+    const int64_t KS4 = (KS + 3) & ~(int64_t)3, pad = KS4 - KS;
+    for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < M * pad; idx += stride) {
+      const int64_t m = idx / pad, kb = KS + idx - m * pad;
+      scales[((kb >> 2) * M + m) * 4 + (kb & 3)] = 0;
+    }
   }
 }
 
@@ -419,9 +423,9 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
 hipError_t launch_mxfp8_quantize(const uint16_t* a, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                                  uint32_t* err, int step_major, int cus, hipStream_t s) {
   const int64_t KS = K >> 5;
-  const int64_t nblocks = M * (step_major ? (KS + 3) & ~(int64_t)3 : KS);
-  if (nblocks <= 0) return hipSuccess;
-  const int64_t grid = std::min<int64_t>((nblocks + kThreads - 1) / kThreads, (int64_t)cus * 16);
+  const int64_t nchunks = M * KS * 4;
+  if (nchunks <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((nchunks + kThreads - 1) / kThreads, (int64_t)cus * 16);
   if (step_major)
     hipLaunchKernelGGL(mxfp8_quantize_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, M, KS, codes,
                        scales, err);
