@@ -29,6 +29,9 @@ section):
 * The capability index's `entrypoints` (`router_epilogue`, `combine_rows`) and
   releases v0.2.6 "The patch point": the routing sort in front of the grouped
   GEMM and the top-k combine after it (oracle.route).
+* "grouped-nf4-gemm releases", v0.2.4 section: the trainable low-rank delta
+  B(Ax) composed with the frozen 4-bit projection at the pre-activation point
+  (oracle.lora).
 * "bw24 releases, v0.9.0", "Changes since v0.8.0": the W4A8 variant, e4m3
   activations times native e2m1 weights in one block-scaled matrix instruction
   (oracle.w4a8, with its readings of the activation scaling stated there).
@@ -50,6 +53,7 @@ from .grouped import (offsets, grouped_ref, loop_ref, dgrad_ref,
 from .block import (silu, swiglu_ref, bf16_rne_from_f64, expert_block_ref,
                     sampled_block_ref, brute_force_block)
 from .route import route_sort_ref, gather_ref, combine_ref, brute_force_route
+from .lora import lora_delta_ref, lora_forward_ref, lora_backward_ref, brute_force_lora
 from .w4a8 import (E4M3_TABLE, e4m3_value, e4m3_round, mxfp8_scale_bytes, quantize_mxfp8,
                    dequant_mxfp8, w4a8_grouped_ref, sampled_w4a8_ref, brute_force_w4a8)
 
@@ -80,6 +84,9 @@ PARITY = {
                       "[256, 512), half-step error bound",
     "w4a8_grouped_ref": "pinned: pure-Python brute force (exhaustive nearest e4m3 "
                         "search, math.fsum), closeness to the bf16 product",
+    "lora_forward_ref / lora_backward_ref": "pinned: torch fp64 autograd of the same "
+                        "forward (independent derivatives), pure-Python brute force, "
+                        "s = 0 reduction, linearity in s",
 }
 
 __all__ = [n for n in dir() if not n.startswith("_")]
