@@ -71,7 +71,7 @@ BLOCK_WORKLOADS = {
     "qwen3_block": ("qwen3_gate_up_t4096", "qwen3_down_t4096", "qwen3_gate_up_t1", "qwen3_down_t1"),
     "gptoss_block": ("gptoss_gate_up_t2048", "gptoss_down_t2048", "gptoss_gate_up_t1", "gptoss_down_t1"),
 }
-KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip", "route.hip", "w4a8.hip",
+KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip", "route.hip", "w4a8.hip", "lora.hip",
                   "geg.cpp"]
 
 

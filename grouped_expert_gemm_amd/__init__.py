@@ -22,6 +22,8 @@ __all__ = [
     "grouped_linear", "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
     "gmxfp4_w4a8_grouped_gemm", "gmxfp8_quantize", "GEG_OP_MXFP4_W4A8", "DEVERR_NON_FINITE",
+    "gnf4_grouped_gemm_lora", "gmxfp4_grouped_gemm_lora", "gnf4_grouped_dgrad_lora",
+    "gmxfp4_grouped_dgrad_lora", "grouped_linear_lora",
     "geg_version", "geg_launch_count", "GEG_OP_NF4_FWD", "GEG_OP_MXFP4_FWD", "GEG_OP_NF4_DGRAD",
     "GEG_OP_NF4_BLOCK", "GEG_OP_MXFP4_BLOCK", "GEG_OP_MXFP4_DGRAD", "DEVERR_NEGATIVE_SIZE", "DEVERR_SIZES_EXCEED_M", "DEVERR_FP16_RANGE",
     "DEVERR_BAD_EXPERT_ID",
@@ -80,6 +82,18 @@ def lib() -> ctypes.CDLL:
                 f = getattr(L, name)
                 f.argtypes, f.restype = gemm_args, ctypes.c_int
             L.gmxfp8_quantize.argtypes, L.gmxfp8_quantize.restype = [_P, _P, _P, _I64, _I64, _P], ctypes.c_int
+            L.geg_lora_workspace_bytes.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32]
+            L.geg_lora_workspace_bytes.restype = _SZ
+            for name in ("gnf4_grouped_gemm_lora", "gmxfp4_grouped_gemm_lora"):
+                f = getattr(L, name)
+                f.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I64, _I64, _I64, _I32, _I32,
+                              _P, _SZ, _P, _P]
+                f.restype = ctypes.c_int
+            for name in ("gnf4_grouped_dgrad_lora", "gmxfp4_grouped_dgrad_lora"):
+                f = getattr(L, name)
+                f.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _I64, _I32,
+                              _I32, _P, _SZ, _P, _P]
+                f.restype = ctypes.c_int
             L.geg_route_sort.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
             L.geg_route_sort.restype = ctypes.c_int
             L.geg_route_workspace_bytes.argtypes = [_I64, _I32, _I32]
@@ -344,6 +358,104 @@ def gmxfp8_quantize(a, stream=None):
     return codes, scales
 
 
+def _check_lora(x, sizes, lora_a, lora_b):
+    import torch
+    M, K = x.shape
+    E, r = lora_a.shape[0], lora_a.shape[1]
+    N = lora_b.shape[1]
+    _check_tensor(x, "x", torch.bfloat16, (M, K))
+    _check_tensor(sizes, "sizes", torch.int32, (E,))
+    _check_tensor(lora_a, "lora_a", torch.float32, (E, r, K))
+    _check_tensor(lora_b, "lora_b", torch.float32, (E, N, r))
+    return M, N, K, E, r
+
+
+def _gemm_lora(fmt, a, sizes, w, scales, lora_a, lora_b, scale, out, u, workspace, opts, stream):
+    import torch
+    M, N, K, E, r = _check_lora(a, sizes, lora_a, lora_b)
+    _check_packed(fmt == "nf4", w, scales, E, N, K, "weights", "scales")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if u is None:
+        u = torch.empty((M, r), dtype=torch.float32, device=a.device)
+    _check_tensor(out, "out", torch.bfloat16, (M, N))
+    _check_tensor(u, "u", torch.float32, (M, r))
+    _require_gpu(a, sizes, w, scales, lora_a, lora_b, out, u)
+    op = GEG_OP_NF4_FWD if fmt == "nf4" else GEG_OP_MXFP4_FWD
+    ws = _workspace(workspace, lib().geg_lora_workspace_bytes(op, M, N, K, E, r), a.device, stream)
+    fn = getattr(lib(), "gnf4_grouped_gemm_lora" if fmt == "nf4" else "gmxfp4_grouped_gemm_lora")
+    _check(fn(_ptr(a), _ptr(sizes), _ptr(w), _ptr(scales), _ptr(lora_a), _ptr(lora_b), float(scale), _ptr(out),
+              _ptr(u), M, N, K, E, r, _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None, _stream(stream)))
+    return out, u
+
+
+def gnf4_grouped_gemm_lora(a, sizes, w, absmax, lora_a, lora_b, scale: float, out=None, u=None,
+                           workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+    """out = a_e W_e^T + scale (a_e A_e^T) B_e^T per expert, the adapter delta added
+    to the fp32 accumulators before the bf16 rounding; lora_a fp32 [E, r, K],
+    lora_b fp32 [E, N, r]. Returns (out bf16 [M, N], u = a A_e^T fp32 [M, r])."""
+    return _gemm_lora("nf4", a, sizes, w, absmax, lora_a, lora_b, scale, out, u, workspace, opts, stream)
+
+
+def gmxfp4_grouped_gemm_lora(a, sizes, blocks, scales, lora_a, lora_b, scale: float, out=None, u=None,
+                             workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+    """The same on MXFP4 weights (blocks uint8 [E, N, K/2], scales uint8 [E, N, K/32])."""
+    if blocks.dim() == 4:
+        blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
+    return _gemm_lora("mxfp4", a, sizes, blocks, scales, lora_a, lora_b, scale, out, u, workspace, opts, stream)
+
+
+def _dgrad_lora(fmt, dy, sizes, w, scales, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b, workspace, opts,
+                stream):
+    import torch
+    M, N, K, E, r = _check_lora(x, sizes, lora_a, lora_b)
+    _check_packed(fmt == "nf4", w, scales, E, N, K, "weights", "scales")
+    _check_tensor(dy, "dy", torch.bfloat16, (M, N))
+    _check_tensor(u, "u", torch.float32, (M, r))
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    if grad_a is None:
+        grad_a = torch.empty((E, r, K), dtype=torch.float32, device=dy.device)
+    if grad_b is None:
+        grad_b = torch.empty((E, N, r), dtype=torch.float32, device=dy.device)
+    _check_tensor(dx, "dx", torch.bfloat16, (M, K))
+    _check_tensor(grad_a, "grad_a", torch.float32, (E, r, K))
+    _check_tensor(grad_b, "grad_b", torch.float32, (E, N, r))
+    _require_gpu(dy, sizes, w, scales, x, lora_a, lora_b, u, dx, grad_a, grad_b)
+    op = GEG_OP_NF4_DGRAD if fmt == "nf4" else GEG_OP_MXFP4_DGRAD
+    ws = _workspace(workspace, lib().geg_lora_workspace_bytes(op, M, N, K, E, r), dy.device, stream)
+    fn = getattr(lib(), "gnf4_grouped_dgrad_lora" if fmt == "nf4" else "gmxfp4_grouped_dgrad_lora")
+    _check(fn(_ptr(dy), _ptr(sizes), _ptr(w), _ptr(scales), _ptr(x), _ptr(lora_a), _ptr(lora_b), _ptr(u),
+              float(scale), _ptr(dx), _ptr(grad_a), _ptr(grad_b), M, N, K, E, r, _ptr(ws.buf), ws.nbytes,
+              ctypes.byref(opts) if opts else None, _stream(stream)))
+    return dx, grad_a, grad_b
+
+
+def gnf4_grouped_dgrad_lora(dy, sizes, w, absmax, x, lora_a, lora_b, u, scale: float, dx=None, grad_a=None,
+                            grad_b=None, workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+    """Backward of gnf4_grouped_gemm_lora: (dx = dy W_e + scale (dy B_e) A_e bf16
+    [M, K], grad_a fp32 [E, r, K], grad_b fp32 [E, N, r])."""
+    return _dgrad_lora("nf4", dy, sizes, w, absmax, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b, workspace,
+                       opts, stream)
+
+
+def gmxfp4_grouped_dgrad_lora(dy, sizes, blocks, scales, x, lora_a, lora_b, u, scale: float, dx=None, grad_a=None,
+                              grad_b=None, workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+    """The same on MXFP4 weights."""
+    if blocks.dim() == 4:
+        blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
+    return _dgrad_lora("mxfp4", dy, sizes, blocks, scales, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b,
+                       workspace, opts, stream)
+
+
+def grouped_linear_lora(a, sizes, w, scales, lora_a, lora_b, scale: float, fmt: str = "nf4"):
+    """The grouped 4-bit projection with a trainable low-rank delta at the
+    pre-activation point, as a torch autograd op: out = a_e W_e^T + scale *
+    (a_e A_e^T) B_e^T per expert. Backward: dA (through the dgrad kernel and the
+    adapter kernels), d lora_a, d lora_b (fp32); the 4-bit weights are frozen."""
+    return _GroupedLinearLora.apply(a, sizes, w, scales, lora_a, lora_b, float(scale), fmt)
+
+
 def grouped_linear(a, sizes, w, scales, fmt: str = "nf4"):
     """The grouped 4-bit GEMM as a differentiable op (torch autograd): out = per
     expert a_e W_e^T; the backward returns dA = per expert dOut_e W_e through the
@@ -373,17 +485,41 @@ def _make_grouped_linear():
     return GroupedLinear
 
 
+def _make_grouped_linear_lora():
+    import torch
+
+    class GroupedLinearLora(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, a, sizes, w, scales, lora_a, lora_b, scale, fmt):
+            fn = gnf4_grouped_gemm_lora if fmt == "nf4" else gmxfp4_grouped_gemm_lora
+            out, u = fn(a, sizes, w, scales, lora_a, lora_b, scale)
+            ctx.save_for_backward(a, sizes, w, scales, lora_a, lora_b, u)
+            ctx.fmt, ctx.scale = fmt, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            a, sizes, w, scales, lora_a, lora_b, u = ctx.saved_tensors
+            fn = gnf4_grouped_dgrad_lora if ctx.fmt == "nf4" else gmxfp4_grouped_dgrad_lora
+            da, ga, gb = fn(grad_out.contiguous(), sizes, w, scales, a, lora_a, lora_b, u, ctx.scale)
+            return (da if ctx.needs_input_grad[0] else None), None, None, None, ga, gb, None, None
+
+    return GroupedLinearLora
+
+
 class _LazyFn:
-    def __init__(self):
+    def __init__(self, make):
+        self._make = make
         self._f = None
 
     def apply(self, *args):
         if self._f is None:
-            self._f = _make_grouped_linear()
+            self._f = self._make()
         return self._f.apply(*args)
 
 
-_GroupedLinear = _LazyFn()
+_GroupedLinear = _LazyFn(_make_grouped_linear)
+_GroupedLinearLora = _LazyFn(_make_grouped_linear_lora)
 
 
 def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream):

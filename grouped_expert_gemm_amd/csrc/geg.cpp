@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 
@@ -135,8 +136,10 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
+  // Scratch of every op starts past the split-K counters, which must stay zero
+  // between calls that share a workspace.
   if (op == GEG_OP_MXFP4_W4A8) {   // e4m3 codes [M, K] and their scales [M, K/32]
-    p.a16_off = kHeader;
+    p.a16_off = kHeader + kCounterBytes;
     // scales step-major, 4 per row and 128-wide k step
     p.a16_bytes = round256((size_t)M * (size_t)K) + round256((size_t)M * (size_t)((K / 32 + 3) & ~3));
     p.total_bytes = p.a16_off + p.a16_bytes;
@@ -225,15 +228,31 @@ geg_status check_shape(int64_t M, int64_t N, int64_t K, int32_t E, int64_t kmult
 }
 
 // glu = 1: the fused expert block's first projection (out is [M, N/2], see GemmArgs).
+// Low-rank adapter delta for the tiled kernel's epilogue (r == 0: none), and a
+// step that runs after every check passed and before the GEMM's launches.
+struct LoraIn {
+  const float* u = nullptr;
+  const float* q = nullptr;
+  int32_t r = 0;
+  float s = 0.f;
+  std::function<hipError_t()> pre;
+  std::function<hipError_t()> post;
+};
+
 geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8_t* wq,
                        const void* scales, void* out, int64_t M, int64_t N, int64_t K, int32_t E,
                        void* ws, size_t ws_bytes, const geg_opts* opts, hipStream_t stream,
-                       int32_t glu = 0) {
+                       int32_t glu = 0, const LoraIn& lora = LoraIn{}) {
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
   if (glu && (N % 2)) return fail(GEG_ERR_BAD_SHAPE, "the fused gate/up width must be even");
   if (glu && opts && opts->force_path == 1)
     return fail(GEG_ERR_BAD_OPTION, "the expert block does not run on the skinny kernel (force_path 1)");
+  // the adapter delta lives in the tiled kernel's epilogue: every expert is tiled
+  geg_opts tiled{};
+  if (opts) tiled = *opts;
+  tiled.force_path = 2;
+  if (lora.r > 0) opts = &tiled;
   Plan p;
   st = make_plan(fmt == geg::NF4 ? GEG_OP_NF4_FWD : GEG_OP_MXFP4_FWD, M, N, K, E, opts, p);
   if (st != GEG_OK) return st;
@@ -272,6 +291,14 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
   g.glu = glu;
+  g.lora_u = lora.u;
+  g.lora_q = lora.q;
+  g.lora_r = lora.r;
+  g.lora_s = lora.s;
+  if (lora.pre) {
+    hipError_t e = lora.pre();
+    if (e != hipSuccess) return hip_fail(e, "adapter launch");
+  }
 
   if (p.run_tile) {
     if (fmt == geg::NF4) {
@@ -323,7 +350,8 @@ geg_status block_layout(int fmt, int64_t M, int64_t H, int64_t I, int32_t E, con
   geg_status st;
   if ((st = make_plan(op, M, 2 * I, H, E, o, p1)) != GEG_OK) return st;
   if ((st = make_plan(op, M, H, I, E, o, p2)) != GEG_OK) return st;
-  act_off = round256(std::max(p1.total_bytes, p2.total_bytes));
+  // past both GEMMs' scratch and never inside the split-K counter region
+  act_off = round256(std::max({p1.total_bytes, p2.total_bytes, kHeader + kCounterBytes}));
   total = act_off + round256((size_t)M * (size_t)I * 2);
   return GEG_OK;
 }
@@ -366,7 +394,8 @@ geg_status block_common(int fmt, const void* a, const int32_t* sizes, const uint
 
 geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uint8_t* w, const void* absmax,
                         void* dx, int64_t M, int64_t N, int64_t K, int32_t E, void* workspace,
-                        size_t workspace_bytes, const geg_opts* opts, hipStream_t stream) {
+                        size_t workspace_bytes, const geg_opts* opts, hipStream_t stream,
+                        const LoraIn& lora = LoraIn{}) {
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
   if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");
@@ -399,9 +428,14 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
   g.K = K;
   g.E = E;
   g.thresh = 0;   // every expert with rows goes through the tiled kernel
+  g.lora_u = lora.u;
+  g.lora_q = lora.q;
+  g.lora_r = lora.r;
+  g.lora_s = lora.s;
   g.split = 1;
   g.err = reinterpret_cast<uint32_t*>(wsb);
   hipError_t e = hipSuccess;
+  if (lora.pre && (e = lora.pre()) != hipSuccess) return hip_fail(e, "adapter launch");
   if (fmt == geg::NF4) {
     e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * N, g.err, stream);
     if (e != hipSuccess) return hip_fail(e, "dY conversion launch");
@@ -414,6 +448,7 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
   if (e == hipSuccess) e = record_event(opts, 1, stream);
   if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
   ++g_launches;
+  if (lora.post && (e = lora.post()) != hipSuccess) return hip_fail(e, "adapter launch");
   return GEG_OK;
 }
 
@@ -528,10 +563,173 @@ geg_status gmxfp8_quantize(const void* a, uint8_t* codes, uint8_t* scales, int64
   return GEG_OK;
 }
 
+size_t geg_lora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E, int32_t r) {
+  if (M < 0 || N <= 0 || K <= 0 || E <= 0 || r <= 0) return 0;
+  Plan p;
+  if (op == GEG_OP_NF4_FWD || op == GEG_OP_MXFP4_FWD) {
+    geg_opts tiled{};
+    tiled.force_path = 2;
+    if (make_plan(op, M, N, K, E, &tiled, p) != GEG_OK) return 0;
+    return p.total_bytes;
+  }
+  if (op != GEG_OP_NF4_DGRAD && op != GEG_OP_MXFP4_DGRAD) return 0;
+  if (make_plan(op, M, N, K, E, nullptr, p) != GEG_OK) return 0;
+  return std::max(p.total_bytes, kHeader + kCounterBytes) + round256((size_t)E * r * N * 4) +
+         round256((size_t)E * K * r * 4) + round256((size_t)M * r * 4);
+}
+
+}  // extern "C"
+
+namespace {
+
+geg_status lora_args(int32_t r, const float* lora_a, const float* lora_b) {
+  if (r < 8 || r > 64 || r % 8) return fail(GEG_ERR_BAD_SHAPE, "the adapter rank r must be 8, 16, ..., 64");
+  if (!lora_a || !lora_b) return fail(GEG_ERR_NULL_POINTER, "lora_a and lora_b are required");
+  if (!aligned(lora_a, 16) || !aligned(lora_b, 16)) return fail(GEG_ERR_MISALIGNED, "lora_a and lora_b must be 16-byte aligned");
+  geg_status st;
+  if ((st = check_device_ptr(lora_a, "lora_a")) != GEG_OK) return st;
+  return check_device_ptr(lora_b, "lora_b");
+}
+
+geg_status gemm_lora(int fmt, const void* a, const int32_t* sizes, const uint8_t* w, const void* scales,
+                     const float* lora_a, const float* lora_b, float scale, void* out, void* u, int64_t M, int64_t N,
+                     int64_t K, int32_t E, int32_t r, void* workspace, size_t workspace_bytes, const geg_opts* opts,
+                     hipStream_t stream) {
+  geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
+  if (st != GEG_OK) return st;
+  if (M == 0) return GEG_OK;
+  if ((st = lora_args(r, lora_a, lora_b)) != GEG_OK) return st;
+  if (!u) return fail(GEG_ERR_NULL_POINTER, "u is required");
+  if (!aligned(u, 16)) return fail(GEG_ERR_MISALIGNED, "u must be 16-byte aligned");
+  if ((st = check_device_ptr(u, "u")) != GEG_OK) return st;
+  LoraIn L;
+  L.u = reinterpret_cast<const float*>(u);
+  L.q = lora_b;
+  L.r = r;
+  L.s = scale;
+  // u = x A_e^T first; the tiled kernel's epilogue then adds s u B_e^T
+  L.pre = [=]() -> hipError_t {
+    ++g_launches;
+    return geg::launch_lora_down(reinterpret_cast<const uint16_t*>(a), lora_a, sizes, E, M, K, r, 1.0f,
+                                 reinterpret_cast<float*>(u), reinterpret_cast<uint32_t*>(workspace), cu_count(),
+                                 stream);
+  };
+  return gemm_common(fmt, a, sizes, w, scales, out, M, N, K, E, workspace, workspace_bytes, opts, stream, 0, L);
+}
+
+geg_status dgrad_lora(int fmt, const void* dy, const int32_t* sizes, const uint8_t* w, const void* scales,
+                      const void* x, const float* lora_a, const float* lora_b, const void* u, float scale, void* dx,
+                      float* grad_a, float* grad_b, int64_t M, int64_t N, int64_t K, int32_t E, int32_t r,
+                      void* workspace, size_t workspace_bytes, const geg_opts* opts, hipStream_t stream) {
+  geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
+  if (st != GEG_OK) return st;
+  if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");
+  if ((st = lora_args(r, lora_a, lora_b)) != GEG_OK) return st;
+  if (!grad_a || !grad_b || !sizes) return fail(GEG_ERR_NULL_POINTER, "grad_a, grad_b and sizes are required");
+  if (!aligned(grad_a, 4) || !aligned(grad_b, 4)) return fail(GEG_ERR_MISALIGNED, "grad_a and grad_b must be 4-byte aligned");
+  if (M > 0 && (!x || !u)) return fail(GEG_ERR_NULL_POINTER, "x and u are required");
+  if (M > 0 && (!aligned(x, 16) || !aligned(u, 16))) return fail(GEG_ERR_MISALIGNED, "x and u must be 16-byte aligned");
+  if (!workspace) return fail(GEG_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = geg_lora_workspace_bytes(fmt == geg::NF4 ? GEG_OP_NF4_DGRAD : GEG_OP_MXFP4_DGRAD, M, N, K, E, r);
+  if (workspace_bytes < need)
+    return fail(GEG_ERR_WORKSPACE, "workspace smaller than geg_lora_workspace_bytes(): need " + std::to_string(need));
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{grad_a, "grad_a"}, {grad_b, "grad_b"},
+                           {sizes, "sizes"}, {workspace, "workspace"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  if (M > 0)
+    for (auto [ptr, name] : {std::pair<const void*, const char*>{x, "x"}, {u, "u"}})
+      if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  Plan p;
+  if ((st = make_plan(fmt == geg::NF4 ? GEG_OP_NF4_DGRAD : GEG_OP_MXFP4_DGRAD, M, N, K, E, nullptr, p)) != GEG_OK)
+    return st;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  uint32_t* err = reinterpret_cast<uint32_t*>(wsb);
+  // adapter scratch past the dgrad's own and past the split-K counter region
+  const size_t lb = std::max(p.total_bytes, kHeader + kCounterBytes);
+  float* Bt = reinterpret_cast<float*>(wsb + lb);                                    // [E, r, N]
+  float* At = reinterpret_cast<float*>(wsb + lb + round256((size_t)E * r * N * 4));  // [E, K, r]
+  float* g = reinterpret_cast<float*>(wsb + lb + round256((size_t)E * r * N * 4) +
+                                      round256((size_t)E * K * r * 4));              // [M, r]
+  const int cus = cu_count();
+  const uint16_t* dy16 = reinterpret_cast<const uint16_t*>(dy);
+  // adapter gradients (zeros for experts without rows, and for M == 0)
+  auto grads = [=]() -> hipError_t {
+    hipError_t e = geg::launch_lora_grad(dy16, reinterpret_cast<const float*>(u), sizes, E, M, N, r, scale, grad_b,
+                                         false, err, cus, stream);
+    if (e == hipSuccess)
+      e = geg::launch_lora_grad(reinterpret_cast<const uint16_t*>(x), g, sizes, E, M, K, r, 1.0f, grad_a, true, err,
+                                cus, stream);
+    g_launches += 2;
+    return e;
+  };
+  if (M == 0) {
+    hipError_t e = grads();
+    return e == hipSuccess ? GEG_OK : hip_fail(e, "adapter launch");
+  }
+  LoraIn L;
+  L.u = g;
+  L.q = At;
+  L.r = r;
+  L.s = 1.0f;
+  // g = s dy B_e (from a transposed copy of B) and a transposed copy of A first;
+  // the dgrad epilogue adds g A_e; the gradients after
+  L.pre = [=]() -> hipError_t {
+    hipError_t e = geg::launch_lora_transpose(lora_b, E, N, r, Bt, cus, stream);
+    if (e == hipSuccess) e = geg::launch_lora_down(dy16, Bt, sizes, E, M, N, r, scale, g, err, cus, stream);
+    if (e == hipSuccess) e = geg::launch_lora_transpose(lora_a, E, r, K, At, cus, stream);
+    g_launches += 3;
+    return e;
+  };
+  L.post = grads;
+  return dgrad_common(fmt, dy, sizes, w, scales, dx, M, N, K, E, workspace, workspace_bytes, opts, stream, L);
+}
+
+}  // namespace
+
+extern "C" {
+
+geg_status gnf4_grouped_gemm_lora(const void* a, const int32_t* sizes, const uint8_t* w, const float* absmax,
+                                  const float* lora_a, const float* lora_b, float scale, void* out, void* u, int64_t M,
+                                  int64_t N, int64_t K, int32_t E, int32_t r, void* workspace, size_t workspace_bytes,
+                                  const geg_opts* opts, hipStream_t stream) {
+  return gemm_lora(geg::NF4, a, sizes, w, absmax, lora_a, lora_b, scale, out, u, M, N, K, E, r, workspace,
+                   workspace_bytes, opts, stream);
+}
+
+geg_status gmxfp4_grouped_gemm_lora(const void* a, const int32_t* sizes, const uint8_t* blocks, const uint8_t* scales,
+                                    const float* lora_a, const float* lora_b, float scale, void* out, void* u,
+                                    int64_t M, int64_t N, int64_t K, int32_t E, int32_t r, void* workspace,
+                                    size_t workspace_bytes, const geg_opts* opts, hipStream_t stream) {
+  return gemm_lora(geg::MXFP4, a, sizes, blocks, scales, lora_a, lora_b, scale, out, u, M, N, K, E, r, workspace,
+                   workspace_bytes, opts, stream);
+}
+
+geg_status gnf4_grouped_dgrad_lora(const void* dy, const int32_t* sizes, const uint8_t* w, const float* absmax,
+                                   const void* x, const float* lora_a, const float* lora_b, const void* u, float scale,
+                                   void* dx, float* grad_a, float* grad_b, int64_t M, int64_t N, int64_t K, int32_t E,
+                                   int32_t r, void* workspace, size_t workspace_bytes, const geg_opts* opts,
+                                   hipStream_t stream) {
+  return dgrad_lora(geg::NF4, dy, sizes, w, absmax, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b, M, N, K, E, r,
+                    workspace, workspace_bytes, opts, stream);
+}
+
+geg_status gmxfp4_grouped_dgrad_lora(const void* dy, const int32_t* sizes, const uint8_t* blocks,
+                                     const uint8_t* scales, const void* x, const float* lora_a, const float* lora_b,
+                                     const void* u, float scale, void* dx, float* grad_a, float* grad_b, int64_t M,
+                                     int64_t N, int64_t K, int32_t E, int32_t r, void* workspace,
+                                     size_t workspace_bytes, const geg_opts* opts, hipStream_t stream) {
+  return dgrad_lora(geg::MXFP4, dy, sizes, blocks, scales, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b, M, N, K,
+                    E, r, workspace, workspace_bytes, opts, stream);
+}
+
 size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0 || E > geg::kMaxExperts) return 0;
   const int64_t nchunks = (T * k + geg::kThreads - 1) / geg::kThreads;
-  return kHeader + round256((size_t)std::max<int64_t>(nchunks, 1) * (size_t)E * 4);
+  // chunk counts past the split-K counter region (a workspace shared with the
+  // grouped GEMM keeps its counters at zero)
+  return kHeader + kCounterBytes + round256((size_t)std::max<int64_t>(nchunks, 1) * (size_t)E * 4);
 }
 
 geg_status geg_route_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
@@ -560,7 +758,7 @@ geg_status geg_route_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t
     if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
   uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
   const int64_t n = T * k;
-  hipError_t e = geg::launch_route_sort(topk_ids, n, E, reinterpret_cast<int32_t*>(wsb + kHeader), sizes,
+  hipError_t e = geg::launch_route_sort(topk_ids, n, E, reinterpret_cast<int32_t*>(wsb + kHeader + kCounterBytes), sizes,
                                         row_of, src_of, reinterpret_cast<uint32_t*>(wsb), stream);
   if (e != hipSuccess) return hip_fail(e, "routing sort launch");
   g_launches += n > 0 ? 3 : 1;

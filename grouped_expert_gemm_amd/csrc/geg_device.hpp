@@ -368,6 +368,29 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
 // sizes[e] counts expert e's rows) and a prefix sum of work units per expert.
 // Negative sizes count as 0 and offsets are clamped to M, so no unit ever
 // touches a row outside [0, M); both conditions are flagged in the error word.
+// 8 consecutive fp32 values of a row (two 16-byte buffer loads; `ok` false or a
+// record past the end reads zeros) as two bf16x8 MFMA operands: hi = bf16(v) and
+// lo = bf16(v - hi), about 16 significant bits together (v scaled first).
+struct Split8 {
+  u32x4 hi, lo;
+};
+__device__ __forceinline__ Split8 load8_split(const __amdgpu_buffer_rsrc_t& R, uint32_t elem_off, bool ok,
+                                              float scale = 1.0f) {
+  const uint32_t b = (elem_off * 4u) | ((uint32_t)!ok << 31);   // bit 31: past every record
+  const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(R, b, 0, 0);
+  const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(R, b + 16u, 0, 0);
+  Split8 s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v0 = scale * __uint_as_float(i < 2 ? p[2 * i] : q[2 * i - 4]);
+    const float v1 = scale * __uint_as_float(i < 2 ? p[2 * i + 1] : q[2 * i - 3]);
+    const uint32_t h = pack_bf16x2(v0, v1);
+    s.hi[i] = h;
+    s.lo[i] = pack_bf16x2(v0 - __uint_as_float(h << 16), v1 - __uint_as_float(h & 0xFFFF0000u));
+  }
+  return s;
+}
+
 struct Plan {
   int32_t off[kMaxExperts + 1];    // clamped row offsets
   int32_t upre[kMaxExperts + 1];   // exclusive prefix of work units

@@ -59,6 +59,14 @@ struct GemmArgs {
   float* partials;        // split-K partials [split, M, N]
   int32_t glu;            // 1: columns 2i, 2i+1 are (gate, up) of unit i and out is
                           // [M, N/2] with out[m, i] = bf16(silu(gate) * up)
+  // Low-rank adapter delta added to the tiled kernel's accumulators before the
+  // bf16 rounding (lora_r == 0: none): acc[m, c] += lora_s * sum_j
+  // lora_u[m, j] lora_q[e, c, j], lora_u fp32 [M, lora_r], lora_q fp32
+  // [E, output width, lora_r].
+  const float* lora_u;
+  const float* lora_q;
+  int32_t lora_r;
+  float lora_s;
 };
 
 // Each launcher returns the hipError_t of its launch.
@@ -85,6 +93,16 @@ hipError_t launch_mxfp8_quantize(const uint16_t* a, int64_t M, int64_t K, uint8_
 hipError_t launch_w4a8(const uint8_t* aq, const uint8_t* as, const int32_t* sizes, const uint8_t* wq,
                        const uint8_t* ws, uint16_t* out, int64_t M, int64_t N, int64_t K, int32_t E, uint32_t* err,
                        int cus, hipStream_t s);
+// Low-rank adapter: U = s X T_e^T (T fp32 [E, r, C], U fp32 [M, r]); G_e = s
+// sum_rows Wd^T Nw (fp32, [E, Wc, r] or with jc [E, r, Wc]); out[e] = in[e]^T
+// for fp32 [E, P, Qd]. The delta U Q^T itself is added in the tiled kernel's
+// epilogue (GemmArgs::lora_*).
+hipError_t launch_lora_down(const uint16_t* X, const float* T, const int32_t* sizes, int32_t E, int64_t M, int64_t C,
+                            int32_t r, float s, float* U, uint32_t* err, int cus, hipStream_t st);
+hipError_t launch_lora_grad(const uint16_t* Wd, const float* Nw, const int32_t* sizes, int32_t E, int64_t M,
+                            int64_t Wc, int32_t r, float s, float* G, bool jc, uint32_t* err, int cus, hipStream_t st);
+hipError_t launch_lora_transpose(const float* in, int64_t E, int64_t P, int64_t Qd, float* out, int cus,
+                                 hipStream_t st);
 hipError_t launch_route_combine(const uint16_t* y, int64_t N, const int32_t* row_of, const float* w, int64_t T,
                                 int32_t k, uint16_t* out, int cus, hipStream_t s);
 hipError_t launch_to_f16_slots(const uint16_t* a, uint16_t* a16, int64_t elems, uint32_t* err,

@@ -1,0 +1,182 @@
+// Low-rank adapter delta on the grouped expert projection: the trainable B(Ax)
+// composed with the frozen 4-bit projection at the pre-activation point, with
+// its backward ("grouped-nf4-gemm releases", v0.2.4 section: the differentiable
+// grouped GEMM). Per expert e, with A_e [r, K] and B_e [N, r] (fp32 master
+// weights) and the layer's scale s:
+//   forward   u = x A_e^T (fp32 [M, r], kept for the backward);  y += s u B_e^T
+//   backward  g = s dy B_e (fp32 [M, r]);  dx += g A_e;
+//             dB_e = s sum_rows dy^T u;  dA_e = sum_rows g^T x   (fp32)
+// The contractions with a rank-wide side run on 16x16x32 bf16 MFMAs with every
+// fp32 operand split into a bf16 high part and a bf16 remainder (x A^T here: two
+// instructions; u B^T and g A in the tiled kernel's epilogue: three, dropping
+// lo x lo), which keeps about 16 significant bits where a plain bf16 operand
+// keeps 8. The delta joins the projection's fp32 accumulators before their one
+// bf16 rounding. The contraction dimension is contiguous in both operands; the
+// backward gets that from transposed fp32 copies of A and B. The reductions
+// over rows for the adapter gradients run on the vector ALUs, one thread per
+// column of the wide operand.
+#include <algorithm>
+
+#include "geg_device.hpp"
+#include "geg_launch.hpp"
+
+namespace geg {
+
+namespace {
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lrsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+// offsets stay below 2^31; bit 31 moves an access past every record (reads 0)
+__device__ __forceinline__ uint32_t l_oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)!ok << 31); }
+
+// U[m, j] = s * sum_c X[m, c] T_e[j, c] for the rows m of each expert: X bf16
+// [M, C], T fp32 [E, r, C], U fp32 [M, r]. One wavefront per block of 16 rows of
+// one expert, all r columns (r / 16 column blocks, the last one partial when
+// r % 16 == 8). C % 8 == 0; rows past the expert read zeros.
+__global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __restrict__ X, const float* __restrict__ T,
+                                                             const int32_t* __restrict__ sizes, int32_t E, int64_t M,
+                                                             int64_t C, int32_t r, float s, float* __restrict__ U,
+                                                             uint32_t* err) {
+  __shared__ Plan plan;
+  const int32_t total = build_plan(plan, sizes, E, M, err, [](int32_t n) -> int32_t { return (n + 15) / 16; });
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ncb = (r + 15) / 16;
+  for (int32_t u = blockIdx.x * 4 + wave; u < total; u += gridDim.x * 4) {
+    const int e = find_expert(plan, E, u);
+    const int64_t row0 = plan.off[e] + (int64_t)(u - plan.upre[e]) * 16;
+    const int rows = (int)min<int64_t>(16, plan.off[e + 1] - row0);
+    const __amdgpu_buffer_rsrc_t RX = lrsrc(X + row0 * C, (int64_t)rows * C * 2);
+    const __amdgpu_buffer_rsrc_t RT = lrsrc(T + (int64_t)e * r * C, (int64_t)r * C * 4);
+    f32x4 acc[4] = {};
+    for (int64_t c0 = 0; c0 < C; c0 += 32) {
+      const int64_t c = c0 + 8 * g;
+      const bool ok = c < C;
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(RX, l_oob_unless(ok, (uint32_t)((r16 * C + c) * 2)), 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if (cb < ncb) {
+          const int j = 16 * cb + r16;
+          const Split8 b = load8_split(RT, (uint32_t)(j * C + c), ok && j < r);
+          acc[cb] = mfma16<MXFP4>(a, b.hi, acc[cb]);
+          acc[cb] = mfma16<MXFP4>(a, b.lo, acc[cb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      if (cb >= ncb) continue;
+      const int j = 16 * cb + r16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = 4 * g + q;
+        if (lr < rows && j < r) U[(row0 + lr) * r + j] = s * acc[cb][q];
+      }
+    }
+  }
+}
+
+// G_e = s * sum over the rows m of expert e of Wd[m, c] Nw[m, j]: Wd bf16
+// [M, Wc] (the wide operand), Nw fp32 [M, r]; G fp32 [E, Wc, r] (CJ) or
+// [E, r, Wc] (JC). One workgroup per (expert, 256 columns), one thread per
+// column; the narrow rows go through LDS 64 at a time. Every expert gets its
+// workgroups, so experts without rows write zeros.
+template <bool JC>
+__global__ __launch_bounds__(kThreads) void lora_grad_kernel(const uint16_t* __restrict__ Wd,
+                                                             const float* __restrict__ Nw,
+                                                             const int32_t* __restrict__ sizes, int32_t E, int64_t M,
+                                                             int64_t Wc, int32_t r, float s, float* __restrict__ G,
+                                                             uint32_t* err) {
+  __shared__ Plan plan;
+  __shared__ float nrow[64 * 64];
+  const int32_t nchunks = (int32_t)((Wc + kThreads - 1) / kThreads);
+  const int32_t total = build_plan(plan, sizes, E, M, err, [&](int32_t) -> int32_t { return nchunks; });
+  const int t = threadIdx.x;
+  for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int e = find_expert(plan, E, u);
+    const int64_t c = (int64_t)(u - plan.upre[e]) * kThreads + t;
+    const int64_t m0 = plan.off[e], m1 = plan.off[e + 1];
+    float acc[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) acc[j] = 0.f;
+    for (int64_t mb = m0; mb < m1; mb += 64) {
+      const int nr = (int)min<int64_t>(64, m1 - mb);
+      __syncthreads();   // the previous block's rows are consumed
+      for (int i = t; i < nr * r; i += kThreads)
+        nrow[(i / r) * 64 + (i % r)] = Nw[(mb + i / r) * r + (i % r)];
+      __syncthreads();
+      if (c < Wc) {
+        for (int i = 0; i < nr; ++i) {
+          const float w = __uint_as_float((uint32_t)Wd[(mb + i) * Wc + c] << 16);
+#pragma unroll
+          for (int j = 0; j < 64; ++j)
+            if (j < r) acc[j] += w * nrow[i * 64 + j];
+        }
+      }
+    }
+    if (c < Wc) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j)
+        if (j < r) G[JC ? ((int64_t)e * r + j) * Wc + c : ((int64_t)e * Wc + c) * r + j] = s * acc[j];
+    }
+    __syncthreads();   // nrow is reused by the next unit
+  }
+}
+
+// out[e, q, p] = in[e, p, q] for fp32 in [E, P, Qd] (32x32 tiles via LDS).
+__global__ __launch_bounds__(kThreads) void lora_transpose_kernel(const float* __restrict__ in, int64_t E, int64_t P,
+                                                                  int64_t Qd, float* __restrict__ out) {
+  __shared__ float tile[32][33];
+  const int64_t tp = (P + 31) / 32, tq = (Qd + 31) / 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  for (int64_t b = blockIdx.x; b < E * tp * tq; b += gridDim.x) {
+    const int64_t e = b / (tp * tq), rem = b % (tp * tq), p0 = (rem / tq) * 32, q0 = (rem % tq) * 32;
+    __syncthreads();
+    for (int i = ty; i < 32; i += 8) {
+      const int64_t p = p0 + i, q = q0 + tx;
+      tile[i][tx] = (p < P && q < Qd) ? in[(e * P + p) * Qd + q] : 0.f;
+    }
+    __syncthreads();
+    for (int i = ty; i < 32; i += 8) {
+      const int64_t q = q0 + i, p = p0 + tx;
+      if (q < Qd && p < P) out[(e * Qd + q) * P + p] = tile[tx][i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lora_down(const uint16_t* X, const float* T, const int32_t* sizes, int32_t E, int64_t M, int64_t C,
+                            int32_t r, float s, float* U, uint32_t* err, int cus, hipStream_t st) {
+  const int64_t units = (M + 15) / 16 + std::min<int64_t>(E, M);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((units + 3) / 4, (int64_t)cus * 8));
+  hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, X, T, sizes, E, M, C, r, s, U, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_grad(const uint16_t* Wd, const float* Nw, const int32_t* sizes, int32_t E, int64_t M,
+                            int64_t Wc, int32_t r, float s, float* G, bool jc, uint32_t* err, int cus, hipStream_t st) {
+  const int64_t units = (int64_t)E * ((Wc + kThreads - 1) / kThreads);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * 4));
+  if (jc)
+    hipLaunchKernelGGL(lora_grad_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, Wd, Nw, sizes, E, M, Wc, r,
+                       s, G, err);
+  else
+    hipLaunchKernelGGL(lora_grad_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, Wd, Nw, sizes, E, M, Wc, r,
+                       s, G, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_transpose(const float* in, int64_t E, int64_t P, int64_t Qd, float* out, int cus,
+                                 hipStream_t st) {
+  const int64_t tiles = E * ((P + 31) / 32) * ((Qd + 31) / 32);
+  if (tiles <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>(tiles, (int64_t)cus * 8);
+  hipLaunchKernelGGL(lora_transpose_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, in, E, P, Qd, out);
+  return hipGetLastError();
+}
+
+}  // namespace geg

@@ -528,6 +528,38 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     // whole 16-byte row pieces. acc[i][j][q] is row 16i + 4(lane/16) + q,
     // column 16j + lane%16 of the block; every write offset is a constant from
     // the lane's base.
+    if (g.lora_r > 0 && rows > 128 * wm) {
+      // Low-rank adapter delta into the accumulators before their bf16 rounding:
+      // block (i, j) += s U[rows 16 i .., 32 of r] Q[columns 16 j .., 32 of r]^T,
+      // the fp32 operands split into bf16 pairs (hi x hi + hi x lo + lo x hi; s
+      // applied to U before the split). Rows past the expert and columns past
+      // the output width read zeros.
+      const int r = g.lora_r;
+      const int r16 = lane & 15, kg = lane >> 4;
+      const int64_t qcols = min<int64_t>(64, O - n0 - 64 * wn);
+      const __amdgpu_buffer_rsrc_t RU = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(g.lora_u + (row0 + 128 * wm) * r), (short)0, (rows - 128 * wm) * r * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t RQ = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(g.lora_q + ((int64_t)e * O + n0 + 64 * wn) * r), (short)0,
+          (int32_t)(qcols > 0 ? qcols * r * 4 : 0), 0x00020000);
+      for (int j0 = 0; j0 < r; j0 += 32) {
+        const int jj = j0 + 8 * kg;
+        const bool ok = jj < r;
+        Split8 bq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bq[j] = load8_split(RQ, (uint32_t)((16 * j + r16) * r + jj), ok);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const Split8 au = load8_split(RU, (uint32_t)((16 * i + r16) * r + jj), ok, g.lora_s);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].hi, acc[i][j]);
+            acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].lo, acc[i][j]);
+            acc[i][j] = mfma16<MXFP4>(au.lo, bq[j].hi, acc[i][j]);
+          }
+        }
+      }
+    }
     uint16_t* E = L.epi[wave];
     if (!DG && g.glu) {
       // Fused expert block: columns 2c, 2c+1 (lanes l, l ^ 1) are the gate and

@@ -47,10 +47,12 @@
  *  - Workspace: `workspace` is a caller-allocated device buffer of at least
  *    geg_workspace_bytes(...) bytes, 256-byte aligned, zeroed once by
  *    geg_workspace_init before its first use. It holds the device error word,
- *    split-K arrival counters (a fixed 4 MiB region, left zeroed by every
- *    completed call), split-K partials and, for the NF4 tiled path, an fp16
- *    copy of the activations (M * K * 2 bytes; dgrad: of dY, M * N * 2 bytes;
- *    rewritten by every call); calls
+ *    split-K arrival counters (a fixed 4 MiB region after the 256-byte header,
+ *    left zeroed by every completed call, and never written by any other op,
+ *    so one workspace can serve every entry point), split-K partials and, for
+ *    the NF4 tiled path, an fp16 copy of the activations (M * K * 2 bytes;
+ *    dgrad: of dY, M * N * 2 bytes; rewritten by every call); every op's other
+ *    scratch also lies past the counter region; calls
  *    on one workspace must be ordered (same stream); concurrent calls must not
  *    share one.
  */
@@ -279,6 +281,47 @@ geg_status gmxfp4_w4a8_grouped_gemm(const void* a, const int32_t* sizes, const u
  */
 geg_status gmxfp8_quantize(const void* a, uint8_t* codes, uint8_t* scales, int64_t M, int64_t K,
                            hipStream_t stream);
+
+/*
+ * Low-rank adapter delta on the grouped projection ("grouped-nf4-gemm releases",
+ * v0.2.4 section: the trainable B(Ax) composed with the frozen 4-bit projection
+ * at the pre-activation point). Per expert e: lora_a fp32 [E, r, K] (A_e),
+ * lora_b fp32 [E, N, r] (B_e), one scale s; r in {8, 16, ..., 64}. The matrix
+ * instructions take each fp32 adapter operand as a bf16 high part plus a bf16
+ * remainder (about 16 significant bits, fp32 accumulation), and the delta joins
+ * the projection's fp32 accumulators before their single bf16 rounding. Every
+ * expert runs on the tiled kernel (force_path is ignored).
+ *
+ * g{nf4,mxfp4}_grouped_gemm_lora: out = x W_e^T + s (x A_e^T) B_e^T; also writes
+ *   u = x A_e^T (fp32 [M, r], 16-B aligned) for the backward. Other arguments
+ *   and the workspace as g{nf4,mxfp4}_grouped_gemm, sized with
+ *   geg_lora_workspace_bytes(GEG_OP_NF4_FWD or GEG_OP_MXFP4_FWD, ...).
+ * g{nf4,mxfp4}_grouped_dgrad_lora: with dy bf16 [M, N] (N % 8 == 0), the
+ *   forward's x and u: dx = dy W_e + g A_e with g = s dy B_e (bf16 [M, K]);
+ *   grad_a = sum over the rows of e of g^T x (fp32 [E, r, K]); grad_b = s sum
+ *   over the rows of e of dy^T u (fp32 [E, N, r]); experts without rows (and
+ *   M == 0) get zero gradients. Workspace: geg_lora_workspace_bytes(
+ *   GEG_OP_NF4_DGRAD or GEG_OP_MXFP4_DGRAD, ...).
+ */
+size_t geg_lora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E, int32_t r);
+geg_status gnf4_grouped_gemm_lora(const void* a, const int32_t* sizes, const uint8_t* w, const float* absmax,
+                                  const float* lora_a, const float* lora_b, float scale, void* out, void* u, int64_t M,
+                                  int64_t N, int64_t K, int32_t E, int32_t r, void* workspace, size_t workspace_bytes,
+                                  const geg_opts* opts, hipStream_t stream);
+geg_status gmxfp4_grouped_gemm_lora(const void* a, const int32_t* sizes, const uint8_t* blocks, const uint8_t* scales,
+                                    const float* lora_a, const float* lora_b, float scale, void* out, void* u,
+                                    int64_t M, int64_t N, int64_t K, int32_t E, int32_t r, void* workspace,
+                                    size_t workspace_bytes, const geg_opts* opts, hipStream_t stream);
+geg_status gnf4_grouped_dgrad_lora(const void* dy, const int32_t* sizes, const uint8_t* w, const float* absmax,
+                                   const void* x, const float* lora_a, const float* lora_b, const void* u, float scale,
+                                   void* dx, float* grad_a, float* grad_b, int64_t M, int64_t N, int64_t K, int32_t E,
+                                   int32_t r, void* workspace, size_t workspace_bytes, const geg_opts* opts,
+                                   hipStream_t stream);
+geg_status gmxfp4_grouped_dgrad_lora(const void* dy, const int32_t* sizes, const uint8_t* blocks,
+                                     const uint8_t* scales, const void* x, const float* lora_a, const float* lora_b,
+                                     const void* u, float scale, void* dx, float* grad_a, float* grad_b, int64_t M,
+                                     int64_t N, int64_t K, int32_t E, int32_t r, void* workspace,
+                                     size_t workspace_bytes, const geg_opts* opts, hipStream_t stream);
 
 /* Workspace bytes needed by one call of operation `op` with these sizes and options. */
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,

@@ -140,3 +140,11 @@ def test_python_binding_checks_operand_types_and_shapes():
     # well-formed operands get as far as the device check
     with pytest.raises(geg.GegError, match="GPU"):
         geg.gmxfp4_grouped_dgrad(dy, sizes, w, mx_s)
+
+
+def test_scratch_lies_past_the_counter_region():
+    # routing counts and the adapter backward's scratch never share bytes with the
+    # split-K counters [256, 256 + 4 MiB)
+    assert geg.lib().geg_route_workspace_bytes(64, 8, 64) >= 256 + (4 << 20) + 2 * 64 * 4   # 512 entries: 2 chunks
+    assert geg.lib().geg_lora_workspace_bytes(geg.GEG_OP_MXFP4_DGRAD, 64, 128, 256, 4, 8) >= 256 + (4 << 20)
+    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_W4A8, 64, 128, 256, 4) >= 256 + (4 << 20) + 64 * 256

@@ -1,0 +1,105 @@
+"""GPU parity of the low-rank adapter delta (forward at the pre-activation point
+and backward for the input and both adapter matrices) against oracle.lora, on
+top of the grouped 4-bit projection and its dgrad. Tolerance: the path's
+|gpu - ref| <= 1e-2 max(1, |ref|) on every output (bf16 activations, fp32
+adapter gradients)."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from oracle import lora as L
+from gpu_util import assert_close, bf16_to_f64, log, up, up_u16_as_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def geg():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_expert_gemm_amd as g
+    g.lib()
+    return g
+
+
+def _case(fmt, E, K, N, r, sizes, seed):
+    rng = np.random.default_rng(seed)
+    M = int(sum(sizes))
+    x = synthetic.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    dy = synthetic.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    A = (rng.standard_normal((E, r, K)) / np.sqrt(K)).astype(np.float32)
+    B = (rng.standard_normal((E, N, r)) * 0.5).astype(np.float32)
+    if fmt == "nf4":
+        packs = [oracle.quantize_pack_nf4((rng.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in range(E)]
+        W = lambda e: oracle.dequant_nf4(*packs[e])
+    else:
+        packs = [(rng.integers(0, 256, (N, K // 2), dtype=np.uint8), rng.integers(119, 124, (N, K // 32), dtype=np.uint8))
+                 for _ in range(E)]
+        W = lambda e: oracle.dequant_mxfp4(*packs[e])
+    codes = np.stack([p[0] for p in packs])
+    scales = np.stack([p[1] for p in packs])
+    return x, dy, A, B, np.array(sizes, np.int32), W, codes, scales
+
+
+@pytest.mark.parametrize("fmt,r,K,N,sizes", [
+    ("nf4", 16, 256, 200, [0, 5, 40, 0, 130, 1]),     # ragged rows and columns, empty experts
+    ("nf4", 8, 512, 96, [17, 3]),
+    ("mxfp4", 64, 288, 136, [9, 0, 70]),               # rank 64: two 32-wide contraction steps
+    ("mxfp4", 32, 128, 57, [4, 33]),                   # odd N (forward only)
+])
+def test_lora_forward_and_backward(geg, fmt, r, K, N, sizes):
+    import torch
+    log(f"case: lora {fmt} r={r} K={K} N={N} sizes={sizes}")
+    x, dy, A, B, sz, W, codes, scales = _case(fmt, len(sizes), K, N, r, sizes, seed=K + N + r)
+    s = 0.5
+    fwd = geg.gnf4_grouped_gemm_lora if fmt == "nf4" else geg.gmxfp4_grouped_gemm_lora
+    xt, szt, At, Bt = up_u16_as_bf16(x), up(sz), up(A), up(B)
+    wt, st = up(codes), up(scales)
+    out, u = fwd(xt, szt, wt, st, At, Bt, s)
+    assert_close(bf16_to_f64(out), L.lora_forward_ref(x, sz, W, A, B, s, N), f"lora forward {fmt} r={r}")
+    _, u_ref = L.lora_delta_ref(x, sz, A, B, s)
+    assert_close(u.cpu().numpy().astype(np.float64), u_ref, f"lora u {fmt} r={r}")
+    if N % 8:
+        return
+    bwd = geg.gnf4_grouped_dgrad_lora if fmt == "nf4" else geg.gmxfp4_grouped_dgrad_lora
+    dx, ga, gb = bwd(up_u16_as_bf16(dy), szt, wt, st, xt, At, Bt, u, s)
+    dx_ref, dA_ref, dB_ref = L.lora_backward_ref(x, dy, sz, W, A, B, s, K)
+    assert_close(bf16_to_f64(dx), dx_ref, f"lora dx {fmt} r={r}")
+    assert_close(ga.cpu().numpy().astype(np.float64), dA_ref, f"lora dA {fmt} r={r}")
+    assert_close(gb.cpu().numpy().astype(np.float64), dB_ref, f"lora dB {fmt} r={r}")
+
+
+def test_lora_autograd_op(geg):
+    import torch
+    log("case: lora autograd op")
+    x, dy, A, B, sz, W, codes, scales = _case("nf4", 4, 320, 136, 16, [5, 0, 90, 30], seed=21)
+    s = 2.0
+    a = up_u16_as_bf16(x).requires_grad_(True)
+    At = up(A).requires_grad_(True)
+    Bt = up(B).requires_grad_(True)
+    out = geg.grouped_linear_lora(a, up(sz), up(codes), up(scales), At, Bt, s, "nf4")
+    out.backward(up_u16_as_bf16(dy))
+    assert_close(bf16_to_f64(out), L.lora_forward_ref(x, sz, W, A, B, s, 136), "autograd lora forward")
+    dx_ref, dA_ref, dB_ref = L.lora_backward_ref(x, dy, sz, W, A, B, s, 320)
+    assert_close(bf16_to_f64(a.grad), dx_ref, "autograd lora dx")
+    assert_close(At.grad.cpu().numpy().astype(np.float64), dA_ref, "autograd lora dA")
+    assert_close(Bt.grad.cpu().numpy().astype(np.float64), dB_ref, "autograd lora dB")
+
+
+def test_lora_empty_batch_gives_zero_gradients(geg):
+    import torch
+    log("case: lora M=0")
+    E, K, N, r = 3, 64, 32, 8
+    x = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    dy = torch.zeros((0, N), dtype=torch.bfloat16, device="cuda")
+    u = torch.zeros((0, r), dtype=torch.float32, device="cuda")
+    A = torch.ones((E, r, K), dtype=torch.float32, device="cuda")
+    B = torch.ones((E, N, r), dtype=torch.float32, device="cuda")
+    w = torch.zeros((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    am = torch.ones((E, N, K // 64), dtype=torch.float32, device="cuda")
+    ga = torch.full((E, r, K), 5.0, device="cuda")
+    gb = torch.full((E, N, r), 5.0, device="cuda")
+    geg.gnf4_grouped_dgrad_lora(dy, up(np.zeros(E, np.int32)), w, am, x, A, B, u, 1.0, grad_a=ga, grad_b=gb)
+    assert not ga.any() and not gb.any()
