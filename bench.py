@@ -67,6 +67,9 @@ WORKLOADS = {
 # cases of one model share their routing; (prefill gate_up, prefill down, decode
 # gate_up, decode down).
 W4A8_WORKLOADS = {"gptoss_w4a8", "gptoss_down_w4a8"}
+# Low-rank adapter (rank, scale) on the grouped projection: forward with the delta
+# fused into the tiled kernel's epilogue, backward with dgrad + adapter gradients.
+LORA_WORKLOADS = {"olmoe_lora": ("olmoe_gate_up_t2048", 16, 2.0)}
 BLOCK_WORKLOADS = {
     "qwen3_block": ("qwen3_gate_up_t4096", "qwen3_down_t4096", "qwen3_gate_up_t1", "qwen3_down_t1"),
     "gptoss_block": ("gptoss_gate_up_t2048", "gptoss_down_t2048", "gptoss_gate_up_t1", "gptoss_down_t1"),
@@ -269,6 +272,128 @@ def cpu_baseline_block(cg, cdn, seed, budget_s=12.0):
                       "fp64 decode + numpy matmuls + SwiGLU", "seconds": secs, "host_cpus": os.cpu_count()}
 
 
+def cpu_baseline_lora(c, seed, r, s, budget_s=12.0):
+    """The adapter oracle (fp64 forward and backward of the frozen projection plus
+    the low-rank delta) on as many routed experts as fit in about budget_s
+    seconds, as TFLOP/s of the whole step's flops."""
+    import oracle
+    import synthetic
+    from oracle import cases as C
+    from oracle import lora as L
+    a_bits, sizes = synthetic.rows_bf16(c, seed)
+    dy = synthetic.dgrad_dy_bf16(c, seed)
+    off = oracle.offsets(sizes)
+    rng = np.random.default_rng([seed, 9])
+    experts = [e for e in range(c.E) if sizes[e]][:16]
+    flops, secs, used = 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    i = 0
+    while True:
+        e = experts[i % len(experts)]
+        i += 1
+        q, sc = C.nf4_expert(c, seed, e)
+        A = (rng.standard_normal((1, r, c.K)) / np.sqrt(c.K)).astype(np.float32)
+        B = (rng.standard_normal((1, c.N, r)) * 0.01).astype(np.float32)
+        rows = slice(int(off[e]), int(off[e + 1]))
+        n = int(off[e + 1] - off[e])
+        t0 = time.perf_counter()
+        W = oracle.dequant_nf4(q, sc)
+        one = np.array([n], np.int32)
+        L.lora_forward_ref(a_bits[rows], one, lambda _e: W, A, B, s, c.N)
+        L.lora_backward_ref(a_bits[rows], dy[rows], one, lambda _e: W, A, B, s, c.K)
+        secs += time.perf_counter() - t0
+        flops += lora_step_flops(n, c.N, c.K, r)
+        used += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0]) or os.cpu_count()
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{c.name} with a rank-{r} adapter: {used} expert forward + backward steps (cycling over "
+                      f"{len(experts)} routed experts), fp64 decode + numpy matmuls", "seconds": secs,
+            "host_cpus": os.cpu_count()}
+
+
+def lora_step_flops(M, N, K, r):
+    """Forward (projection + adapter) and backward (dgrad + adapter input gradient
+    + both adapter gradients) of the adapted grouped projection."""
+    return 2.0 * M * N * K * 2 + 2.0 * M * r * (K + N) + 2.0 * M * r * (N + K) + 2.0 * M * r * (N + K)
+
+
+def main_lora(args, torch, geg, synthetic):
+    name, r, s = LORA_WORKLOADS[args.workload]
+    c = synthetic.case(name)
+    dev = torch.device("cuda", 0)
+    a, sz, sizes, codes, scales = make_inputs(c, args.seed, torch, geg, dev)
+    rng = np.random.default_rng([args.seed, 9])
+    A = torch.from_numpy((rng.standard_normal((c.E, r, c.K)) / np.sqrt(c.K)).astype(np.float32)).to(dev)
+    B = torch.from_numpy((rng.standard_normal((c.E, c.N, r)) * 0.01).astype(np.float32)).to(dev)
+    dy = torch.from_numpy(synthetic.dgrad_dy_bf16(c, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((c.M, r), dtype=torch.float32, device=dev)
+    dx = torch.empty((c.M, c.K), dtype=torch.bfloat16, device=dev)
+    ga = torch.empty((c.E, r, c.K), dtype=torch.float32, device=dev)
+    gb = torch.empty((c.E, c.N, r), dtype=torch.float32, device=dev)
+    ws = geg.Workspace(max(geg.lib().geg_lora_workspace_bytes(geg.GEG_OP_NF4_FWD, c.M, c.N, c.K, c.E, r),
+                           geg.lib().geg_lora_workspace_bytes(geg.GEG_OP_NF4_DGRAD, c.M, c.N, c.K, c.E, r)))
+    wc = [(codes, scales)]
+
+    def fwd(w, opts=None):
+        geg.gnf4_grouped_gemm_lora(a, sz, w[0], w[1], A, B, s, out=out, u=u, workspace=ws, opts=opts)
+
+    def bwd(w, opts=None):
+        geg.gnf4_grouped_dgrad_lora(dy, sz, w[0], w[1], a, A, B, u, s, dx=dx, grad_a=ga, grad_b=gb, workspace=ws,
+                                    opts=opts)
+
+    def fwd_plain(w, opts=None):
+        geg.gnf4_grouped_gemm(a, sz, w[0], w[1], out=out, workspace=ws, opts=geg.Opts(2, 0))
+
+    def bwd_plain(w, opts=None):
+        geg.gnf4_grouped_dgrad(dy, sz, w[0], w[1], dx=dx, workspace=ws)
+
+    fwd(wc[0])
+    bwd(wc[0])
+    torch.cuda.synchronize()
+    assert ws.read_error() == 0, "device error word set"
+    for i in range(args.warmup):
+        fwd(wc[0]); bwd(wc[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd(wc[0]); bwd(wc[0])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    f_ms = float(np.mean(time_calls(fwd, wc, args.steps, args.warmup, torch)[0]))
+    b_ms = float(np.mean(time_calls(bwd, wc, args.steps, args.warmup, torch)[0]))
+    fp_ms = float(np.mean(time_calls(fwd_plain, wc, args.steps, args.warmup, torch)[0]))
+    bp_ms = float(np.mean(time_calls(bwd_plain, wc, args.steps, args.warmup, torch)[0]))
+    kern_ms = time_kernel(fwd, wc, args.steps, args.warmup, geg, torch, 0)
+    flops = lora_step_flops(c.M, c.N, c.K, r)
+    kflops = 2.0 * c.M * c.N * c.K + 2.0 * c.M * r * c.N   # the tiled kernel: projection + adapter delta
+    result = {
+        "metric": METRIC, "value": round(flops / ((f_ms + b_ms) * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": f"{name} with a rank-{r} adapter (forward + backward)", "format": c.fmt, "E": c.E,
+                   "K": c.K, "N": c.N, "rows": c.M, "rank": r, "scale": s},
+        "lora": {"forward_ms": round(f_ms, 5), "backward_ms": round(b_ms, 5), "plain_forward_ms": round(fp_ms, 5),
+                 "plain_dgrad_ms": round(bp_ms, 5),
+                 "adapter_overhead": round((f_ms + b_ms) / (fp_ms + bp_ms) - 1.0, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(kflops / (kern_ms * 1e-3) / 1e12, 2),
+                     "peak": round(PEAK_MFMA_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(kflops / (kern_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                     "kernel": f"tiled kernel with the adapter epilogue (nf4), {name}",
+                     "per_launch_gflop": round(kflops / 1e9, 3), "kernel_ms": round(kern_ms, 5), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_lora(c, args.seed, r, s, args.cpu_budget)
+    result["kernel_sha"] = kernel_sha()
+    print(json.dumps(result), flush=True)
+
+
 def main_block(args, torch, geg, synthetic):
     """Fused expert block workloads: prefill and decode calls of gnf4/gmxfp4_expert_block."""
     dev = torch.device("cuda", 0)
@@ -391,7 +516,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="olmoe", choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
+    ap.add_argument("--workload", default="olmoe",
+                    choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS) + sorted(LORA_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -422,6 +548,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload in BLOCK_WORKLOADS:
         main_block(args, torch, geg, synthetic)
+        return
+    if args.workload in LORA_WORKLOADS:
+        main_lora(args, torch, geg, synthetic)
         return
     pre_name, dec_name = WORKLOADS[args.workload]
     cp = synthetic.case(pre_name or dec_name)

@@ -82,16 +82,17 @@ __global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __r
 // G_e = s * sum over the rows m of expert e of Wd[m, c] Nw[m, j]: Wd bf16
 // [M, Wc] (the wide operand), Nw fp32 [M, r]; G fp32 [E, Wc, r] (CJ) or
 // [E, r, Wc] (JC). One workgroup per (expert, 256 columns), one thread per
-// column; the narrow rows go through LDS 64 at a time. Every expert gets its
+// column; the narrow rows go through LDS 64 at a time and each thread issues the
+// loads of 16 wide rows before their multiply-adds. Every expert gets its
 // workgroups, so experts without rows write zeros.
-template <bool JC>
+template <bool JC, int R>
 __global__ __launch_bounds__(kThreads) void lora_grad_kernel(const uint16_t* __restrict__ Wd,
                                                              const float* __restrict__ Nw,
                                                              const int32_t* __restrict__ sizes, int32_t E, int64_t M,
-                                                             int64_t Wc, int32_t r, float s, float* __restrict__ G,
+                                                             int64_t Wc, float s, float* __restrict__ G,
                                                              uint32_t* err) {
   __shared__ Plan plan;
-  __shared__ float nrow[64 * 64];
+  __shared__ __attribute__((aligned(16))) float nrow[64 * R];
   const int32_t nchunks = (int32_t)((Wc + kThreads - 1) / kThreads);
   const int32_t total = build_plan(plan, sizes, E, M, err, [&](int32_t) -> int32_t { return nchunks; });
   const int t = threadIdx.x;
@@ -99,28 +100,42 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(const uint16_t* __r
     const int e = find_expert(plan, E, u);
     const int64_t c = (int64_t)(u - plan.upre[e]) * kThreads + t;
     const int64_t m0 = plan.off[e], m1 = plan.off[e + 1];
-    float acc[64];
+    float acc[R];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) acc[j] = 0.f;
+    for (int j = 0; j < R; ++j) acc[j] = 0.f;
     for (int64_t mb = m0; mb < m1; mb += 64) {
       const int nr = (int)min<int64_t>(64, m1 - mb);
       __syncthreads();   // the previous block's rows are consumed
-      for (int i = t; i < nr * r; i += kThreads)
-        nrow[(i / r) * 64 + (i % r)] = Nw[(mb + i / r) * r + (i % r)];
+      // rows past the expert's last one read as zeros (no stale or unset LDS)
+      for (int i = t; i < 64 * R; i += kThreads) nrow[i] = i < nr * R ? Nw[mb * R + i] : 0.f;
       __syncthreads();
       if (c < Wc) {
-        for (int i = 0; i < nr; ++i) {
-          const float w = __uint_as_float((uint32_t)Wd[(mb + i) * Wc + c] << 16);
+        const uint16_t* wp = Wd + mb * Wc + c;
+        for (int i0 = 0; i0 < nr; i0 += 16) {
+          // 16 independent loads in flight before the multiply-adds
+          float w[16];
 #pragma unroll
-          for (int j = 0; j < 64; ++j)
-            if (j < r) acc[j] += w * nrow[i * 64 + j];
+          for (int k = 0; k < 16; ++k)
+            w[k] = i0 + k < nr ? __uint_as_float((uint32_t)wp[(int64_t)(i0 + k) * Wc] << 16) : 0.f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const float4* nv = reinterpret_cast<const float4*>(nrow + (i0 + k) * R);   // same address on every lane
+#pragma unroll
+            for (int j = 0; j < R / 4; ++j) {
+              const float4 v = nv[j];
+              acc[4 * j] += w[k] * v.x;
+              acc[4 * j + 1] += w[k] * v.y;
+              acc[4 * j + 2] += w[k] * v.z;
+              acc[4 * j + 3] += w[k] * v.w;
+            }
+          }
         }
       }
     }
     if (c < Wc) {
 #pragma unroll
-      for (int j = 0; j < 64; ++j)
-        if (j < r) G[JC ? ((int64_t)e * r + j) * Wc + c : ((int64_t)e * Wc + c) * r + j] = s * acc[j];
+      for (int j = 0; j < R; ++j)
+        G[JC ? ((int64_t)e * R + j) * Wc + c : ((int64_t)e * Wc + c) * R + j] = s * acc[j];
     }
     __syncthreads();   // nrow is reused by the next unit
   }
@@ -157,17 +172,30 @@ hipError_t launch_lora_down(const uint16_t* X, const float* T, const int32_t* si
   return hipGetLastError();
 }
 
+template <bool JC>
+hipError_t launch_grad_r(const uint16_t* Wd, const float* Nw, const int32_t* sizes, int32_t E, int64_t M, int64_t Wc,
+                         int32_t r, float s, float* G, uint32_t* err, int64_t grid, hipStream_t st) {
+  switch (r) {
+#define GEG_LORA_R(RR)                                                                                          \
+  case RR:                                                                                                      \
+    hipLaunchKernelGGL((lora_grad_kernel<JC, RR>), dim3((unsigned)grid), dim3(kThreads), 0, st, Wd, Nw, sizes, E, M, \
+                       Wc, s, G, err);                                                                          \
+    break;
+    GEG_LORA_R(8) GEG_LORA_R(16) GEG_LORA_R(24) GEG_LORA_R(32) GEG_LORA_R(40) GEG_LORA_R(48) GEG_LORA_R(56)
+    GEG_LORA_R(64)
+#undef GEG_LORA_R
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_lora_grad(const uint16_t* Wd, const float* Nw, const int32_t* sizes, int32_t E, int64_t M,
                             int64_t Wc, int32_t r, float s, float* G, bool jc, uint32_t* err, int cus, hipStream_t st) {
   const int64_t units = (int64_t)E * ((Wc + kThreads - 1) / kThreads);
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * 4));
-  if (jc)
-    hipLaunchKernelGGL(lora_grad_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, Wd, Nw, sizes, E, M, Wc, r,
-                       s, G, err);
-  else
-    hipLaunchKernelGGL(lora_grad_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, Wd, Nw, sizes, E, M, Wc, r,
-                       s, G, err);
-  return hipGetLastError();
+  return jc ? launch_grad_r<true>(Wd, Nw, sizes, E, M, Wc, r, s, G, err, grid, st)
+            : launch_grad_r<false>(Wd, Nw, sizes, E, M, Wc, r, s, G, err, grid, st);
 }
 
 hipError_t launch_lora_transpose(const float* in, int64_t E, int64_t P, int64_t Qd, float* out, int cus,
