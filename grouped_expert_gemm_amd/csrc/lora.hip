@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __r
 // [M, Wc] (the wide operand), Nw fp32 [M, r]; G fp32 [E, Wc, r] (CJ) or
 // [E, r, Wc] (JC). One workgroup per (expert, 256 columns), one thread per
 // column; the narrow rows go through LDS 64 at a time and each thread issues the
-// loads of 16 wide rows before their multiply-adds. Every expert gets its
+// loads of 32 wide rows before their multiply-adds. Every expert gets its
 // workgroups, so experts without rows write zeros.
 template <bool JC, int R>
 __global__ __launch_bounds__(kThreads) void lora_grad_kernel(const uint16_t* __restrict__ Wd,
@@ -107,18 +107,23 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(const uint16_t* __r
       const int nr = (int)min<int64_t>(64, m1 - mb);
       __syncthreads();   // the previous block's rows are consumed
       // rows past the expert's last one read as zeros (no stale or unset LDS)
-      for (int i = t; i < 64 * R; i += kThreads) nrow[i] = i < nr * R ? Nw[mb * R + i] : 0.f;
+      for (int i = 4 * t; i < 64 * R; i += 4 * kThreads)   // R % 8 == 0: whole 16-byte pieces
+        *reinterpret_cast<float4*>(nrow + i) =
+            i < nr * R ? *reinterpret_cast<const float4*>(Nw + mb * R + i) : float4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
       if (c < Wc) {
-        const uint16_t* wp = Wd + mb * Wc + c;
-        for (int i0 = 0; i0 < nr; i0 += 16) {
-          // 16 independent loads in flight before the multiply-adds
-          float w[16];
+        // rows past nr get offsets beyond the record and load zeros: no branches,
+        // so all 32 loads of a batch are in flight before the multiply-adds
+        const __amdgpu_buffer_rsrc_t RW = lrsrc(Wd + mb * Wc, (int64_t)nr * Wc * 2);
+        for (int i0 = 0; i0 < nr; i0 += 32) {
+          float w[32];
 #pragma unroll
-          for (int k = 0; k < 16; ++k)
-            w[k] = i0 + k < nr ? __uint_as_float((uint32_t)wp[(int64_t)(i0 + k) * Wc] << 16) : 0.f;
+          for (int k = 0; k < 32; ++k) {
+            const uint32_t off = l_oob_unless(i0 + k < nr, (uint32_t)(((int64_t)(i0 + k) * Wc + c) * 2));
+            w[k] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(RW, off, 0, 0) << 16);
+          }
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
+          for (int k = 0; k < 32; ++k) {
             const float4* nv = reinterpret_cast<const float4*>(nrow + (i0 + k) * R);   // same address on every lane
 #pragma unroll
             for (int j = 0; j < R / 4; ++j) {
