@@ -32,50 +32,76 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t lrsrc(const void* base, int64_
 __device__ __forceinline__ uint32_t l_oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)!ok << 31); }
 
 // U[m, j] = s * sum_c X[m, c] T_e[j, c] for the rows m of each expert: X bf16
-// [M, C], T fp32 [E, r, C], U fp32 [M, r]. One wavefront per block of 16 rows of
-// one expert, all r columns (r / 16 column blocks, the last one partial when
-// r % 16 == 8). C % 8 == 0; rows past the expert read zeros.
+// [M, C], T fp32 [E, r, C], U fp32 [M, r]. One workgroup per block of 16 rows
+// of one expert, all r columns (NCB = ceil(r / 16) column blocks, the last one
+// partial when r % 16 == 8); its four wavefronts take interleaved batches of the
+// contraction and are summed through LDS in wave order (deterministic).
+// C % 8 == 0; rows past the expert read zeros.
+template <int NCB>
 __global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __restrict__ X, const float* __restrict__ T,
                                                              const int32_t* __restrict__ sizes, int32_t E, int64_t M,
                                                              int64_t C, int32_t r, float s, float* __restrict__ U,
                                                              uint32_t* err) {
   __shared__ Plan plan;
+  __shared__ f32x4 red[3][NCB][64];
   const int32_t total = build_plan(plan, sizes, E, M, err, [](int32_t n) -> int32_t { return (n + 15) / 16; });
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int ncb = (r + 15) / 16;
-  for (int32_t u = blockIdx.x * 4 + wave; u < total; u += gridDim.x * 4) {
+  for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
     const int e = find_expert(plan, E, u);
     const int64_t row0 = plan.off[e] + (int64_t)(u - plan.upre[e]) * 16;
     const int rows = (int)min<int64_t>(16, plan.off[e + 1] - row0);
     const __amdgpu_buffer_rsrc_t RX = lrsrc(X + row0 * C, (int64_t)rows * C * 2);
     const __amdgpu_buffer_rsrc_t RT = lrsrc(T + (int64_t)e * r * C, (int64_t)r * C * 4);
-    f32x4 acc[4] = {};
-    for (int64_t c0 = 0; c0 < C; c0 += 32) {
-      const int64_t c = c0 + 8 * g;
-      const bool ok = c < C;
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(RX, l_oob_unless(ok, (uint32_t)((r16 * C + c) * 2)), 0, 0);
+    f32x4 acc[NCB] = {};
+    // kU steps' loads are issued before their MFMAs; steps past C read zeros
+    // through bit-31 offsets, so the batch has no branches
+    constexpr int kU = NCB <= 2 ? 8 : 4;
+    for (int64_t c00 = 32 * kU * wave; c00 < C; c00 += 32 * kU * 4) {
+      u32x4 a[kU];
+      Split8 b[kU][NCB];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (cb < ncb) {
+      for (int q = 0; q < kU; ++q) {
+        const int64_t c = c00 + 32 * q + 8 * g;
+        const bool ok = c < C;
+        a[q] = __builtin_amdgcn_raw_buffer_load_b128(RX, l_oob_unless(ok, (uint32_t)((r16 * C + c) * 2)), 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
           const int j = 16 * cb + r16;
-          const Split8 b = load8_split(RT, (uint32_t)(j * C + c), ok && j < r);
-          acc[cb] = mfma16<MXFP4>(a, b.hi, acc[cb]);
-          acc[cb] = mfma16<MXFP4>(a, b.lo, acc[cb]);
+          b[q][cb] = load8_split(RT, (uint32_t)(j * C + c), ok && j < r);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          acc[cb] = mfma16<MXFP4>(a[q], b[q][cb].hi, acc[cb]);
+          acc[cb] = mfma16<MXFP4>(a[q], b[q][cb].lo, acc[cb]);
         }
       }
     }
+    if (wave > 0) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      if (cb >= ncb) continue;
-      const int j = 16 * cb + r16;
+      for (int cb = 0; cb < NCB; ++cb) red[wave - 1][cb][lane] = acc[cb];
+    }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = 4 * g + q;
-        if (lr < rows && j < r) U[(row0 + lr) * r + j] = s * acc[cb][q];
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] += red[w][cb][lane];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int j = 16 * cb + r16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lr = 4 * g + q;
+          if (lr < rows && j < r) U[(row0 + lr) * r + j] = s * acc[cb][q];
+        }
       }
     }
+    __syncthreads();   // red is reused by the next unit
   }
 }
 
@@ -172,8 +198,14 @@ __global__ __launch_bounds__(kThreads) void lora_transpose_kernel(const float* _
 hipError_t launch_lora_down(const uint16_t* X, const float* T, const int32_t* sizes, int32_t E, int64_t M, int64_t C,
                             int32_t r, float s, float* U, uint32_t* err, int cus, hipStream_t st) {
   const int64_t units = (M + 15) / 16 + std::min<int64_t>(E, M);
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((units + 3) / 4, (int64_t)cus * 8));
-  hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, X, T, sizes, E, M, C, r, s, U, err);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * 16));
+  switch ((r + 15) / 16) {
+    case 1: hipLaunchKernelGGL(lora_down_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, st, X, T, sizes, E, M, C, r, s, U, err); break;
+    case 2: hipLaunchKernelGGL(lora_down_kernel<2>, dim3((unsigned)grid), dim3(kThreads), 0, st, X, T, sizes, E, M, C, r, s, U, err); break;
+    case 3: hipLaunchKernelGGL(lora_down_kernel<3>, dim3((unsigned)grid), dim3(kThreads), 0, st, X, T, sizes, E, M, C, r, s, U, err); break;
+    case 4: hipLaunchKernelGGL(lora_down_kernel<4>, dim3((unsigned)grid), dim3(kThreads), 0, st, X, T, sizes, E, M, C, r, s, U, err); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
