@@ -103,3 +103,42 @@ def test_lora_empty_batch_gives_zero_gradients(geg):
     gb = torch.full((E, N, r), 5.0, device="cuda")
     geg.gnf4_grouped_dgrad_lora(dy, up(np.zeros(E, np.int32)), w, am, x, A, B, u, 1.0, grad_a=ga, grad_b=gb)
     assert not ga.any() and not gb.any()
+
+
+@pytest.mark.timeout(900)
+def test_lora_full_size_sampled(geg):
+    """OLMoE gate_up NF4 at T=2048 (16384 routed rows, E=64, K=N=2048) with a
+    rank-16 adapter, through the same entry points the adapter bench times: the
+    projection on sampled outputs (the oracle computes them one by one), the
+    adapter parts (u, dA, dB and the adapter's share of dx) on every element."""
+    from oracle import cases as C
+    from gpu_util import gpu_weights_nf4, sample_positions
+    c = synthetic.case("olmoe_gate_up_t2048")
+    seed, r, s = 0, 16, 2.0
+    log(f"case: lora full size {c.name} (M={c.M} N={c.N} K={c.K} E={c.E}) r={r}")
+    a_bits, sizes = synthetic.rows_bf16(c, seed)
+    w, sc = gpu_weights_nf4(c, seed, experts=np.nonzero(sizes)[0])
+    rng = np.random.default_rng([seed, 9])
+    A = (rng.standard_normal((c.E, r, c.K)) / np.sqrt(c.K)).astype(np.float32)
+    B = (rng.standard_normal((c.E, c.N, r)) * 0.5).astype(np.float32)
+    dy = synthetic.f32_to_bf16_bits(rng.standard_normal((c.M, c.N)).astype(np.float32))
+    xt, szt, At, Bt = up_u16_as_bf16(a_bits), up(sizes), up(A), up(B)
+    out, u = geg.gnf4_grouped_gemm_lora(xt, szt, w, sc, At, Bt, s)
+    dx, ga, gb = geg.gnf4_grouped_dgrad_lora(up_u16_as_bf16(dy), szt, w, sc, xt, At, Bt, u, s)
+    # forward: frozen projection on samples + the adapter delta
+    delta, u_ref = L.lora_delta_ref(a_bits, sizes, A, B, s)
+    rows, cols = sample_positions(sizes, c.N, 1500, seed=1)
+    ref = oracle.sampled_fwd_ref(a_bits, sizes, C.nf4_rows_fn(c, seed), rows, cols) + delta[rows, cols]
+    assert_close(bf16_to_f64(out)[rows, cols], ref, "lora full forward (sampled)")
+    assert_close(u.cpu().numpy().astype(np.float64), u_ref, "lora full u")
+    # backward: the adapter parts in full (frozen weight set to zero), the frozen
+    # dgrad on samples inside a few 64-wide column blocks (plus the last one)
+    zero_w = lambda e: np.zeros((c.N, c.K))
+    dx_ad, dA_ref, dB_ref = L.lora_backward_ref(a_bits, dy, sizes, zero_w, A, B, s, c.K)
+    assert_close(ga.cpu().numpy().astype(np.float64), dA_ref, "lora full dA")
+    assert_close(gb.cpu().numpy().astype(np.float64), dB_ref, "lora full dB")
+    rows, cols = sample_positions(sizes, c.K, 600, seed=2)
+    blocks = np.append(np.random.default_rng(3).choice(c.K // 64 - 1, 3, replace=False), c.K // 64 - 1)
+    cols = blocks[cols % 4] * 64 + cols % 64
+    ref = oracle.sampled_dgrad_ref(dy, sizes, C.nf4_cols_fn(c, seed), rows, cols) + dx_ad[rows, cols]
+    assert_close(bf16_to_f64(dx)[rows, cols], ref, "lora full dx (sampled)")
