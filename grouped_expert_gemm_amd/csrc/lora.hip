@@ -7,10 +7,10 @@
 //   backward  g = s dy B_e (fp32 [M, r]);  dx += g A_e;
 //             dB_e = s sum_rows dy^T u;  dA_e = sum_rows g^T x   (fp32)
 // The contractions with a rank-wide side run on 16x16x32 bf16 MFMAs with every
-// fp32 operand split into a bf16 high part and a bf16 remainder (x A^T here: two
-// instructions; u B^T and g A in the tiled kernel's epilogue: three, dropping
-// lo x lo), which keeps about 16 significant bits where a plain bf16 operand
-// keeps 8. The delta joins the projection's fp32 accumulators before their one
+// fp32 operand split into bf16 parts: x A^T here (bf16 x times A in three
+// parts, about 24 significant bits: three instructions), u B^T and g A in the
+// tiled kernel's epilogue (both sides in two parts, about 16 bits: three
+// instructions, dropping lo x lo), where a plain bf16 operand keeps 8 bits. The delta joins the projection's fp32 accumulators before their one
 // bf16 rounding. The contraction dimension is contiguous in both operands; the
 // backward gets that from transposed fp32 copies of A and B. The reductions
 // over rows for the adapter gradients run on the vector ALUs, one thread per
@@ -30,6 +30,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t lrsrc(const void* base, int64_
 }
 // offsets stay below 2^31; bit 31 moves an access past every record (reads 0)
 __device__ __forceinline__ uint32_t l_oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)!ok << 31); }
+
+// Eight consecutive fp32 values of T at elem_off as three bf16 parts each
+// (v = hi + mid + lo exactly up to the last bits of lo: about 24 significant
+// bits); reads zeros when !ok (bit 31 puts the offset past every record).
+struct Split8x3 {
+  u32x4 hi, mid, lo;
+};
+__device__ __forceinline__ Split8x3 load8_split3(const __amdgpu_buffer_rsrc_t& R, uint32_t elem_off, bool ok) {
+  const uint32_t b = (elem_off * 4u) | ((uint32_t)!ok << 31);
+  const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(R, b, 0, 0);
+  const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(R, b + 16u, 0, 0);
+  Split8x3 t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v0 = __uint_as_float(i < 2 ? p[2 * i] : q[2 * i - 4]);
+    const float v1 = __uint_as_float(i < 2 ? p[2 * i + 1] : q[2 * i - 3]);
+    const uint32_t h = pack_bf16x2(v0, v1);
+    const float r0 = v0 - __uint_as_float(h << 16), r1 = v1 - __uint_as_float(h & 0xFFFF0000u);   // exact
+    const uint32_t m = pack_bf16x2(r0, r1);
+    t.hi[i] = h;
+    t.mid[i] = m;
+    t.lo[i] = pack_bf16x2(r0 - __uint_as_float(m << 16), r1 - __uint_as_float(m & 0xFFFF0000u));
+  }
+  return t;
+}
 
 // U[m, j] = s * sum_c X[m, c] T_e[j, c] for the rows m of each expert: X bf16
 // [M, C], T fp32 [E, r, C], U fp32 [M, r]. One workgroup per block of 16 rows
@@ -60,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __r
     constexpr int kU = NCB <= 2 ? 8 : 4;
     for (int64_t c00 = 32 * kU * wave; c00 < C; c00 += 32 * kU * 4) {
       u32x4 a[kU];
-      Split8 b[kU][NCB];
+      Split8x3 b[kU][NCB];
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
         const int64_t c = c00 + 32 * q + 8 * g;
@@ -69,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __r
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const int j = 16 * cb + r16;
-          b[q][cb] = load8_split(RT, (uint32_t)(j * C + c), ok && j < r);
+          b[q][cb] = load8_split3(RT, (uint32_t)(j * C + c), ok && j < r);
         }
       }
 #pragma unroll
@@ -77,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void lora_down_kernel(const uint16_t* __r
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           acc[cb] = mfma16<MXFP4>(a[q], b[q][cb].hi, acc[cb]);
+          acc[cb] = mfma16<MXFP4>(a[q], b[q][cb].mid, acc[cb]);
           acc[cb] = mfma16<MXFP4>(a[q], b[q][cb].lo, acc[cb]);
         }
       }
