@@ -1,29 +1,34 @@
 #!/usr/bin/env python3
 """Benchmark of the grouped 4-bit expert GEMM on one MI355X.
 
-Default workload: the OLMoE-1B-7B gate_up projection in NF4 (E=64 experts,
-K=2048, N=2048, top-8), one step = one prefill GEMM over 2048 tokens
-(M=16384 routed rows) plus one decode GEMM for one token (M=8). Inputs are
-seeded synthetic draws of the workload's shapes and distributions, resident in
-HBM before timing; weight stacks rotate over enough copies (>2 GiB) that no
-launch finds its weights in the 256 MB Infinity Cache.
+Default workload (`--workload headline`): the Mixtral-8x7B configuration, the
+largest single-GPU one, w1/w3 fused in NF4 (E=8 experts, K=4096, N=28672,
+top-2 over 4096 tokens: M=8192 routed rows). One step = the prefill forward
+GEMM, its input gradient (dgrad) on the same packed weights, and one decode
+call of every configured token-decode case (OLMoE, Qwen3 gate_up and down,
+gpt-oss gate_up and down at T=1; Qwen3 gate_up and down at T=64). Inputs are
+seeded synthetic draws of the workloads' shapes and distributions, resident in
+HBM before timing; every weight stack rotates over enough copies (>2.5 GB)
+that no launch finds its weights in the 256 MB Infinity Cache.
 
 Prints ONE JSON line:
-  value      prefill TFLOP/s (2*M*N*K over routed rows / prefill call time); for
-             the decode-only workloads (qwen3_t64, qwen3_down_t64) the decode
-             call's packed-weight GB/s
-  decode     packed-weight GB/s of the decode call (codes + scales of touched experts)
-  roofline   the dominant kernel (tiled/dgrad kernel; the decode kernels -- vector
-             or narrow path -- for decode-only workloads) against its bound: algorithmic flops (or packed-weight
-             bytes) per launch over the kernel's own time, from the two HIP events
-             the library records around it on the launch stream
+  value      prefill TFLOP/s of the Mixtral w1/w3 forward call (2*M*N*K over
+             routed rows / call time, HIP-graph timed); the dgrad leg beside it
+  decode     packed-weight GB/s of each decode case (codes + scales of touched
+             experts / call time) beside a plain device copy of the same bytes
+  roofline   the dominant kernel of the step (the longer of the forward and the
+             dgrad tiled kernels): algorithmic flops per launch over the kernel's
+             own time from two HIP events the library records around it on the
+             launch stream; beside it the profiler's mean of the same kernel, the
+             clock it ran at and the peak at that clock, from profiles/kernels.json
+             when that file matches the kernel sources
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same case
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
-The *_block workloads time the fused expert block (gate_up -> SwiGLU -> down in
-one call) at prefill and decode shapes; their value is the block's TFLOP/s over
-both projections, next to the two plain GEMMs of the same shapes.
+Other workloads time one configuration's prefill and decode calls (olmoe,
+qwen3, ...), the fused expert block (*_block), the adapter step (olmoe_lora) or
+the W4A8 variant (*_w4a8).
 """
 from __future__ import annotations
 
@@ -74,7 +79,8 @@ BLOCK_WORKLOADS = {
     "qwen3_block": ("qwen3_gate_up_t4096", "qwen3_down_t4096", "qwen3_gate_up_t1", "qwen3_down_t1"),
     "gptoss_block": ("gptoss_gate_up_t2048", "gptoss_down_t2048", "gptoss_gate_up_t1", "gptoss_down_t1"),
 }
-KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip", "route.hip", "w4a8.hip", "lora.hip",
+KERNEL_SOURCES = ["geg_device.hpp", "geg_launch.hpp", "tile.hip", "skinny.hip", "vec.hip", "narrow.hip", "route.hip",
+                  "w4a8.hip", "lora.hip", "util.hip",
                   "geg.cpp"]
 
 
@@ -172,49 +178,57 @@ def time_kernel(fn, copies, steps, warmup, geg, torch, slot, force_path=0):
     return float(np.mean(ms)) if ms else None
 
 
-def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s", w4a8=False):
+def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s", w4a8=False, max_cols=4096):
     """The fp64 oracle (decode each expert to fp64, one matmul per expert) on as
-    many of the case's experts as fit in about budget_s seconds (at least one),
-    as TFLOP/s or, for decode-class cases, packed-weight GB/s. With w4a8, the
-    oracle of that variant: each expert's rows quantised to MXFP8 first (timed
-    with the matmul)."""
+    many of the case's routed experts as fit in about budget_s seconds (at least
+    one), as TFLOP/s or, for decode-class cases, packed-weight GB/s. Experts are
+    packed one at a time as needed (not timed); for a projection wider than
+    max_cols output columns only the first max_cols weight rows of each expert
+    enter the sample (the oracle's rate does not depend on the width). With w4a8,
+    the oracle of that variant: each expert's rows quantised to MXFP8 first
+    (timed with the matmul)."""
     import oracle
     import synthetic
-    from oracle import cases as C
     a_bits, sizes = synthetic.rows_bf16(c, seed)
     off = oracle.offsets(sizes)
-    packed = []
-    for e in range(c.E):                      # input preparation, not timed
-        if sizes[e] == 0:
-            continue
-        if c.fmt == "nf4":
-            packed.append((e, C.nf4_expert(c, seed, e)))
-        else:
-            packed.append((e, synthetic.mxfp4_bytes(c, seed, e)))
-        if len(packed) >= 32:
-            break
+    ncols = min(c.N, max_cols)
+    # distinct experts in the sample: up to 32, fewer for large experts (about
+    # 6e7 packed weights in all, a few seconds of the oracle's packer)
+    distinct = max(1, min(32, int(6e7 // (ncols * c.K))))
+    routed = [e for e in range(c.E) if sizes[e] > 0][:distinct]
+    packed = {}
+
+    def pack(e):                              # input preparation, not timed
+        if e not in packed:
+            if c.fmt == "nf4":
+                packed[e] = oracle.quantize_pack_nf4(synthetic.nf4_weight_f32(c, seed, e, first_rows=ncols))
+            else:
+                q, sc = synthetic.mxfp4_bytes(c, seed, e)
+                packed[e] = (q[:ncols], sc[:ncols])
+        return packed[e]
+
     flops, wbytes, t_dq, t_mm, used = 0.0, 0, 0.0, 0.0, 0
-    t_start = time.perf_counter()
     i = 0
     while True:
-        e, (q, s) = packed[i % len(packed)]
+        e = routed[i % len(routed)]
         i += 1
+        q, s = pack(e)
         t0 = time.perf_counter()
         W = oracle.dequant_nf4(q, s) if c.fmt == "nf4" else oracle.dequant_mxfp4(q, s)
         t1 = time.perf_counter()
         rows = a_bits[off[e]:off[e + 1]]
         if w4a8:
-            out = oracle.w4a8_grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, c.N)
+            out = oracle.w4a8_grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, ncols)
         else:
-            out = oracle.grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, c.N)
+            out = oracle.grouped_ref(rows, np.array([len(rows)], np.int32), lambda _e: W, ncols)
         t2 = time.perf_counter()
         t_dq += t1 - t0
         t_mm += t2 - t1
-        flops += 2.0 * len(rows) * c.N * c.K
-        wbytes += c.N * c.K // 2 + (c.N * (c.K // 64) * 4 if c.fmt == "nf4" else c.N * (c.K // 32))
+        flops += 2.0 * len(rows) * ncols * c.K
+        wbytes += ncols * c.K // 2 + (ncols * (c.K // 64) * 4 if c.fmt == "nf4" else ncols * (c.K // 32))
         used += 1
         del W, out
-        if time.perf_counter() - t_start > budget_s:
+        if t_dq + t_mm > budget_s:
             break
     secs = t_dq + t_mm
     try:
@@ -223,9 +237,10 @@ def cpu_baseline(c, seed, budget_s=12.0, unit="TFLOP/s", w4a8=False):
     except Exception:
         threads = os.cpu_count()
     value = flops / secs / 1e12 if unit == "TFLOP/s" else wbytes / secs / 1e9
+    width = f"the first {ncols} of {c.N} weight rows of each expert" if ncols < c.N else "whole experts"
     return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "sample": f"{c.name}: {used} expert GEMMs (cycling over the first {len(packed)} of "
-                      f"{int(np.count_nonzero(sizes))} routed experts, {int(flops / 2 / c.N / c.K)} rows), "
+            "sample": f"{c.name}: {used} expert GEMMs ({width}; cycling over the first {len(packed)} of "
+                      f"{int(np.count_nonzero(sizes))} routed experts, {int(flops / 2 / ncols / c.K)} rows), "
                       + ("MXFP8 activation quantisation + " if w4a8 else "") + "fp64 decode + numpy matmul",
             "seconds": secs, "dequant_s": t_dq, "matmul_s": t_mm,
             "host_cpus": os.cpu_count()}
@@ -511,13 +526,266 @@ def main_block(args, torch, geg, synthetic):
     print(json.dumps(result), flush=True)
 
 
+HEADLINE_PREFILL = "mixtral_w13_t4096"
+HEADLINE_DGRAD = "mixtral_dgrad_w13"
+HEADLINE_DECODE = ["olmoe_gate_up_t1", "qwen3_gate_up_t1", "qwen3_down_t1", "gptoss_gate_up_t1",
+                   "gptoss_down_t1", "qwen3_gate_up_t64", "qwen3_down_t64"]
+PROFILE_FILE = os.path.join(ROOT, "profiles", "kernels.json")
+
+
+def make_weights(c, seed, torch, geg, dev, experts):
+    """Packed weight stack [E, N, K/2] + scales of case c with the listed experts
+    filled (the kernels read only experts with routed rows; the rest stay zero)."""
+    import synthetic
+    codes = torch.zeros((c.E, c.N, c.K // 2), dtype=torch.uint8, device=dev)
+    if c.fmt == "nf4":
+        scales = torch.zeros((c.E, c.N, c.K // 64), dtype=torch.float32, device=dev)
+    else:
+        scales = torch.zeros((c.E, c.N, c.K // 32), dtype=torch.uint8, device=dev)
+    for e in experts:
+        e = int(e)
+        if c.fmt == "nf4":
+            w = torch.from_numpy(synthetic.nf4_weight_f32(c, seed, e)).to(dev)
+            q, sc = geg.gnf4_quantize(w)
+            del w
+        else:
+            qn, sn = synthetic.mxfp4_bytes(c, seed, e)
+            q, sc = torch.from_numpy(qn).to(dev), torch.from_numpy(sn).to(dev)
+        codes[e].copy_(q)
+        scales[e].copy_(sc)
+    return codes, scales
+
+
+def rotated_copies(tensors):
+    """The stack plus as many clones as make the copies exceed ROTATE_BYTES."""
+    nbytes = sum(t.numel() * t.element_size() for t in tensors)
+    n = max(1, int(np.ceil(ROTATE_BYTES / nbytes)))
+    return [tuple(tensors)] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
+
+
+def host_info():
+    """CPU model, logical CPUs and the BLAS numpy runs the oracle's matmuls on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas": blas}
+
+
+def profile_record(workload, kernel):
+    """The profiler's figures for (workload, kernel) from profiles/kernels.json, if
+    they were taken with the current kernel sources."""
+    try:
+        rec = json.load(open(PROFILE_FILE)).get(f"{workload}:{kernel}")
+    except Exception:
+        return None
+    if rec and rec.get("kernel_sha") == kernel_sha():
+        return rec
+    return None
+
+
+def traffic_record(name):
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(tfile)).get(name)
+    except Exception:
+        return None
+    if rec and rec.get("kernel_sha") == kernel_sha():
+        return rec["hbm_bytes"]
+    return None
+
+
+def copy_floor_ms(nbytes, steps, warmup, torch, dev):
+    """Per-call time of one plain device copy of nbytes (read nbytes, write
+    nbytes), sources rotated like the weight stacks, HIP-graph timed."""
+    n = max(16, (int(nbytes) + 15) // 16 * 16)
+    k = max(2, int(np.ceil(ROTATE_BYTES / n)))
+    srcs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(k)]
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    ms, _ = time_calls(lambda src: dst.copy_(src), srcs, steps, warmup, torch)
+    del srcs, dst
+    return float(np.mean(ms))
+
+
+def main_headline(args, torch, geg, synthetic):
+    dev = torch.device("cuda", 0)
+    cp, cg = synthetic.case(HEADLINE_PREFILL), synthetic.case(HEADLINE_DGRAD)
+    assert (cp.E, cp.K, cp.N, cp.T) == (cg.E, cg.K, cg.N, cg.T), "the dgrad runs on the forward's weights"
+    a_bits, sizes = synthetic.rows_bf16(cp, args.seed)
+    a = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    sz = torch.from_numpy(sizes).to(dev)
+    codes, scales = make_weights(cp, args.seed, torch, geg, dev, np.nonzero(sizes)[0])
+    wcopies = rotated_copies((codes, scales))
+    out = torch.empty((cp.M, cp.N), dtype=torch.bfloat16, device=dev)
+    ws = geg.Workspace(geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, cp.M, cp.N, cp.K, cp.E))
+    dy = torch.from_numpy(synthetic.dgrad_dy_bf16(cg, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    dx = torch.empty((cg.M, cg.K), dtype=torch.bfloat16, device=dev)
+    dws = geg.Workspace(geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, cg.M, cg.N, cg.K, cg.E))
+
+    def fwd(wc, opts=None):
+        geg.gnf4_grouped_gemm(a, sz, wc[0], wc[1], out=out, workspace=ws, opts=opts)
+
+    def dgrad(wc, opts=None):
+        geg.gnf4_grouped_dgrad(dy, sz, wc[0], wc[1], dx=dx, workspace=dws, opts=opts)
+
+    # decode cases: weights of the same model shared across token counts
+    decs = []
+    stacks = {}
+    for name in HEADLINE_DECODE:
+        c = synthetic.case(name)
+        key = (c.fmt, c.E, c.K, c.N)
+        dbits, dsizes = synthetic.rows_bf16(c, args.seed)
+        touched = set(np.nonzero(dsizes)[0].tolist())
+        for other in HEADLINE_DECODE:          # every case of this stack
+            oc = synthetic.case(other)
+            if (oc.fmt, oc.E, oc.K, oc.N) == key:
+                touched |= set(np.nonzero(synthetic.rows_bf16(oc, args.seed)[1])[0].tolist())
+        if key not in stacks:
+            stacks[key] = rotated_copies(make_weights(c, args.seed, torch, geg, dev, sorted(touched)))
+        da = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).to(dev)
+        dsz = torch.from_numpy(dsizes).to(dev)
+        dout = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+        dws_c = geg.Workspace(geg.geg_workspace_bytes(0 if c.fmt == "nf4" else 1, c.M, c.N, c.K, c.E))
+        fn = geg.gnf4_grouped_gemm if c.fmt == "nf4" else geg.gmxfp4_grouped_gemm
+
+        def dec(wc, opts=None, fn=fn, da=da, dsz=dsz, dout=dout, w=dws_c):
+            fn(da, dsz, wc[0], wc[1], out=dout, workspace=w, opts=opts)
+        decs.append((c, dsizes, dec, stacks[key], dws_c))
+
+    # correctness gate before timing: device error words clean
+    fwd(wcopies[0])
+    dgrad(wcopies[0])
+    for c, _, dec, cps, w in decs:
+        dec(cps[0])
+    torch.cuda.synchronize()
+    assert ws.read_error() == 0 and dws.read_error() == 0, "device error word set"
+    for c, _, _, _, w in decs:
+        assert w.read_error() == 0, f"device error word set ({c.name})"
+
+    # ---- timed region: K steps (forward, dgrad, every decode case), wall clock
+    def step(i):
+        fwd(wcopies[i % len(wcopies)])
+        dgrad(wcopies[i % len(wcopies)])
+        for c, _, dec, cps, _ in decs:
+            dec(cps[i % len(cps)])
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    flops = 2.0 * cp.M * cp.N * cp.K
+    # forward call, timed twice (self-pair: the run-to-run noise beside every ratio)
+    f1, how = time_calls(fwd, wcopies, args.steps, args.warmup, torch)
+    f2, _ = time_calls(fwd, wcopies, args.steps, args.warmup, torch)
+    f_ms, f2_ms = float(np.mean(f1)), float(np.mean(f2))
+    fk_ms = time_kernel(fwd, wcopies, args.steps, args.warmup, geg, torch, 0)
+    g1, _ = time_calls(dgrad, wcopies, args.steps, args.warmup, torch)
+    g_ms = float(np.mean(g1))
+    gk_ms = time_kernel(dgrad, wcopies, args.steps, args.warmup, geg, torch, 0)
+
+    def kroof(name, kernel, kms, gflop):
+        ach = gflop * 1e9 / (kms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_MFMA_TFLOPS, 1), "unit": "TFLOP/s",
+             "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "kernel": f"{kernel} (nf4), {name}",
+             "per_launch_gflop": round(gflop, 3), "kernel_ms": round(kms, 5),
+             "timing": f"HIP events around the kernel on its launch stream, mean of {args.steps} back-to-back "
+                       "launches"}
+        prof = profile_record(name, kernel)
+        if prof:
+            pms = prof["mean_us"] * 1e-3
+            r["profile"] = {"kernel_ms": round(pms, 5), "frac": round(gflop * 1e9 / (pms * 1e-3) / 1e12
+                                                                        / PEAK_MFMA_TFLOPS, 4),
+                            "events_over_profile": round(kms / pms, 4), "launches": prof.get("launches"),
+                            "source": prof.get("source")}
+            if prof.get("clock_ghz"):
+                peak_clk = 256 * 4096 * prof["clock_ghz"] * 1e9 / 1e12
+                r["measured_clock"] = {"ghz": prof["clock_ghz"], "peak_at_clock": round(peak_clk, 1),
+                                       "frac_at_clock": round(ach / peak_clk, 4), "source": prof.get("source")}
+            if prof.get("mfma_busy") is not None:
+                r["mfma_busy"] = prof["mfma_busy"]
+        r["traffic"] = traffic_record(name)
+        return r
+
+    rf = kroof(cp.name, "tile_kernel", fk_ms, flops / 1e9)
+    rg = kroof(cg.name, "tile_kernel_dgrad", gk_ms, flops / 1e9)
+
+    # decode legs: each call (HIP graph), its kernels (events), a copy of the same bytes
+    dsteps = max(args.steps, 50)
+    dec_res = {}
+    tot_b, tot_ms = 0, 0.0
+    for c, dsizes, dec, cps, _ in decs:
+        dms, dhow = time_calls(dec, cps, dsteps, args.warmup, torch)
+        d_ms = float(np.mean(dms))
+        kms = time_kernel(dec, cps, dsteps, args.warmup, geg, torch, 1)
+        dbytes = touched_weight_bytes(c, dsizes)
+        cms = copy_floor_ms(dbytes, dsteps, args.warmup, torch, dev)
+        dec_res[c.name] = {"gbps": round(dbytes / (d_ms * 1e-3) / 1e9, 1), "ms": round(d_ms, 5),
+                           "weight_bytes": dbytes, "frac_of_hbm_peak": round(dbytes / (d_ms * 1e-3) / 1e9
+                                                                             / PEAK_HBM_GBPS, 4),
+                           "kernels_ms": round(kms, 5),
+                           "copy_of_same_bytes_ms": round(cms, 5),
+                           "frac_of_copy_time": round(cms / d_ms, 4)}
+        if c.T == 1:
+            tot_b += dbytes
+            tot_ms += d_ms
+    dec_gbps = tot_b / (tot_ms * 1e-3) / 1e9
+
+    roof = max((rf, rg), key=lambda r: r["kernel_ms"])
+    result = {
+        "metric": METRIC, "value": round(flops / (f_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": f"{cp.name} (forward + dgrad) + decode " + ", ".join(HEADLINE_DECODE),
+                   "format": cp.fmt, "E": cp.E, "K": cp.K, "N": cp.N, "prefill_rows": cp.M, "top_k": cp.top_k,
+                   "weight_copies_rotated": len(wcopies)},
+        "prefill": {"ms": round(f_ms, 5), "gflop": flops / 1e9, "tflops": round(flops / (f_ms * 1e-3) / 1e12, 2),
+                    "timing": how, "self_pair_ms": [round(f_ms, 5), round(f2_ms, 5)],
+                    "self_pair_ratio": round(f2_ms / f_ms, 4),
+                    "kernel_ms": round(fk_ms, 5), "kernel_tflops": rf["achieved"],
+                    "frac_of_mfma_peak": round(flops / (f_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        "dgrad": {"workload": cg.name, "ms": round(g_ms, 5), "tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
+                  "kernel_ms": round(gk_ms, 5), "kernel_tflops": rg["achieved"]},
+        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s",
+                   "what": "packed-weight bytes of the five T=1 cases over their summed call times",
+                   "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4), "timing": "hip graph of "
+                   f"{dsteps} calls, 5 replays; copies: torch device copy of the same byte count",
+                   "cases": dec_res},
+        "roofline": roof,
+        "roofline_other": rg if roof is rf else rf,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(cp, args.seed, args.cpu_budget, "TFLOP/s")
+        cb.update(host_info())
+        result["cpu_baseline"] = cb
+    result["kernel_sha"] = kernel_sha()
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="olmoe",
-                    choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS) + sorted(LORA_WORKLOADS))
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline"] + sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS) + sorted(LORA_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -546,6 +814,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.workload == "headline":
+        main_headline(args, torch, geg, synthetic)
+        return
     if args.workload in BLOCK_WORKLOADS:
         main_block(args, torch, geg, synthetic)
         return
@@ -688,6 +959,7 @@ def main():
     result["roofline"] = roof
     if not args.no_cpu_baseline and cp.op == "fwd":
         result["cpu_baseline"] = cpu_baseline(cp, args.seed, args.cpu_budget, result["unit"], w4a8=w4a8)
+        result["cpu_baseline"].update(host_info())
     result["kernel_sha"] = kernel_sha()
     print(json.dumps(result), flush=True)
 

@@ -17,7 +17,7 @@ import re
 import threading
 
 __all__ = [
-    "GegError", "Opts", "Workspace", "lib", "header_functions",
+    "GegError", "GegDeviceError", "Opts", "Workspace", "lib", "header_functions",
     "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad", "gmxfp4_grouped_dgrad",
     "grouped_linear", "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
@@ -41,7 +41,7 @@ DEVERR_BAD_EXPERT_ID, DEVERR_NON_FINITE = 0x8, 0x10
 
 _STATUS = {0: "GEG_OK", 1: "GEG_ERR_NULL_POINTER", 2: "GEG_ERR_BAD_SHAPE", 3: "GEG_ERR_MISALIGNED",
            4: "GEG_ERR_NOT_DEVICE_MEMORY", 5: "GEG_ERR_WORKSPACE", 6: "GEG_ERR_UNSUPPORTED_DEVICE",
-           7: "GEG_ERR_HIP", 8: "GEG_ERR_BAD_OPTION"}
+           7: "GEG_ERR_HIP", 8: "GEG_ERR_BAD_OPTION", 9: "device error word"}
 
 
 class GegError(RuntimeError):
@@ -53,9 +53,24 @@ class GegError(RuntimeError):
 class Opts(ctypes.Structure):
     """geg_opts: force_path 0 auto / 1 skinny / 2 tiled / 3 vector / 4 narrow; split_k 0
     auto / 1..16 (skinny); kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end,
-    decode start/end) recorded around the call's kernels."""
+    decode start/end) recorded around the call's kernels; cu_limit 0, or n > 0 to size every
+    grid for at most n compute units (persistent loops then run more rounds; for tests)."""
     _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("kernel_events", ctypes.c_void_p)]
+                ("kernel_events", ctypes.c_void_p), ("cu_limit", ctypes.c_int32)]
+
+
+class GegDeviceError(GegError):
+    """A call's kernels flagged a condition in the workspace's device error word
+    (GEG_DEVERR_* bits): raised by the wrappers when called with check_errors=True."""
+
+    NAMES = {0x1: "negative sizes[e] (treated as 0)", 0x2: "sum(sizes) > M (rows past M not computed)",
+             0x4: "an fp16 operand overflowed or is not finite", 0x8: "a top-k id outside [0, E) (dropped)",
+             0x10: "a non-finite W4A8 activation"}
+
+    def __init__(self, bits: int):
+        self.bits = bits
+        what = "; ".join(v for k, v in self.NAMES.items() if bits & k) or "unknown bits"
+        super().__init__(9, f"device error word 0x{bits:x}: {what}")
 
 
 _lib = None
@@ -170,6 +185,19 @@ def _check(status: int) -> None:
         raise GegError(status, lib().geg_last_error().decode(errors="replace"))
 
 
+def _check_device_errors(ws, check_errors: bool, stream) -> None:
+    """With check_errors, wait for the call, read the workspace's device error word
+    and raise GegDeviceError if any bit is set (the word is cleared first, so the
+    next call starts clean). Without it, flagged conditions are visible only
+    through Workspace.read_error()."""
+    if not check_errors:
+        return
+    bits = ws.read_error(stream)
+    if bits:
+        ws.reset(stream)
+        raise GegDeviceError(bits)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -265,7 +293,7 @@ def _workspace(ws, need, device, stream):
     return ws
 
 
-def _gemm(fn_name, op, a, sizes, wq, scales, out, workspace, opts, stream):
+def _gemm(fn_name, op, a, sizes, wq, scales, out, workspace, opts, stream, check_errors=False):
     import torch
     M, K = a.shape
     E, N = wq.shape[0], wq.shape[1]
@@ -281,27 +309,34 @@ def _gemm(fn_name, op, a, sizes, wq, scales, out, workspace, opts, stream):
     f = getattr(lib(), fn_name)
     _check(f(_ptr(a), _ptr(sizes), _ptr(wq), _ptr(scales), _ptr(out), M, N, K, E,
              _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None, _stream(stream)))
+    _check_device_errors(ws, check_errors, stream)
     return out
 
 
 def gnf4_grouped_gemm(a, sizes, w, absmax, out=None, workspace: Workspace | None = None,
-                      opts: Opts | None = None, stream=None):
+                      opts: Opts | None = None, stream=None, check_errors: bool = False):
     """a bf16 [M,K] (rows grouped by expert), sizes int32 [E], w uint8 [E,N,K/2],
-    absmax fp32 [E,N,K/64] -> out bf16 [M,N]."""
-    return _gemm("gnf4_grouped_gemm", GEG_OP_NF4_FWD, a, sizes, w, absmax, out, workspace, opts, stream)
+    absmax fp32 [E,N,K/64] -> out bf16 [M,N].
+
+    Conditions the kernels flag on the device (negative sizes, sum(sizes) > M,
+    fp16 overflow on a decode path) are clamped there and recorded in the
+    workspace's error word; check_errors=True waits for the call and raises
+    GegDeviceError when the word is set (the same holds for every wrapper below)."""
+    return _gemm("gnf4_grouped_gemm", GEG_OP_NF4_FWD, a, sizes, w, absmax, out, workspace, opts, stream,
+                 check_errors)
 
 
 def gmxfp4_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace | None = None,
-                        opts: Opts | None = None, stream=None):
+                        opts: Opts | None = None, stream=None, check_errors: bool = False):
     """a bf16 [M,K], sizes int32 [E], blocks uint8 [E,N,K/2] (or [E,N,K/32,16]),
     scales uint8 [E,N,K/32] -> out bf16 [M,N]."""
     if blocks.dim() == 4:
         blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
     return _gemm("gmxfp4_grouped_gemm", GEG_OP_MXFP4_FWD, a, sizes, blocks, scales, out, workspace,
-                 opts, stream)
+                 opts, stream, check_errors)
 
 
-def _dgrad(fn_name, op, dy, sizes, w, scales, dx, workspace, opts, stream):
+def _dgrad(fn_name, op, dy, sizes, w, scales, dx, workspace, opts, stream, check_errors=False):
     import torch
     M, N = dy.shape
     E, K = w.shape[0], w.shape[2] * 2
@@ -317,33 +352,35 @@ def _dgrad(fn_name, op, dy, sizes, w, scales, dx, workspace, opts, stream):
     _check(getattr(lib(), fn_name)(_ptr(dy), _ptr(sizes), _ptr(w), _ptr(scales), _ptr(dx), M, N, K, E,
                                    _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None,
                                    _stream(stream)))
+    _check_device_errors(ws, check_errors, stream)
     return dx
 
 
 def gnf4_grouped_dgrad(dy, sizes, w, absmax, dx=None, workspace: Workspace | None = None,
-                       opts: Opts | None = None, stream=None):
+                       opts: Opts | None = None, stream=None, check_errors: bool = False):
     """dy bf16 [M,N], w uint8 [E,N,K/2], absmax fp32 [E,N,K/64] -> dx bf16 [M,K]."""
-    return _dgrad("gnf4_grouped_dgrad", GEG_OP_NF4_DGRAD, dy, sizes, w, absmax, dx, workspace, opts, stream)
+    return _dgrad("gnf4_grouped_dgrad", GEG_OP_NF4_DGRAD, dy, sizes, w, absmax, dx, workspace, opts, stream,
+                  check_errors)
 
 
 def gmxfp4_grouped_dgrad(dy, sizes, blocks, scales, dx=None, workspace: Workspace | None = None,
-                         opts: Opts | None = None, stream=None):
+                         opts: Opts | None = None, stream=None, check_errors: bool = False):
     """dy bf16 [M,N], blocks uint8 [E,N,K/2], scales uint8 [E,N,K/32] -> dx bf16 [M,K]."""
     if blocks.dim() == 4:
         blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
     return _dgrad("gmxfp4_grouped_dgrad", GEG_OP_MXFP4_DGRAD, dy, sizes, blocks, scales, dx, workspace, opts,
-                  stream)
+                  stream, check_errors)
 
 
 def gmxfp4_w4a8_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace | None = None,
-                             opts: Opts | None = None, stream=None):
+                             opts: Opts | None = None, stream=None, check_errors: bool = False):
     """W4A8: a bf16 [M,K] quantised on the device to MXFP8 (e4m3, one e8m0 scale per
     32 k) times MXFP4 blocks uint8 [E,N,K/2] (or [E,N,K/32,16]) with scales uint8
     [E,N,K/32] on the block-scaled matrix instruction -> out bf16 [M,N]."""
     if blocks.dim() == 4:
         blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
     return _gemm("gmxfp4_w4a8_grouped_gemm", GEG_OP_MXFP4_W4A8, a, sizes, blocks, scales, out, workspace,
-                 opts, stream)
+                 opts, stream, check_errors)
 
 
 def gmxfp8_quantize(a, stream=None):
@@ -370,7 +407,8 @@ def _check_lora(x, sizes, lora_a, lora_b):
     return M, N, K, E, r
 
 
-def _gemm_lora(fmt, a, sizes, w, scales, lora_a, lora_b, scale, out, u, workspace, opts, stream):
+def _gemm_lora(fmt, a, sizes, w, scales, lora_a, lora_b, scale, out, u, workspace, opts, stream,
+               check_errors=False):
     import torch
     M, N, K, E, r = _check_lora(a, sizes, lora_a, lora_b)
     _check_packed(fmt == "nf4", w, scales, E, N, K, "weights", "scales")
@@ -386,27 +424,32 @@ def _gemm_lora(fmt, a, sizes, w, scales, lora_a, lora_b, scale, out, u, workspac
     fn = getattr(lib(), "gnf4_grouped_gemm_lora" if fmt == "nf4" else "gmxfp4_grouped_gemm_lora")
     _check(fn(_ptr(a), _ptr(sizes), _ptr(w), _ptr(scales), _ptr(lora_a), _ptr(lora_b), float(scale), _ptr(out),
               _ptr(u), M, N, K, E, r, _ptr(ws.buf), ws.nbytes, ctypes.byref(opts) if opts else None, _stream(stream)))
+    _check_device_errors(ws, check_errors, stream)
     return out, u
 
 
 def gnf4_grouped_gemm_lora(a, sizes, w, absmax, lora_a, lora_b, scale: float, out=None, u=None,
-                           workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+                           workspace: Workspace | None = None, opts: Opts | None = None, stream=None,
+                           check_errors: bool = False):
     """out = a_e W_e^T + scale (a_e A_e^T) B_e^T per expert, the adapter delta added
     to the fp32 accumulators before the bf16 rounding; lora_a fp32 [E, r, K],
     lora_b fp32 [E, N, r]. Returns (out bf16 [M, N], u = a A_e^T fp32 [M, r])."""
-    return _gemm_lora("nf4", a, sizes, w, absmax, lora_a, lora_b, scale, out, u, workspace, opts, stream)
+    return _gemm_lora("nf4", a, sizes, w, absmax, lora_a, lora_b, scale, out, u, workspace, opts, stream,
+                      check_errors)
 
 
 def gmxfp4_grouped_gemm_lora(a, sizes, blocks, scales, lora_a, lora_b, scale: float, out=None, u=None,
-                             workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+                             workspace: Workspace | None = None, opts: Opts | None = None, stream=None,
+                             check_errors: bool = False):
     """The same on MXFP4 weights (blocks uint8 [E, N, K/2], scales uint8 [E, N, K/32])."""
     if blocks.dim() == 4:
         blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
-    return _gemm_lora("mxfp4", a, sizes, blocks, scales, lora_a, lora_b, scale, out, u, workspace, opts, stream)
+    return _gemm_lora("mxfp4", a, sizes, blocks, scales, lora_a, lora_b, scale, out, u, workspace, opts, stream,
+                      check_errors)
 
 
 def _dgrad_lora(fmt, dy, sizes, w, scales, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b, workspace, opts,
-                stream):
+                stream, check_errors=False):
     import torch
     M, N, K, E, r = _check_lora(x, sizes, lora_a, lora_b)
     _check_packed(fmt == "nf4", w, scales, E, N, K, "weights", "scales")
@@ -428,40 +471,47 @@ def _dgrad_lora(fmt, dy, sizes, w, scales, x, lora_a, lora_b, u, scale, dx, grad
     _check(fn(_ptr(dy), _ptr(sizes), _ptr(w), _ptr(scales), _ptr(x), _ptr(lora_a), _ptr(lora_b), _ptr(u),
               float(scale), _ptr(dx), _ptr(grad_a), _ptr(grad_b), M, N, K, E, r, _ptr(ws.buf), ws.nbytes,
               ctypes.byref(opts) if opts else None, _stream(stream)))
+    _check_device_errors(ws, check_errors, stream)
     return dx, grad_a, grad_b
 
 
 def gnf4_grouped_dgrad_lora(dy, sizes, w, absmax, x, lora_a, lora_b, u, scale: float, dx=None, grad_a=None,
-                            grad_b=None, workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+                            grad_b=None, workspace: Workspace | None = None, opts: Opts | None = None, stream=None,
+                            check_errors: bool = False):
     """Backward of gnf4_grouped_gemm_lora: (dx = dy W_e + scale (dy B_e) A_e bf16
     [M, K], grad_a fp32 [E, r, K], grad_b fp32 [E, N, r])."""
     return _dgrad_lora("nf4", dy, sizes, w, absmax, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b, workspace,
-                       opts, stream)
+                       opts, stream, check_errors)
 
 
 def gmxfp4_grouped_dgrad_lora(dy, sizes, blocks, scales, x, lora_a, lora_b, u, scale: float, dx=None, grad_a=None,
-                              grad_b=None, workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+                              grad_b=None, workspace: Workspace | None = None, opts: Opts | None = None, stream=None,
+                              check_errors: bool = False):
     """The same on MXFP4 weights."""
     if blocks.dim() == 4:
         blocks = blocks.reshape(blocks.shape[0], blocks.shape[1], -1)
     return _dgrad_lora("mxfp4", dy, sizes, blocks, scales, x, lora_a, lora_b, u, scale, dx, grad_a, grad_b,
-                       workspace, opts, stream)
+                       workspace, opts, stream, check_errors)
 
 
-def grouped_linear_lora(a, sizes, w, scales, lora_a, lora_b, scale: float, fmt: str = "nf4"):
+def grouped_linear_lora(a, sizes, w, scales, lora_a, lora_b, scale: float, fmt: str = "nf4",
+                        check_errors: bool = False):
     """The grouped 4-bit projection with a trainable low-rank delta at the
     pre-activation point, as a torch autograd op: out = a_e W_e^T + scale *
     (a_e A_e^T) B_e^T per expert. Backward: dA (through the dgrad kernel and the
-    adapter kernels), d lora_a, d lora_b (fp32); the 4-bit weights are frozen."""
-    return _GroupedLinearLora.apply(a, sizes, w, scales, lora_a, lora_b, float(scale), fmt)
+    adapter kernels), d lora_a, d lora_b (fp32); the 4-bit weights are frozen.
+    check_errors=True makes both directions raise GegDeviceError on a flagged
+    device condition (see gnf4_grouped_gemm)."""
+    return _GroupedLinearLora.apply(a, sizes, w, scales, lora_a, lora_b, float(scale), fmt, bool(check_errors))
 
 
-def grouped_linear(a, sizes, w, scales, fmt: str = "nf4"):
+def grouped_linear(a, sizes, w, scales, fmt: str = "nf4", check_errors: bool = False):
     """The grouped 4-bit GEMM as a differentiable op (torch autograd): out = per
     expert a_e W_e^T; the backward returns dA = per expert dOut_e W_e through the
     library's dgrad kernel on the same packed bytes. The 4-bit weights are frozen
-    (no gradient), as in 4-bit adapter training."""
-    return _GroupedLinear.apply(a, sizes, w, scales, fmt)
+    (no gradient), as in 4-bit adapter training. check_errors=True makes both
+    directions raise GegDeviceError on a flagged device condition."""
+    return _GroupedLinear.apply(a, sizes, w, scales, fmt, bool(check_errors))
 
 
 def _make_grouped_linear():
@@ -469,18 +519,19 @@ def _make_grouped_linear():
 
     class GroupedLinear(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, a, sizes, w, scales, fmt):
+        def forward(ctx, a, sizes, w, scales, fmt, check_errors):
             ctx.save_for_backward(sizes, w, scales)
-            ctx.fmt = fmt
+            ctx.fmt, ctx.check_errors = fmt, check_errors
             fn = gnf4_grouped_gemm if fmt == "nf4" else gmxfp4_grouped_gemm
-            return fn(a, sizes, w, scales)
+            return fn(a, sizes, w, scales, check_errors=check_errors)
 
         @staticmethod
         def backward(ctx, grad_out):
             sizes, w, scales = ctx.saved_tensors
             fn = gnf4_grouped_dgrad if ctx.fmt == "nf4" else gmxfp4_grouped_dgrad
-            da = fn(grad_out.contiguous().to(torch.bfloat16), sizes, w, scales) if ctx.needs_input_grad[0] else None
-            return da, None, None, None, None
+            da = (fn(grad_out.contiguous().to(torch.bfloat16), sizes, w, scales, check_errors=ctx.check_errors)
+                  if ctx.needs_input_grad[0] else None)
+            return da, None, None, None, None, None
 
     return GroupedLinear
 
@@ -490,19 +541,20 @@ def _make_grouped_linear_lora():
 
     class GroupedLinearLora(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, a, sizes, w, scales, lora_a, lora_b, scale, fmt):
+        def forward(ctx, a, sizes, w, scales, lora_a, lora_b, scale, fmt, check_errors):
             fn = gnf4_grouped_gemm_lora if fmt == "nf4" else gmxfp4_grouped_gemm_lora
-            out, u = fn(a, sizes, w, scales, lora_a, lora_b, scale)
+            out, u = fn(a, sizes, w, scales, lora_a, lora_b, scale, check_errors=check_errors)
             ctx.save_for_backward(a, sizes, w, scales, lora_a, lora_b, u)
-            ctx.fmt, ctx.scale = fmt, scale
+            ctx.fmt, ctx.scale, ctx.check_errors = fmt, scale, check_errors
             return out
 
         @staticmethod
         def backward(ctx, grad_out):
             a, sizes, w, scales, lora_a, lora_b, u = ctx.saved_tensors
             fn = gnf4_grouped_dgrad_lora if ctx.fmt == "nf4" else gmxfp4_grouped_dgrad_lora
-            da, ga, gb = fn(grad_out.contiguous(), sizes, w, scales, a, lora_a, lora_b, u, ctx.scale)
-            return (da if ctx.needs_input_grad[0] else None), None, None, None, ga, gb, None, None
+            da, ga, gb = fn(grad_out.contiguous(), sizes, w, scales, a, lora_a, lora_b, u, ctx.scale,
+                            check_errors=ctx.check_errors)
+            return (da if ctx.needs_input_grad[0] else None), None, None, None, ga, gb, None, None, None
 
     return GroupedLinearLora
 
@@ -522,7 +574,7 @@ _GroupedLinear = _LazyFn(_make_grouped_linear)
 _GroupedLinearLora = _LazyFn(_make_grouped_linear_lora)
 
 
-def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream):
+def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream, check_errors=False):
     import torch
     M, H = a.shape
     E, I = w13.shape[0], w13.shape[1] // 2
@@ -540,20 +592,23 @@ def _block(fn_name, op, a, sizes, w13, s13, w2, s2, out, workspace, opts, stream
     _check(getattr(lib(), fn_name)(_ptr(a), _ptr(sizes), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
                                    _ptr(out), M, H, I, E, _ptr(ws.buf), ws.nbytes,
                                    ctypes.byref(opts) if opts else None, _stream(stream)))
+    _check_device_errors(ws, check_errors, stream)
     return out
 
 
 def gnf4_expert_block(a, sizes, w13, absmax13, w2, absmax2, out=None,
-                      workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+                      workspace: Workspace | None = None, opts: Opts | None = None, stream=None,
+                      check_errors: bool = False):
     """Fused SwiGLU expert MLP: a bf16 [M,H], w13 uint8 [E,2I,H/2] (rows 2i gate,
     2i+1 up), absmax13 fp32 [E,2I,H/64], w2 uint8 [E,H,I/2], absmax2 fp32
     [E,H,I/64] -> out bf16 [M,H]."""
     return _block("gnf4_expert_block", GEG_OP_NF4_BLOCK, a, sizes, w13, absmax13, w2, absmax2, out,
-                  workspace, opts, stream)
+                  workspace, opts, stream, check_errors)
 
 
 def gmxfp4_expert_block(a, sizes, blocks13, scales13, blocks2, scales2, out=None,
-                        workspace: Workspace | None = None, opts: Opts | None = None, stream=None):
+                        workspace: Workspace | None = None, opts: Opts | None = None, stream=None,
+                        check_errors: bool = False):
     """The same block on MXFP4: blocks13 uint8 [E,2I,H/2], scales13 uint8
     [E,2I,H/32], blocks2 uint8 [E,H,I/2], scales2 uint8 [E,H,I/32]."""
     if blocks13.dim() == 4:
@@ -561,10 +616,11 @@ def gmxfp4_expert_block(a, sizes, blocks13, scales13, blocks2, scales2, out=None
     if blocks2.dim() == 4:
         blocks2 = blocks2.reshape(blocks2.shape[0], blocks2.shape[1], -1)
     return _block("gmxfp4_expert_block", GEG_OP_MXFP4_BLOCK, a, sizes, blocks13, scales13, blocks2,
-                  scales2, out, workspace, opts, stream)
+                  scales2, out, workspace, opts, stream, check_errors)
 
 
-def route_sort(topk_ids, E: int, x=None, workspace: Workspace | None = None, stream=None):
+def route_sort(topk_ids, E: int, x=None, workspace: Workspace | None = None, stream=None,
+               check_errors: bool = False):
     """Device-side routing sort of topk_ids int32 [T, k] over E experts.
 
     Returns (sizes int32 [E], row_of int32 [T*k], src_of int32 [T*k], x_sorted):
@@ -589,6 +645,7 @@ def route_sort(topk_ids, E: int, x=None, workspace: Workspace | None = None, str
     ws = _workspace(workspace, need, dev, stream)
     _check(lib().geg_route_sort(_ptr(topk_ids), T, k, E, _ptr(x), H, _ptr(sizes), _ptr(row_of),
                                 _ptr(src_of), _ptr(xs), _ptr(ws.buf), ws.nbytes, _stream(stream)))
+    _check_device_errors(ws, check_errors, stream)
     return sizes, row_of, src_of, xs
 
 

@@ -76,7 +76,18 @@ geg_status check_device_ptr(const void* p, const char* name) {
   return GEG_OK;
 }
 
-// Compute units of the current device (256 on MI355X when it cannot be queried).
+// geg_opts.cu_limit of the entry point running on this thread (0: none).
+thread_local int g_cu_limit = 0;
+
+// Sets the launch-sizing limit for the duration of one entry point call.
+struct CuScope {
+  int prev;
+  explicit CuScope(const geg_opts* o) : prev(g_cu_limit) { g_cu_limit = (o && o->cu_limit > 0) ? o->cu_limit : 0; }
+  ~CuScope() { g_cu_limit = prev; }
+};
+
+// Compute units that launches are sized for: the current device's (256 on
+// MI355X when it cannot be queried), or fewer under geg_opts.cu_limit.
 int cu_count() {
   static int cus = 0;
   if (cus == 0) {
@@ -86,7 +97,7 @@ int cu_count() {
       cus = prop.multiProcessorCount;
     if (cus <= 0) cus = 256;
   }
-  return cus;
+  return g_cu_limit > 0 ? std::min(cus, g_cu_limit) : cus;
 }
 
 // Record entry i of the caller's kernel timing events, if any.
@@ -107,7 +118,8 @@ struct Plan {
   int64_t rc_bound;        // bound on skinny row chunks
   size_t counters_off, counters_bytes;
   size_t partials_off, partials_bytes;
-  size_t a16_off, a16_bytes;   // NF4 tile path: fp16 copy of the activations
+  size_t a16_off, a16_bytes;   // NF4 tile path: fp16 copy of the row-scaled activations
+  size_t rexp_off;             // ... followed by the rows' int32 exponents
   size_t total_bytes;
 };
 
@@ -126,13 +138,16 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
   const int32_t split_req = o ? o->split_k : 0;
   if (force < 0 || force > 4) return fail(GEG_ERR_BAD_OPTION, "force_path must be 0..4");
   if (split_req < 0 || split_req > 16) return fail(GEG_ERR_BAD_OPTION, "split_k must be 0..16");
+  if (o && o->cu_limit < 0) return fail(GEG_ERR_BAD_OPTION, "cu_limit must be >= 0");
   std::memset(&p, 0, sizeof(p));
   p.split = 1;
   if (op == GEG_OP_NF4_DGRAD) {
-    // dY as fp16 for the tiled kernel, outside the counter region
+    // row-scaled dY as fp16 for the tiled kernel and the rows' exponents,
+    // outside the counter region
     p.run_tile = M > 0;
     p.a16_off = kHeader + kCounterBytes;
-    p.a16_bytes = round256((size_t)M * (size_t)N * 2);
+    p.a16_bytes = round256((size_t)M * (size_t)N * 2) + round256((size_t)M * 4);
+    p.rexp_off = p.a16_off + round256((size_t)M * (size_t)N * 2);
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
@@ -207,7 +222,8 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     // Never inside the counter region, even when this call has no split-K: a
     // later split-K call on the same workspace expects its counters at zero.
     p.a16_off = kHeader + kCounterBytes + p.partials_bytes;
-    p.a16_bytes = round256((size_t)M * (size_t)K * 2);
+    p.a16_bytes = round256((size_t)M * (size_t)K * 2) + round256((size_t)M * 4);
+    p.rexp_off = p.a16_off + round256((size_t)M * (size_t)K * 2);
     p.total_bytes = p.a16_off + p.a16_bytes;
   }
   return GEG_OK;
@@ -218,12 +234,22 @@ int persistent_grid(int64_t units_bound, int per_cu) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(units_bound, cap));
 }
 
+// Largest byte range one buffer resource of a kernel may cover.
+constexpr int64_t kMaxWindow = 0x7FFFFFF0;
+
 geg_status check_shape(int64_t M, int64_t N, int64_t K, int32_t E, int64_t kmult) {
   if (M < 0 || N <= 0 || K <= 0 || E <= 0)
     return fail(GEG_ERR_BAD_SHAPE, "need M >= 0, N > 0, K > 0, E > 0");
   if (E > geg::kMaxExperts) return fail(GEG_ERR_BAD_SHAPE, "E exceeds 1024 experts");
   if (M >= (int64_t)INT32_MAX) return fail(GEG_ERR_BAD_SHAPE, "M must be below 2^31");
   if (K % kmult) return fail(GEG_ERR_BAD_SHAPE, "K must be a multiple of " + std::to_string(kmult));
+  // The kernels read one expert's packed weights, and at most 256 rows of an
+  // activation / dY / output tensor, through 32-bit buffer windows. Refuse
+  // shapes whose windows would not fit instead of clamping them.
+  if (512 * std::max(N, K) > kMaxWindow)
+    return fail(GEG_ERR_BAD_SHAPE, "256 rows of N or K bf16 values must fit in 0x7FFFFFF0 bytes (N, K <= 4194303)");
+  if (N * (K / 2) > kMaxWindow)
+    return fail(GEG_ERR_BAD_SHAPE, "an expert's packed weights (N * K / 2 bytes) must not exceed 0x7FFFFFF0 bytes");
   return GEG_OK;
 }
 
@@ -243,6 +269,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
                        const void* scales, void* out, int64_t M, int64_t N, int64_t K, int32_t E,
                        void* ws, size_t ws_bytes, const geg_opts* opts, hipStream_t stream,
                        int32_t glu = 0, const LoraIn& lora = LoraIn{}) {
+  CuScope cu_scope(opts);
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
   if (glu && (N % 2)) return fail(GEG_ERR_BAD_SHAPE, "the fused gate/up width must be even");
@@ -290,6 +317,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
+  g.rexp = p.a16_bytes ? reinterpret_cast<const int32_t*>(wsb + p.rexp_off) : nullptr;
   g.glu = glu;
   g.lora_u = lora.u;
   g.lora_q = lora.q;
@@ -302,7 +330,8 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
 
   if (p.run_tile) {
     if (fmt == geg::NF4) {
-      hipError_t e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * K, g.err, stream);
+      hipError_t e = geg::launch_to_f16_rows(g.a, const_cast<uint16_t*>(g.a16), const_cast<int32_t*>(g.rexp), M, K,
+                                             g.err, cu_count(), stream);
       if (e != hipSuccess) return hip_fail(e, "activation conversion launch");
       ++g_launches;
     }
@@ -360,6 +389,7 @@ geg_status block_common(int fmt, const void* a, const int32_t* sizes, const uint
                         const void* s13, const uint8_t* w2, const void* s2, void* out, int64_t M,
                         int64_t H, int64_t I, int32_t E, void* ws, size_t ws_bytes,
                         const geg_opts* opts, hipStream_t stream) {
+  CuScope cu_scope(opts);
   const int64_t kmult = fmt == geg::NF4 ? 64 : 32;
   geg_status st;
   if ((st = check_shape(M, 2 * I, H, E, kmult)) != GEG_OK) return st;
@@ -396,6 +426,7 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
                         void* dx, int64_t M, int64_t N, int64_t K, int32_t E, void* workspace,
                         size_t workspace_bytes, const geg_opts* opts, hipStream_t stream,
                         const LoraIn& lora = LoraIn{}) {
+  CuScope cu_scope(opts);
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
   if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");
@@ -419,6 +450,7 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
   std::memset(&g, 0, sizeof(g));
   g.a = reinterpret_cast<const uint16_t*>(dy);
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
+  g.rexp = p.a16_bytes ? reinterpret_cast<const int32_t*>(wsb + p.rexp_off) : nullptr;
   g.sizes = sizes;
   g.wq = w;
   g.scales = absmax;
@@ -437,7 +469,8 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
   hipError_t e = hipSuccess;
   if (lora.pre && (e = lora.pre()) != hipSuccess) return hip_fail(e, "adapter launch");
   if (fmt == geg::NF4) {
-    e = geg::launch_to_f16_slots(g.a, const_cast<uint16_t*>(g.a16), M * N, g.err, stream);
+    e = geg::launch_to_f16_rows(g.a, const_cast<uint16_t*>(g.a16), const_cast<int32_t*>(g.rexp), M, N, g.err,
+                                cu_count(), stream);
     if (e != hipSuccess) return hip_fail(e, "dY conversion launch");
     ++g_launches;
   }
@@ -509,10 +542,14 @@ geg_status gmxfp4_w4a8_grouped_gemm(const void* a, const int32_t* sizes, const u
                                     const uint8_t* scales, void* out, int64_t M, int64_t N, int64_t K,
                                     int32_t E, void* workspace, size_t workspace_bytes,
                                     const geg_opts* opts, hipStream_t stream) {
+  CuScope cu_scope(opts);
   geg_status st = check_shape(M, N, K, E, 32);
   if (st != GEG_OK) return st;
   // 32-bit buffer offsets within a 256-row tile of activation codes
   if (K >= (int64_t)1 << 23) return fail(GEG_ERR_BAD_SHAPE, "K must be below 2^23");
+  // the activation scales are read through one window: ceil(K / 128) steps of M rows of 4 bytes
+  if ((K + 127) / 128 * M * 4 > kMaxWindow)
+    return fail(GEG_ERR_BAD_SHAPE, "the activation scales (ceil(K/128) * M * 4 bytes) must fit in 0x7FFFFFF0 bytes");
   Plan p;
   if ((st = make_plan(GEG_OP_MXFP4_W4A8, M, N, K, E, opts, p)) != GEG_OK) return st;
   if (M == 0) return GEG_OK;
@@ -595,6 +632,7 @@ geg_status gemm_lora(int fmt, const void* a, const int32_t* sizes, const uint8_t
                      const float* lora_a, const float* lora_b, float scale, void* out, void* u, int64_t M, int64_t N,
                      int64_t K, int32_t E, int32_t r, void* workspace, size_t workspace_bytes, const geg_opts* opts,
                      hipStream_t stream) {
+  CuScope cu_scope(opts);
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
   if (M == 0) return GEG_OK;
@@ -621,6 +659,7 @@ geg_status dgrad_lora(int fmt, const void* dy, const int32_t* sizes, const uint8
                       const void* x, const float* lora_a, const float* lora_b, const void* u, float scale, void* dx,
                       float* grad_a, float* grad_b, int64_t M, int64_t N, int64_t K, int32_t E, int32_t r,
                       void* workspace, size_t workspace_bytes, const geg_opts* opts, hipStream_t stream) {
+  CuScope cu_scope(opts);
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
   if (N % 8) return fail(GEG_ERR_BAD_SHAPE, "dgrad needs N % 8 == 0");

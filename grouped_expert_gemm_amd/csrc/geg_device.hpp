@@ -465,6 +465,53 @@ __device__ int32_t build_plan(int32_t* off, int32_t* upre, const int32_t* __rest
   return upre[E];
 }
 
+// Two work lists in one scan: units(size, c) gives expert e's units of class c
+// (0 or 1); upre0 / upre1 receive the exclusive prefix of each class over the
+// experts. The tiled kernel runs every class-0 unit before any class-1 unit.
+// Returns the class-0 total; upre1[E] holds the class-1 total.
+template <typename UnitFn>
+__device__ int32_t build_plan2(int32_t* off, int32_t* upre0, int32_t* upre1, const int32_t* __restrict__ sizes,
+                               int E, int64_t M, uint32_t* err_word, UnitFn units) {
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const int lane = t;
+    const uint32_t m = (uint32_t)M;
+    uint32_t run = 0, urun0 = 0, urun1 = 0, err = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      int32_t raw = e < E ? sizes[e] : 0;
+      if (raw < 0) {
+        err |= kErrNegativeSize;
+        raw = 0;
+      }
+      const uint32_t s = min((uint32_t)raw, m + 1u);
+      const uint32_t incl = __builtin_elementwise_add_sat(wave_scan_sat(s), run);
+      const uint32_t lo = min(incl - s, m), hi = min(incl, m);
+      const uint32_t u0 = e < E ? (uint32_t)units((int32_t)(hi - lo), 0) : 0u;
+      const uint32_t u1 = e < E ? (uint32_t)units((int32_t)(hi - lo), 1) : 0u;
+      const uint32_t i0 = wave_scan_sat(u0) + urun0;
+      const uint32_t i1 = wave_scan_sat(u1) + urun1;
+      if (e < E) {
+        off[e] = (int32_t)lo;
+        upre0[e] = (int32_t)(i0 - u0);
+        upre1[e] = (int32_t)(i1 - u1);
+      }
+      run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      urun0 = (uint32_t)__builtin_amdgcn_readlane((int)i0, 63);
+      urun1 = (uint32_t)__builtin_amdgcn_readlane((int)i1, 63);
+    }
+    if (lane == 0) {
+      off[E] = (int32_t)min(run, m);
+      upre0[E] = (int32_t)urun0;
+      upre1[E] = (int32_t)urun1;
+      if (run > m) err |= kErrSizesExceedM;
+    }
+    if (err) atomicOr(err_word, err);
+  }
+  __syncthreads();
+  return upre0[E];
+}
+
 template <typename UnitFn, typename Overlap = NoOverlap>
 __device__ int32_t build_plan(Plan& p, const int32_t* __restrict__ sizes, int E, int64_t M,
                               uint32_t* err_word, UnitFn units, Overlap overlap = Overlap{}) {

@@ -41,8 +41,9 @@ constexpr int kTileN = 256;
 
 struct GemmArgs {
   const uint16_t* a;      // bf16 [M, K]
-  const uint16_t* a16;    // NF4 tile path: the same activations as fp16 in NF4 slot order
-                          // (dgrad: dY [M, N] as fp16 in NF4 slot order)
+  const uint16_t* a16;    // NF4 tile path: the activations as fp16 in NF4 slot order, each
+                          // row multiplied by 2^-rexp[row] (dgrad: dY [M, N] likewise)
+  const int32_t* rexp;    // NF4 tile path: per-row exponents; row results are multiplied by 2^rexp
   const int32_t* sizes;   // [E]
   const uint8_t* wq;      // packed codes [E, N, K/2]
   const void* scales;     // NF4: fp32 [E, N, K/64]; MXFP4: u8 [E, N, K/32]
@@ -105,7 +106,10 @@ hipError_t launch_lora_transpose(const float* in, int64_t E, int64_t P, int64_t 
                                  hipStream_t st);
 hipError_t launch_route_combine(const uint16_t* y, int64_t N, const int32_t* row_of, const float* w, int64_t T,
                                 int32_t k, uint16_t* out, int cus, hipStream_t s);
-hipError_t launch_to_f16_slots(const uint16_t* a, uint16_t* a16, int64_t elems, uint32_t* err,
-                               hipStream_t s);
+// Row-scaled fp16 copy of bf16 [M, C] rows (C % 8 == 0) in the NF4 slot order:
+// a16[r] = fp16(a[r] * 2^-rexp[r]) with the row's largest magnitude scaled into
+// [2^14, 2^15); a non-finite element flags kErrFp16Range.
+hipError_t launch_to_f16_rows(const uint16_t* a, uint16_t* a16, int32_t* rexp, int64_t M, int64_t C,
+                              uint32_t* err, int cus, hipStream_t s);
 
 }  // namespace geg

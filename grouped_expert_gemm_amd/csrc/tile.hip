@@ -2,7 +2,7 @@
 //
 // One persistent launch walks every 256x256 output tile of every expert that has
 // more rows than the skinny path takes. Per 64-wide K stage a workgroup stages
-// its activation tile (NF4: from the fp16 copy a prior pass made) and decodes
+// its activation tile (NF4: from the row-scaled fp16 copy a prior pass made) and decodes
 // its 256 weight rows once into LDS: codes through the 16-value table, times the
 // block scale, so the decode is shared by all 256 rows of the tile
 // ("grouped-nf4-gemm 0.33.1", opening description: table decode in registers,
@@ -408,8 +408,13 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+#ifndef GEG_TILE_BARRIER_X
+#define GEG_TILE_BARRIER_X 1
+#endif
+#if GEG_TILE_BARRIER_X
   // X: every wavefront is done with the current buffers.
   __syncthreads();
+#endif
 }
 
 // Main loop over the K stages of one tile (H = the wavefront's active 64-row
@@ -467,6 +472,9 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
       tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff,
                                     m4, base);
   }
+#if !GEG_TILE_BARRIER_X
+  __syncthreads();   // the epilogue reuses the stage buffers
+#endif
 }
 
 // Forward (DG = false): out[M, N] = a . W^T per expert. dgrad (DG = true):
@@ -474,19 +482,32 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
 // MXFP4 reads the bf16 dY directly).
 // TAIL: the contraction length is not a multiple of 64, so the last stage's
 // activation chunks past it must be zeroed (MXFP4 K, dgrad N).
+//
+// Work order. An expert's rows split into full 256-row blocks and a remainder
+// block. A tile's cost follows the MFMA work of its 64-row halves while its
+// weight decode is the same for any row count, so a remainder of up to 128 rows
+// costs half a full tile or less. Class 0 (every full block, and remainders of
+// more than 128 rows) comes first, expert by expert; class 1 (the smaller
+// remainders) follows, so the persistent rounds end on the cheapest tiles
+// instead of leaving whole tiles for a last, mostly idle round.
 template <Fmt F, bool DG, bool TAIL>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
-  __shared__ Plan plan;
+  __shared__ int32_t p_off[kMaxExperts + 1];
+  __shared__ int32_t p_u0[kMaxExperts + 1];
+  __shared__ int32_t p_u1[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) TileLds<DG> L;
 
   const int64_t C = DG ? g.N : g.K;   // contraction length
   const int64_t O = DG ? g.K : g.N;   // output width
   const int n_tiles = (int)((O + BN - 1) / BN);
   const int32_t thresh = g.thresh;
-  const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
+  const int32_t total0 = build_plan2(p_off, p_u0, p_u1, g.sizes, g.E, g.M, g.err, [&](int32_t s, int c) -> int32_t {
     if (s <= thresh) return 0;
-    return ((s + BM - 1) / BM) * n_tiles;
+    const int32_t full = s / BM, rem = s % BM;
+    if (c == 0) return (full + (rem > BM / 2 ? 1 : 0)) * n_tiles;
+    return rem > 0 && rem <= BM / 2 ? n_tiles : 0;
   });
+  const int32_t total = total0 + p_u1[g.E];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -501,11 +522,20 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   for (int32_t base = 0; base < total; base += G) {
     const int32_t u = base + slot;
     if (u >= total) break;
-    const int e = find_expert(plan, g.E, u);
-    const int32_t lu = u - plan.upre[e];
-    const int mt = lu / n_tiles, nt = lu % n_tiles;
-    const int64_t row0 = (int64_t)plan.off[e] + (int64_t)mt * BM;
-    const int rows = min(BM, (int)(plan.off[e + 1] - row0));
+    int e, mt, nt;
+    if (u < total0) {
+      e = find_expert(p_u0, g.E, u);
+      const int32_t lu = u - p_u0[e];
+      mt = lu / n_tiles;
+      nt = lu % n_tiles;
+    } else {
+      const int32_t u1 = u - total0;
+      e = find_expert(p_u1, g.E, u1);
+      mt = (p_off[e + 1] - p_off[e]) / BM;   // the remainder block
+      nt = u1 - p_u1[e];
+    }
+    const int64_t row0 = (int64_t)p_off[e] + (int64_t)mt * BM;
+    const int rows = min(BM, (int)(p_off[e + 1] - row0));
     const int64_t n0 = (int64_t)nt * BN;
 
     f32x4 acc[8][4];
@@ -522,6 +552,25 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       run_tile_h<F, DG, TAIL, 1>(L, src, C, g.K, wave, lane, acc);
     else
       run_tile_h<F, DG, TAIL, 0>(L, src, C, g.K, wave, lane, acc);
+
+    if constexpr (F == NF4) {
+      // The fp16 operand rows were multiplied by 2^-rexp[row] (exact); multiply
+      // the rows' fp32 results by 2^rexp[row] (exact) before anything else.
+      // acc[i][j][q] is row 16 i + 4 (lane / 16) + q of the wavefront's block;
+      // rows past the expert read 0 and are never stored.
+      const int brows = max(0, rows - 128 * wm);
+      const __amdgpu_buffer_rsrc_t RE = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(g.rexp + row0 + 128 * wm), (short)0, brows * 4, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ex = (int)__builtin_amdgcn_raw_buffer_load_b32(RE, (uint32_t)((16 * i + 4 * (lane >> 4) + q) * 4),
+                                                                   0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j][q] = __builtin_amdgcn_ldexpf(acc[i][j][q], ex);
+        }
+    }
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores

@@ -1,4 +1,6 @@
 // Auxiliary kernels: dequantisation exports, the NF4 packer, workspace zeroing.
+#include <algorithm>
+
 #include "geg_device.hpp"
 #include "geg_launch.hpp"
 
@@ -122,18 +124,97 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(uint32_t* __restrict__ p
     p[i] = 0u;
 }
 
-// bf16 activations -> fp16 in the NF4 slot order, 8 elements (16 bytes) per step.
-// The NF4 MFMA consumes fp16 activations; converting them once here, instead of
-// in every output-column tile that reads them, leaves the tile kernel a plain
-// copy. An element that overflows fp16 sets the range bit of the error word.
-__global__ __launch_bounds__(kThreads) void to_f16_kernel(const u32x4* __restrict__ a,
-                                                          u32x4* __restrict__ a16, int64_t chunks,
-                                                          uint32_t* __restrict__ err) {
-  uint32_t range = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks;
-       i += (int64_t)gridDim.x * kThreads)
-    a16[i] = bf16x8_to_f16_slots(a[i], range);
-  if (range_overflowed(range)) atomicOr(err, kErrFp16Range);
+// Row-scaled fp16 copy of bf16 rows for the NF4 tiled path. The NF4 MFMA takes
+// fp16 operands, whose exponent range is far narrower than bf16's: activation
+// gradients of 1e-6 and below would fall into fp16's subnormals or flush to
+// zero, and values above 65504 would overflow. Each row is therefore multiplied
+// by the power of two 2^-rexp[r] that puts its largest magnitude in [2^14, 2^15)
+// before the conversion, and the tiled kernel multiplies the row's fp32 results
+// by 2^rexp[r] before their bf16 rounding. Both multiplications are exact, so
+// a row's result is what unbounded fp16 range would give. Converting once here
+// rather than in every output-column tile that reads a row leaves the tiled
+// kernel a plain copy of the operand.
+//
+// One row per TP = 2^tp_log2 lanes of a wavefront (64 / TP rows per wavefront);
+// lane j of a row's group takes the row's 16-byte chunks j, j + TP, ... With
+// CPL > 0 each lane holds its (at most CPL) chunks in registers between the
+// maximum and the conversion; CPL == 0 reads them again (longer rows).
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void to_f16_rows_kernel(const u32x4* __restrict__ a, u32x4* __restrict__ a16,
+                                                               int32_t* __restrict__ rexp, int64_t M,
+                                                               int64_t chunks, int tp_log2,
+                                                               uint32_t* __restrict__ err) {
+  const int lane = threadIdx.x & 63;
+  const int TP = 1 << tp_log2;
+  const int sub = lane & (TP - 1);
+  const int rows_per_wave = 64 >> tp_log2;
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / 64) * rows_per_wave;
+  uint32_t bad = 0;
+  for (int64_t r0 = wave * rows_per_wave; r0 < M; r0 += stride) {
+    const int64_t row = r0 + (lane >> tp_log2);
+    const bool live = row < M;
+    const u32x4* src = a + row * chunks;
+    u32x4* dst = a16 + row * chunks;
+    // largest |x| of the row as bf16 magnitude bits (ordered like the values;
+    // 0x7F80 and above are inf and NaN)
+    uint32_t mx = 0;
+    u32x4 v[CPL > 0 ? CPL : 1];
+    auto absmax8 = [](const u32x4& x, uint32_t m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, max(x[i] & 0x7FFFu, (x[i] >> 16) & 0x7FFFu));
+      return m;
+    };
+    if constexpr (CPL > 0) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int64_t j = sub + (int64_t)i * TP;
+        v[i] = (live && j < chunks) ? src[j] : u32x4{0u, 0u, 0u, 0u};
+        mx = absmax8(v[i], mx);
+      }
+    } else if (live) {
+      for (int64_t j = sub; j < chunks; j += TP) mx = absmax8(src[j], mx);
+    }
+    for (int o = TP >> 1; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    // exponent of the largest magnitude: floor(log2 |x|)
+    int ex = 0;
+    if (mx >= 0x7F80u) {
+      bad = 1;   // inf or NaN: converted unscaled, flagged
+    } else if (mx >= 0x80u) {
+      ex = (int)(mx >> 7) - 127 - 14;
+    } else if (mx > 0u) {
+      ex = (31 - __builtin_clz(mx)) - 133 - 14;   // bf16 subnormal: mantissa * 2^-133
+    }
+    if (live && sub == 0) rexp[row] = ex;
+    auto conv = [ex](const u32x4& x) {
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, x[i] << 16), -ex);
+        f[2 * i + 1] = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, x[i] & 0xFFFF0000u), -ex);
+      }
+      constexpr int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};   // the NF4 slot order
+      u32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x2 h;
+        h[0] = (_Float16)f[order[2 * i]];
+        h[1] = (_Float16)f[order[2 * i + 1]];
+        r[i] = __builtin_bit_cast(uint32_t, h);
+      }
+      return r;
+    };
+    if constexpr (CPL > 0) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int64_t j = sub + (int64_t)i * TP;
+        if (live && j < chunks) dst[j] = conv(v[i]);
+      }
+    } else if (live) {
+      for (int64_t j = sub; j < chunks; j += TP) dst[j] = conv(src[j]);
+    }
+  }
+  if (bad) atomicOr(err, kErrFp16Range);
 }
 
 int grid_for(int64_t work) {
@@ -162,13 +243,33 @@ hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, in
   return hipGetLastError();
 }
 
-hipError_t launch_to_f16_slots(const uint16_t* a, uint16_t* a16, int64_t elems, uint32_t* err,
-                               hipStream_t s) {
-  const int64_t chunks = elems >> 3;
-  int64_t g = (chunks + kThreads - 1) / kThreads;
-  g = g < 1 ? 1 : (g > 2048 ? 2048 : g);
-  hipLaunchKernelGGL(to_f16_kernel, dim3((int)g), dim3(kThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(a), reinterpret_cast<u32x4*>(a16), chunks, err);
+hipError_t launch_to_f16_rows(const uint16_t* a, uint16_t* a16, int32_t* rexp, int64_t M, int64_t C,
+                              uint32_t* err, int cus, hipStream_t s) {
+  const int64_t chunks = C >> 3;
+  int tp_log2 = 0;
+  while (tp_log2 < 6 && ((int64_t)1 << tp_log2) < chunks) ++tp_log2;
+  const int64_t per_lane = (chunks + (1 << tp_log2) - 1) >> tp_log2;
+  const int64_t rows_per_block = (kThreads / 64) * (64 >> tp_log2);
+  int64_t grid = (M + rows_per_block - 1) / rows_per_block;
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)cus * 16));
+  const u32x4* src = reinterpret_cast<const u32x4*>(a);
+  u32x4* dst = reinterpret_cast<u32x4*>(a16);
+#define GEG_TO_F16(CPL)                                                                                        \
+  hipLaunchKernelGGL(to_f16_rows_kernel<CPL>, dim3((int)grid), dim3(kThreads), 0, s, src, dst, rexp, M, chunks, \
+                     tp_log2, err)
+  if (per_lane <= 1)
+    GEG_TO_F16(1);
+  else if (per_lane <= 2)
+    GEG_TO_F16(2);
+  else if (per_lane <= 4)
+    GEG_TO_F16(4);
+  else if (per_lane <= 8)
+    GEG_TO_F16(8);
+  else if (per_lane <= 16)
+    GEG_TO_F16(16);
+  else
+    GEG_TO_F16(0);
+#undef GEG_TO_F16
   return hipGetLastError();
 }
 

@@ -40,18 +40,32 @@
  *    (negative -> 0, prefix sums clamped to M; no access outside rows [0, M))
  *    and OR a bit into the workspace's device error word (GEG_DEVERR_*).
  *  - Numerics: fp32 accumulation, bf16 output rounded to nearest even. NF4
- *    multiplies fp16 operands (activations converted from bf16; exact for
- *    2^-14 <= |x| <= 65504, an activation that overflows fp16 sets
- *    GEG_DEVERR_FP16_RANGE); MXFP4 multiplies bf16 operands (e2m1 * 2^k is exact
- *    in bf16 for normal results). Results are bitwise reproducible run to run.
+ *    multiplies fp16 operands. On the tiled path (prefill and every dgrad) each
+ *    activation row (dgrad: each dY row) is first multiplied by a power of two
+ *    that puts its largest magnitude in [2^14, 2^15), converted to fp16, and the
+ *    row's fp32 results are multiplied back by the inverse power before the bf16
+ *    rounding: both steps are exact, so no row under- or overflows fp16 whatever
+ *    its scale (elements below 2^-29 of their row's largest lose precision);
+ *    a non-finite element sets GEG_DEVERR_FP16_RANGE. The decode paths (vector,
+ *    narrow, skinny) convert bf16 -> fp16 directly (exact for 2^-14 <= |x| <=
+ *    65504; an activation that overflows fp16 sets GEG_DEVERR_FP16_RANGE).
+ *    MXFP4 multiplies bf16 operands (e2m1 * 2^k is exact in bf16 for normal
+ *    results). Results are bitwise reproducible run to run.
+ *  - Sizes: every kernel addresses one expert's packed weights, and at most 256
+ *    rows of an activation, dY or output tensor, through 32-bit buffer windows,
+ *    so a call is refused with GEG_ERR_BAD_SHAPE (nothing is clamped) unless
+ *    N * K / 2 <= 0x7FFFFFF0 and 512 * max(N, K) <= 0x7FFFFFF0. M itself may
+ *    exceed 2^31 / K (the tensors are addressed with 64-bit row offsets); M must
+ *    be below 2^31.
  *  - Workspace: `workspace` is a caller-allocated device buffer of at least
  *    geg_workspace_bytes(...) bytes, 256-byte aligned, zeroed once by
  *    geg_workspace_init before its first use. It holds the device error word,
  *    split-K arrival counters (a fixed 4 MiB region after the 256-byte header,
  *    left zeroed by every completed call, and never written by any other op,
  *    so one workspace can serve every entry point), split-K partials and, for
- *    the NF4 tiled path, an fp16 copy of the activations (M * K * 2 bytes;
- *    dgrad: of dY, M * N * 2 bytes; rewritten by every call); every op's other
+ *    the NF4 tiled path, an fp16 copy of the row-scaled activations (M * K * 2
+ *    bytes; dgrad: of dY, M * N * 2 bytes) and the rows' int32 exponents (M * 4
+ *    bytes), both rewritten by every call; every op's other
  *    scratch also lies past the counter region; calls
  *    on one workspace must be ordered (same stream); concurrent calls must not
  *    share one.
@@ -67,12 +81,13 @@
 extern "C" {
 #endif
 
-#define GEG_VERSION 100 /* 1.0.0 */
+#define GEG_VERSION 110 /* 1.1.0 */
 
 typedef enum {
   GEG_OK = 0,
   GEG_ERR_NULL_POINTER = 1,       /* a required pointer is NULL (when M > 0)                     */
-  GEG_ERR_BAD_SHAPE = 2,          /* M < 0, N <= 0, K <= 0, E <= 0, K % 64 (NF4) or % 32 (MXFP4) */
+  GEG_ERR_BAD_SHAPE = 2,          /* M < 0, N <= 0, K <= 0, E <= 0, K % 64 (NF4) or % 32 (MXFP4),
+                                     a buffer window past 0x7FFFFFF0 bytes (see Sizes)            */
   GEG_ERR_MISALIGNED = 3,         /* a, w/blocks, out, dy, dx not 16-byte aligned                */
   GEG_ERR_NOT_DEVICE_MEMORY = 4,  /* a host pointer was passed                                    */
   GEG_ERR_WORKSPACE = 5,          /* workspace NULL, misaligned or too small                      */
@@ -84,7 +99,8 @@ typedef enum {
 /* Bits of the device error word (workspace word 0), sticky until geg_workspace_init. */
 #define GEG_DEVERR_NEGATIVE_SIZE 0x1u /* some sizes[e] < 0: treated as 0                     */
 #define GEG_DEVERR_SIZES_EXCEED_M 0x2u /* sum(sizes) > M: rows past M are not computed        */
-#define GEG_DEVERR_FP16_RANGE 0x4u    /* an NF4-path operand overflowed fp16 (|x| > 65504)   */
+#define GEG_DEVERR_FP16_RANGE 0x4u    /* an NF4-path operand overflowed fp16 (|x| > 65504 on a
+                                         decode path) or is not finite                         */
 #define GEG_DEVERR_BAD_EXPERT_ID 0x8u /* geg_route_sort: a top-k id outside [0, E) (entry dropped) */
 #define GEG_DEVERR_NON_FINITE 0x10u  /* W4A8: an activation is inf or NaN (its block's codes are unspecified) */
 
@@ -102,6 +118,11 @@ typedef struct {
    * kernels the call does not launch are not recorded. The caller creates the
    * events (hipEventCreate) and owns them. */
   hipEvent_t* kernel_events;
+  /* 0: size every launch for the device's compute units. n > 0: size every grid
+   * as if the device had min(n, its compute units) of them (persistent kernels
+   * then walk their work lists in more rounds; the results are the same). For
+   * tests of the persistent loops; negative values are refused. */
+  int32_t cu_limit;
 } geg_opts;
 
 /* Operation ids for geg_workspace_bytes. */

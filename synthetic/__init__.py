@@ -54,8 +54,9 @@ def _mk(name, fmt, E, K, N, T, k, zipf=0.0, op="fwd"):
     return Case(name, fmt, E, K, N, T, k, zipf, op)
 
 
-# The five workload families. OLMoE gate_up is the headline (decode T=1 and
-# prefill T=2048); the rest are parity cases.
+# The five workload families. The benchmark's headline is Mixtral w1/w3 (the
+# largest single-GPU configuration) with its dgrad, beside every T=1 and T=64
+# decode case; every case is a parity case.
 CASES = {c.name: c for c in [
     _mk("tiny", "nf4", 8, 256, 512, 64, 2),
     _mk("olmoe_gate_up_t1", "nf4", 64, 2048, 2048, 1, 8),
@@ -137,14 +138,17 @@ def rows_bf16(c: Case, seed: int):
     return np.ascontiguousarray(x[token]), sizes
 
 
-def nf4_weight_f32(c: Case, seed: int, e: int, rows=None) -> np.ndarray:
+def nf4_weight_f32(c: Case, seed: int, e: int, rows=None, first_rows=None) -> np.ndarray:
     """Unquantised weights of expert e, [N, K] fp32 drawn from N(0, 0.02).
 
     rows: optional index array to return only those output rows (the whole
     expert is still drawn, so the values do not depend on `rows`).
+    first_rows: optional n to return rows 0..n-1 only; the stream is drawn in
+    row-major order, so drawing its first n * K values gives the same rows.
     """
     g = np.random.default_rng([seed, 2, e])
-    w = g.standard_normal((c.N, c.K), dtype=np.float32)
+    n = c.N if first_rows is None else min(int(first_rows), c.N)
+    w = g.standard_normal((n, c.K), dtype=np.float32)
     w *= np.float32(0.02)
     return w if rows is None else np.ascontiguousarray(w[rows])
 

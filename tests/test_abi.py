@@ -25,7 +25,7 @@ def test_library_exports_every_header_function():
 
 
 def test_version_and_status_strings():
-    assert L().geg_version() == 100
+    assert L().geg_version() == 110
     assert L().geg_status_string(0) == b"GEG_OK"
     assert L().geg_status_string(5) == b"GEG_ERR_WORKSPACE"
 
@@ -38,19 +38,50 @@ def _gemm(name="gnf4_grouped_gemm", a=P, sizes=P, w=P, s=P, out=P, M=16, N=64, K
 
 def test_bad_shapes_are_refused():
     assert _gemm(K=100) == 2                        # K % 64
+    assert b"multiple of 64" in L().geg_last_error()
     assert _gemm("gmxfp4_grouped_gemm", K=48) == 2  # K % 32
+    assert b"multiple of 32" in L().geg_last_error()
     assert _gemm(M=-1) == 2
     assert _gemm(N=0) == 2
     assert _gemm(E=0) == 2
     assert _gemm(E=2000) == 2
-    assert b"multiple of 64" in L().geg_last_error() or True
+    assert b"1024 experts" in L().geg_last_error()
     assert L().gnf4_grouped_dgrad(P, P, P, P, P, 16, 60, 128, 4, P, 1 << 20, None, None) == 2  # N % 8
+    assert b"N % 8" in L().geg_last_error()
+
+
+def test_buffer_windows_past_2gib_are_refused_not_clamped():
+    # one expert's packed weights must fit one 32-bit buffer window: N * K / 2 bytes
+    # just past 0x7FFFFFF0 is refused on the host (before any device check) by
+    # every entry point, instead of the kernels reading zeros past the window
+    N, K = 65536, 65536                              # N * K / 2 = 2^31
+    for name in ("gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad", "gmxfp4_grouped_dgrad",
+                 "gmxfp4_w4a8_grouped_gemm"):
+        assert _gemm(name, N=N, K=K) == 2, name
+        assert b"0x7FFFFFF0" in L().geg_last_error(), name
+    assert _gemm(N=32768, K=131072) == 2               # 2^31 bytes again
+    # within the window the shape passes and the call stops at a later check
+    # (no GPU here, or P is not device memory)
+    assert _gemm(N=32767, K=131072) not in (0, 2)      # 2^31 - 2^16 bytes
+    assert _gemm(N=65536 - 64, K=65536) not in (0, 2)  # 2^31 - 2^21 bytes
+    # 256 rows of the contraction or output width must fit one window (512 * max(N, K) bytes)
+    assert _gemm(N=64, K=4194304) == 2
+    assert b"4194303" in L().geg_last_error()
+    assert L().gnf4_grouped_dgrad(P, P, P, P, P, 16, 4194304, 64, 4, P, 1 << 20, None, None) == 2
+    # the W4A8 activation scales are read through one window: ceil(K/128) * M * 4 bytes
+    assert _gemm("gmxfp4_w4a8_grouped_gemm", M=(1 << 28), N=64, K=512) == 2
+    assert b"activation scales" in L().geg_last_error()
+    # the block checks both projections
+    assert L().gnf4_expert_block(P, P, P, P, P, P, P, 16, 65536, 32768, 4, P, 1 << 20, None, None) == 2
 
 
 def test_bad_options_are_refused():
     assert _gemm(opts=geg.Opts(5, 0)) == 8
     assert _gemm(opts=geg.Opts(0, 17)) == 8
     assert _gemm(opts=geg.Opts(0, -1)) == 8
+    assert _gemm(opts=geg.Opts(0, 0, None, -1)) == 8
+    assert b"cu_limit" in L().geg_last_error()
+    assert _gemm(opts=geg.Opts(0, 0, None, 3)) not in (0, 2, 8)   # accepted: stops at the device check
 
 
 def test_empty_problem_is_a_noop_even_with_null_pointers():
@@ -83,9 +114,14 @@ def test_workspace_sizes():
     # NF4 prefill: the 256-byte header (error word), the split-K counter region
     # (kept clear of other data) and the fp16 copy of the activations that the
     # tiled path reads; MXFP4 reads bf16 activations as given
-    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == 256 + (4 << 20) + 16384 * 2048 * 2
+    # (plus the rows' int32 exponents of the row-scaled copy)
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == \
+        256 + (4 << 20) + 16384 * 2048 * 2 + 16384 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
-    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == 256 + (4 << 20) + 8192 * 28672 * 2
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == \
+        256 + (4 << 20) + 8192 * 28672 * 2 + 8192 * 4
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 3000, 2048, 64, 4) == \
+        256 + (4 << 20) + 3000 * 64 * 2 + ((3000 * 4 + 255) & ~255)
     # skinny split-K partials; a small batch on the automatic path goes to the
     # vector path, which needs nothing beyond the header
     one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(1, 1))

@@ -1,8 +1,24 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (automatic path choice). The oracle computes sampled outputs one
-dot product at a time: first and last row of every expert, the last column, and
-uniform random positions. NF4 bytes are made on the GPU by the library's packer;
-the sampled rows' bytes are checked bit for bit against the oracle's packer."""
+benchmark times (automatic path choice).
+
+* Every forward and dgrad workload at seeds 0, 1 and 2 on sampled outputs that
+  the oracle computes one dot product at a time: first and last row of every
+  expert, the last column, and uniform random positions. NF4 bytes are made on
+  the GPU by the library's packer; the sampled rows' bytes are checked bit for
+  bit against the oracle's packer.
+* One workload per weight format on every output element (OLMoE gate_up
+  T=2048 in NF4, gpt-oss gate_up T=2048 in MXFP4), with the oracle's own packed
+  bytes uploaded as the weights.
+* The fused expert block at the benchmark's prefill shapes (Qwen3 T=4096 in NF4,
+  gpt-oss T=2048 in MXFP4) on whole sampled output rows.
+* Offsets past 2^31 elements: an activation tensor of more than 2^31 elements
+  (and a dY of as many), in a process of its own (tests/boundary_case.py).
+"""
+import json
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 
@@ -47,15 +63,15 @@ def _check_packed_rows(c, seed, w, s, rows_by_expert):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", FWD)
-def test_forward_full_size(geg, name):
+def test_forward_full_size(geg, name, seed):
     c = synthetic.case(name)
-    seed = 0
     log(f"case: {name} (M={c.M} N={c.N} K={c.K} E={c.E} {c.fmt}) seed={seed}")
     a_bits, sizes, w, s = _inputs(c, seed)
     fn = geg.gnf4_grouped_gemm if c.fmt == "nf4" else geg.gmxfp4_grouped_gemm
     out = fn(up_u16_as_bf16(a_bits), up(sizes), w, s)
-    rows, cols = sample_positions(sizes, c.N, 1500, seed=1)
+    rows, cols = sample_positions(sizes, c.N, 1500, seed=1 + 10 * seed)
     got = bf16_to_f64(out)[rows, cols]
     rows_fn = C.nf4_rows_fn(c, seed) if c.fmt == "nf4" else C.mxfp4_rows_fn(c, seed)
     ref = oracle.sampled_fwd_ref(a_bits, sizes, rows_fn, rows, cols)
@@ -66,22 +82,156 @@ def test_forward_full_size(geg, name):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", DGRAD)
-def test_dgrad_full_size(geg, name):
+def test_dgrad_full_size(geg, name, seed):
     c = synthetic.case(name)
-    seed = 0
     log(f"case: {name} dgrad (M={c.M} N={c.N} K={c.K} E={c.E}) seed={seed}")
     a_bits, sizes, w, s = _inputs(c, seed)
     dy = synthetic.dgrad_dy_bf16(c, seed)
     fn = geg.gnf4_grouped_dgrad if c.fmt == "nf4" else geg.gmxfp4_grouped_dgrad
     dx = fn(up_u16_as_bf16(dy), up(sizes), w, s)
-    rows, cols = sample_positions(sizes, c.K, 600, seed=2)
+    rows, cols = sample_positions(sizes, c.K, 600, seed=2 + 10 * seed)
     # keep the sampled columns inside a few 64-wide blocks (plus the last one) so
     # the oracle packs only those blocks of each expert
-    rng = np.random.default_rng(3)
+    rng = np.random.default_rng(3 + 10 * seed)
     blocks = np.append(rng.choice(c.K // 64 - 1, 3, replace=False), c.K // 64 - 1)
     cols = blocks[cols % 4] * 64 + cols % 64
     got = bf16_to_f64(dx)[rows, cols]
     cols_fn = C.nf4_cols_fn(c, seed) if c.fmt == "nf4" else C.mxfp4_cols_fn(c, seed)
     ref = oracle.sampled_dgrad_ref(dy, sizes, cols_fn, rows, cols)
     assert_close(got, ref, name + " dgrad")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["olmoe_gate_up_t2048", "gptoss_gate_up_t2048"])
+def test_forward_full_size_every_element(geg, name):
+    import torch
+    c = synthetic.case(name)
+    seed = 0
+    log(f"case: {name} every element (M={c.M} N={c.N} K={c.K} E={c.E} {c.fmt})")
+    a_bits, sizes = synthetic.rows_bf16(c, seed)
+    touched = np.nonzero(sizes)[0]
+    w = torch.zeros((c.E, c.N, c.K // 2), dtype=torch.uint8, device="cuda")
+    nsc = c.K // 64 if c.fmt == "nf4" else c.K // 32
+    s = torch.zeros((c.E, c.N, nsc), dtype=torch.float32 if c.fmt == "nf4" else torch.uint8, device="cuda")
+    packed = {}
+    for e in touched:
+        e = int(e)
+        q, sc = C.nf4_expert(c, seed, e) if c.fmt == "nf4" else synthetic.mxfp4_bytes(c, seed, e)
+        w[e].copy_(up(q))
+        s[e].copy_(up(sc))
+        packed[e] = (q, sc)
+    fn = geg.gnf4_grouped_gemm if c.fmt == "nf4" else geg.gmxfp4_grouped_gemm
+    out = bf16_to_f64(fn(up_u16_as_bf16(a_bits), up(sizes), w, s, check_errors=True))
+    dec = oracle.dequant_nf4 if c.fmt == "nf4" else oracle.dequant_mxfp4
+    ref = oracle.grouped_ref(a_bits, sizes, lambda e: dec(*packed[e]), c.N)
+    assert_close(out, ref, f"{name} every element")
+
+
+BLOCKS = {"qwen3_block": ("qwen3_gate_up_t4096", "qwen3_down_t4096"),
+          "gptoss_block": ("gptoss_gate_up_t2048", "gptoss_down_t2048")}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", sorted(BLOCKS))
+def test_block_full_size_sampled_rows(geg, name):
+    import torch
+    cg, cd = (synthetic.case(n) for n in BLOCKS[name])
+    seed = 0
+    H, I = cg.K, cg.N // 2
+    log(f"case: {name} full size (M={cg.M} H={H} I={I} E={cg.E} {cg.fmt})")
+    a_bits, sizes = synthetic.rows_bf16(cg, seed)
+    _, sizes2 = synthetic.rows_bf16(cd, seed)
+    assert (sizes == sizes2).all()
+    touched = np.nonzero(sizes)[0]
+    # whole output rows of the first and last row of 6 experts plus 12 random rows
+    rng = np.random.default_rng(5)
+    off = oracle.offsets(sizes)
+    ex = rng.choice(touched, 6, replace=False)
+    rows = np.concatenate([[off[e], off[e + 1] - 1] for e in ex] + [rng.integers(0, cg.M, 12)]).astype(np.int64)
+    need = np.unique(np.searchsorted(off, rows, side="right") - 1)
+    if cg.fmt == "nf4":
+        w13, s13 = gpu_weights_nf4(cg, seed, experts=touched)
+        w2, s2 = gpu_weights_nf4(cd, seed, experts=touched)
+        p13 = {int(e): C.nf4_expert(cg, seed, int(e)) for e in need}
+        p2 = {int(e): C.nf4_expert(cd, seed, int(e)) for e in need}
+        for e in need:   # the oracle decodes its own bytes: check the device's are the same
+            assert np.array_equal(w13[e].cpu().numpy(), p13[int(e)][0]) and np.array_equal(w2[e].cpu().numpy(), p2[int(e)][0])
+            assert np.array_equal(s13[e].cpu().numpy().view(np.uint32), p13[int(e)][1].view(np.uint32))
+            assert np.array_equal(s2[e].cpu().numpy().view(np.uint32), p2[int(e)][1].view(np.uint32))
+        dec = oracle.dequant_nf4
+        fn = geg.gnf4_expert_block
+    else:
+        w13, s13 = gpu_weights_mxfp4(cg, seed, experts=touched)
+        w2, s2 = gpu_weights_mxfp4(cd, seed, experts=touched)
+        p13 = {int(e): synthetic.mxfp4_bytes(cg, seed, int(e)) for e in need}
+        p2 = {int(e): synthetic.mxfp4_bytes(cd, seed, int(e)) for e in need}
+        dec = oracle.dequant_mxfp4
+        fn = geg.gmxfp4_expert_block
+    out = fn(up_u16_as_bf16(a_bits), up(sizes), w13, s13, w2, s2, check_errors=True)
+    got = bf16_to_f64(out)[rows]
+    order = np.argsort(rows, kind="stable")        # group rows by expert for the oracle's cache
+    ref = np.empty_like(got)
+    ref[order] = oracle.sampled_block_ref(a_bits, sizes, rows[order], lambda e: dec(*p13[e]), lambda e: dec(*p2[e]))
+    allow = np.zeros_like(got)
+    n_amb = 0
+    ex = np.searchsorted(off, rows, side="right") - 1
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        x = synthetic.bf16_bits_to_f32(a_bits[rows[sel]]).astype(np.float64)
+        allow[sel], k = _act_rounding_allowance(x, dec(*p13[int(e)]), dec(*p2[int(e)]))
+        n_amb += k
+    err = np.abs(got - ref)
+    plain = 1e-2 * np.maximum(1.0, np.abs(ref))
+    log(f"  {name}: max |err|/max(1,|ref|) = {np.max(err / np.maximum(1.0, np.abs(ref))):.5f}; "
+        f"{n_amb} of {len(rows) * I} intermediate values within the fp32 band of a bf16 rounding midpoint; "
+        f"share within 1e-2 max(1,|ref|) = {float(np.mean(err <= plain)):.5f}; "
+        f"max err / (plain bound + rounding allowance) = {np.max(err / (plain + allow)):.4f}")
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= plain + allow), f"{name}: outside the bound at {np.argwhere(err > plain + allow)[:3].tolist()}"
+
+
+def _act_rounding_allowance(x, w13, w2):
+    """How far the block's bf16 intermediate can legitimately move each output.
+
+    The block rounds act = silu(h_gate) * h_up to bf16 once, a decision taken
+    from the kernel's fp32 h. The kernel's h differs from the exact h by at most
+    2^-16 sum_k |a_k w_k| (at most 256 fp32 roundings along any accumulation
+    chain, each within 2^-24 of the running sum), so where the exact act lies
+    within the resulting band of a bf16 rounding midpoint both roundings are
+    correct results; elsewhere the rounding is unique and must agree. Returns,
+    per output, sum over the ambiguous act_i of (two bf16 spacings of act_i) *
+    |W2[n, i]|, and the number of ambiguous act values.
+    """
+    h = x @ w13.T
+    band = 2.0 ** -19 * (np.abs(x) @ np.abs(w13).T)
+    g, u, dg, du = h[:, 0::2], h[:, 1::2], band[:, 0::2], band[:, 1::2]
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    act = silu * u
+    # |d act| from the h band, plus the kernel's fp32 exponential and reciprocal
+    dact = np.abs(sig * (1.0 + g * (1.0 - sig)) * u) * dg + np.abs(silu) * du + 2.0 ** -20 * np.abs(act)
+    _, ex = np.frexp(np.abs(act))
+    spacing = np.ldexp(1.0, np.maximum(ex - 8, -133))
+    r = synthetic.bf16_bits_to_f32(oracle.bf16_rne_from_f64(act)).astype(np.float64)
+    amb = spacing / 2 - np.abs(act - r) <= dact
+    return np.where(amb, 2 * spacing, 0.0) @ np.abs(w2).T, int(amb.sum())
+
+
+@pytest.mark.timeout(900)
+def test_offsets_past_2_31_elements_in_own_process():
+    """More than 2^31 activation (and dY) elements, run by tests/boundary_case.py
+    in a process of its own; it prints one JSON line of per-case errors."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    script = os.path.join(os.path.dirname(os.path.abspath(__file__)), "boundary_case.py")
+    log("case: offsets past 2^31 elements (child process)")
+    r = subprocess.run([sys.executable, "-u", script], capture_output=True, text=True, timeout=600)
+    log(r.stdout[-3000:])
+    assert r.returncode == 0, r.stderr[-3000:]
+    res = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1])
+    for case, err in res.items():
+        assert err <= 1e-2, (case, err)

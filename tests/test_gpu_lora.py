@@ -71,6 +71,31 @@ def test_lora_forward_and_backward(geg, fmt, r, K, N, sizes):
     assert_close(gb.cpu().numpy().astype(np.float64), dB_ref, f"lora dB {fmt} r={r}")
 
 
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+def test_lora_backward_small_gradients(geg, fmt):
+    # dY ~ N(0, 1e-7), the scale of activation gradients in training: dx, dA and
+    # dB keep their relative precision (checked against max|err| / max|ref|, not
+    # the absolute floor of max(1, |ref|)); the NF4 dgrad scales each dY row by a
+    # power of two before its fp16 conversion
+    log(f"case: lora backward {fmt} with dY ~ N(0, 1e-7)")
+    x, dy, A, B, sz, W, codes, scales = _case(fmt, 4, 320 if fmt == "nf4" else 288, 136, 16, [5, 0, 90, 30],
+                                               seed=23)
+    K = x.shape[1]
+    dy = synthetic.f32_to_bf16_bits(synthetic.bf16_bits_to_f32(dy) * np.float32(1e-7))
+    s = 0.5
+    fwd = geg.gnf4_grouped_gemm_lora if fmt == "nf4" else geg.gmxfp4_grouped_gemm_lora
+    bwd = geg.gnf4_grouped_dgrad_lora if fmt == "nf4" else geg.gmxfp4_grouped_dgrad_lora
+    xt, szt, At, Bt, wt, st = up_u16_as_bf16(x), up(sz), up(A), up(B), up(codes), up(scales)
+    _, u = fwd(xt, szt, wt, st, At, Bt, s)
+    dx, ga, gb = bwd(up_u16_as_bf16(dy), szt, wt, st, xt, At, Bt, u, s, check_errors=True)
+    dx_ref, dA_ref, dB_ref = L.lora_backward_ref(x, dy, sz, W, A, B, s, K)
+    for got, ref, what in ((bf16_to_f64(dx), dx_ref, "dx"), (ga.cpu().numpy().astype(np.float64), dA_ref, "dA"),
+                           (gb.cpu().numpy().astype(np.float64), dB_ref, "dB")):
+        rel = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        log(f"  {what}: max|err|/max|ref| = {rel:.2e}")
+        assert rel <= 1e-2, what
+
+
 def test_lora_autograd_op(geg):
     import torch
     log("case: lora autograd op")

@@ -202,18 +202,72 @@ def test_bad_sizes_are_flagged_and_clamped(geg):
 
 
 def test_fp16_range_flag(geg):
+    # An activation beyond fp16 range: the decode paths convert bf16 -> fp16
+    # directly and flag the overflow; the tiled path scales each row by a power
+    # of two first, so the same row is computed exactly and nothing is flagged;
+    # a non-finite activation is flagged on the tiled path too.
     log("case: activation beyond fp16 range on the NF4 path")
     c, d = custom_case("nf4", 2, 128, 64, [3, 40], seed=4)
     d["a_bits"][1, 5] = synthetic.f32_to_bf16_bits(np.array([1.0e5], np.float32))[0]
     g = upload_case(d)
-    for path in ["skinny", "tiled"]:
+    for path in ["skinny", "narrow", "vec"]:
         ws = geg.Workspace(1 << 16)
         run_fwd(geg, c, g, path, ws=ws)
         assert ws.read_error() & geg.DEVERR_FP16_RANGE, path
     ws = geg.Workspace(1 << 16)
+    out = run_fwd(geg, c, g, "tiled", ws=ws)
+    assert ws.read_error() == 0
+    assert_close(bf16_to_f64(out), ref_of(d), "tiled, row holding 1e5")
+    d["a_bits"][1, 5] = 0x7F80                                            # +inf
+    ws = geg.Workspace(1 << 16)
+    run_fwd(geg, c, upload_case(d), "tiled", ws=ws)
+    assert ws.read_error() & geg.DEVERR_FP16_RANGE
+    with pytest.raises(geg.GegDeviceError, match="fp16"):
+        run_fwd_checked = geg.gnf4_grouped_gemm
+        run_fwd_checked(*(upload_case(d)[k] for k in ("a", "sizes", "w", "s")), opts=geg.Opts(2, 0),
+                        workspace=ws, check_errors=True)
+    assert ws.read_error() == 0                                           # cleared when it raised
+    ws = geg.Workspace(1 << 16)
     d["a_bits"][1, 5] = 0
     run_fwd(geg, c, upload_case(d), "auto", ws=ws)
     assert ws.read_error() == 0
+
+
+@pytest.mark.parametrize("scale", [1e-6, 1e-7, 1e-8, 1e6])
+def test_nf4_dgrad_row_scaling_keeps_small_and_large_gradients(geg, scale):
+    # Activation gradients of a training step sit far below fp16's normal range
+    # (2^-14); the tiled NF4 path multiplies each dY row by a power of two before
+    # its fp16 conversion and the results back after, so dX keeps its relative
+    # precision at any scale. Checked against max|err| / max|ref|, which does not
+    # fall back on the absolute floor of max(1, |ref|) when |ref| << 1.
+    log(f"case: nf4 dgrad with dY ~ N(0, {scale:g})")
+    c, d = custom_case("nf4", 4, 320, 136, [0, 37, 150, 5], seed=6)
+    rng = np.random.default_rng(8)
+    dyf = (rng.standard_normal((192, 136)) * scale).astype(np.float32)
+    dyf[3, :] *= 1e-3                        # one row three decades smaller than the rest
+    dy = synthetic.f32_to_bf16_bits(dyf)
+    g = upload_case(d)
+    dx = geg.gnf4_grouped_dgrad(up_u16_as_bf16(dy), g["sizes"], g["w"], g["s"], check_errors=True)
+    ref = oracle.dgrad_ref(dy, d["sizes"], C.weight_fn(d), c.K)
+    got = bf16_to_f64(dx)
+    rel = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    row_rel = float(np.max(np.abs(got[3] - ref[3])) / np.max(np.abs(ref[3])))
+    log(f"  max|err|/max|ref| = {rel:.2e}, small row {row_rel:.2e}")
+    assert rel <= 1e-2 and row_rel <= 1e-2
+
+
+@pytest.mark.parametrize("scale", [1e-7, 1e4])
+def test_nf4_forward_row_scaling(geg, scale):
+    # the same on the forward tiled path: activations far below or above fp16's
+    # range are computed at full relative precision
+    log(f"case: nf4 tiled forward with activations ~ N(0, {scale:g})")
+    c, d = custom_case("nf4", 3, 256, 200, [40, 0, 260], seed=12)
+    d["a_bits"] = synthetic.f32_to_bf16_bits(synthetic.bf16_bits_to_f32(d["a_bits"]) * np.float32(scale))
+    out = run_fwd(geg, c, upload_case(d), "tiled")
+    ref = ref_of(d)
+    rel = float(np.max(np.abs(bf16_to_f64(out) - ref)) / np.max(np.abs(ref)))
+    log(f"  max|err|/max|ref| = {rel:.2e}")
+    assert rel <= 1e-2
 
 
 def test_empty_and_single_expert(geg):

@@ -4,14 +4,12 @@ block-scaled matrix instruction) against oracle.w4a8.
 The activation quantisation is integer work decided on exactly scaled values:
 codes and scales must match the oracle bit for bit.
 
-The GEMM's tolerance is derived from the instruction's arithmetic: its 128-wide
-dot products keep about 12 bits below the largest product (in-bounds probes on
-gfx950 measured errors up to 3e-4 of max |a w| per instruction, unbiased), and
-the per-instruction results accumulate in fp32 and round once to bf16. So
-|gpu - ref| <= 1e-2 max(1, |ref|) + 2^-10 S, with S = sum_k |a_k w_k| (the
-quantised operands), which covers 3x the measured per-instruction error summed
-over every instruction of a dot product. The share of outputs that also meet
-the plain 1e-2 max(1, |ref|) bound is printed beside it.
+The GEMM is asserted at the path's tolerance, |gpu - ref| <= 1e-2 max(1, |ref|)
+per element, against the oracle of the quantised operands. The instruction's
+128-wide dot products keep about 12 bits below the largest product (in-bounds
+probes on gfx950 measured errors up to 3e-4 of max |a w| per instruction,
+unbiased), so the error is also printed against S = sum_k |a_k w_k| as a
+diagnostic of that arithmetic (err / (2^-10 S) stays below 1 on every case).
 """
 import numpy as np
 import pytest
@@ -104,11 +102,12 @@ def _sum_abs(a_bits, sizes, wfn, N):
 def _check(got, ref, S, what):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
-    bound = TOL * np.maximum(1.0, np.abs(ref)) + ACC * S
-    strict = float(np.mean(err <= TOL * np.maximum(1.0, np.abs(ref))))
-    log(f"  {what}: max err/bound = {np.max(err / bound):.4f}, max err/S = {np.max(err / np.maximum(S, 1e-30)):.2e}, "
-        f"share within 1e-2 max(1,|ref|) = {strict:.5f}")
-    assert np.all(err <= bound), f"{what}: err exceeds the bound at {np.argwhere(err > bound)[:3].tolist()}"
+    bound = TOL * np.maximum(1.0, np.abs(ref))
+    acc_bound = ACC * S   # diagnostic only: the instruction's dot-product arithmetic
+    log(f"  {what}: max |err|/max(1,|ref|) = {np.max(err / np.maximum(1.0, np.abs(ref))):.5f}, "
+        f"max err/(2^-10 S) = {np.max(err / np.maximum(acc_bound, 1e-30)):.4f}, "
+        f"share within 1e-2 max(1,|ref|) = {float(np.mean(err <= bound)):.5f}")
+    assert np.all(err <= bound), f"{what}: err exceeds 1e-2 max(1,|ref|) at {np.argwhere(err > bound)[:3].tolist()}"
 
 
 @pytest.mark.parametrize("K,N,sizes", [

@@ -61,3 +61,10 @@ def test_generators_are_deterministic():
     nib = np.concatenate([codes & 15, codes >> 4]).ravel()
     counts = np.bincount(nib, minlength=16)
     assert counts.min() > 0.98 * counts.mean()           # uniform over all 16 nibbles
+
+
+def test_first_rows_draw_is_a_prefix_of_the_whole_expert():
+    c = synthetic.case("qwen3_down_t1")
+    whole = synthetic.nf4_weight_f32(c, 0, 5)
+    for n in (1, 7, 300):
+        assert np.array_equal(synthetic.nf4_weight_f32(c, 0, 5, first_rows=n), whole[:n])
