@@ -18,7 +18,7 @@ import threading
 
 __all__ = [
     "GegError", "GegDeviceError", "Opts", "Workspace", "lib", "header_functions",
-    "gnf4_grouped_gemm", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad", "gmxfp4_grouped_dgrad",
+    "gnf4_grouped_gemm", "gnf4_grouped_gemm_noalloc", "gmxfp4_grouped_gemm", "gnf4_grouped_dgrad", "gmxfp4_grouped_dgrad",
     "grouped_linear", "gnf4_expert_block", "gmxfp4_expert_block", "route_sort", "route_combine",
     "gnf4_dequant", "gmxfp4_dequant", "gnf4_quantize", "geg_workspace_bytes",
     "gmxfp4_w4a8_grouped_gemm", "gmxfp8_quantize", "GEG_OP_MXFP4_W4A8", "DEVERR_NON_FINITE",
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
                 f = getattr(L, name)
                 f.argtypes, f.restype = gemm_args, ctypes.c_int
             L.gmxfp8_quantize.argtypes, L.gmxfp8_quantize.restype = [_P, _P, _P, _I64, _I64, _P], ctypes.c_int
+            L.gnf4_grouped_gemm_noalloc.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
+            L.gnf4_grouped_gemm_noalloc.restype = ctypes.c_int
             L.geg_lora_workspace_bytes.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32]
             L.geg_lora_workspace_bytes.restype = _SZ
             for name in ("gnf4_grouped_gemm_lora", "gmxfp4_grouped_gemm_lora"):
@@ -324,6 +326,27 @@ def gnf4_grouped_gemm(a, sizes, w, absmax, out=None, workspace: Workspace | None
     GegDeviceError when the word is set (the same holds for every wrapper below)."""
     return _gemm("gnf4_grouped_gemm", GEG_OP_NF4_FWD, a, sizes, w, absmax, out, workspace, opts, stream,
                  check_errors)
+
+
+def gnf4_grouped_gemm_noalloc(a, sizes, w, absmax, out, error_word=None, opts: Opts | None = None, stream=None):
+    """gnf4_grouped_gemm without a workspace, for callers that cannot allocate device
+    memory: the library's kernels take their scratch from a library-held static
+    array (144 MiB per GPU; larger calls raise GEG_ERR_WORKSPACE), so `out` must be
+    given. error_word: None or a device int32 tensor of one element that receives
+    the call's device error bits (OR-ed in). Calls that overlap on one GPU race on
+    the shared array; calls ordered on one stream do not."""
+    import torch
+    M, K = a.shape
+    E, N = w.shape[0], w.shape[1]
+    _check_tensor(a, "a", torch.bfloat16, (M, K))
+    _check_tensor(sizes, "sizes", torch.int32, (E,))
+    _check_packed(True, w, absmax, E, N, K, "weights", "absmax")
+    _check_tensor(out, "out", torch.bfloat16, (M, N))
+    _check_tensor(error_word, "error_word", torch.int32, (1,))
+    _require_gpu(a, sizes, w, absmax, out, error_word)
+    _check(lib().gnf4_grouped_gemm_noalloc(_ptr(a), _ptr(sizes), _ptr(w), _ptr(absmax), _ptr(out), M, N, K, E,
+                                           _ptr(error_word), ctypes.byref(opts) if opts else None, _stream(stream)))
+    return out
 
 
 def gmxfp4_grouped_gemm(a, sizes, blocks, scales, out=None, workspace: Workspace | None = None,

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgeg.so")
 
-SOURCES = ["geg.cpp", "skinny.hip", "tile.hip", "util.hip", "vec.hip", "narrow.hip", "route.hip", "w4a8.hip", "lora.hip"]
+SOURCES = ["geg.cpp", "skinny.hip", "tile.hip", "util.hip", "vec.hip", "narrow.hip", "route.hip", "w4a8.hip", "lora.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

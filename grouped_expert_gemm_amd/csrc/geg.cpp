@@ -265,10 +265,17 @@ struct LoraIn {
   std::function<hipError_t()> post;
 };
 
+// The library-held scratch of gnf4_grouped_gemm_noalloc in place of a caller's
+// workspace, and the caller's device error word (NULL: the scratch header's).
+struct Scratch {
+  bool library = false;
+  uint32_t* err_word = nullptr;
+};
+
 geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8_t* wq,
                        const void* scales, void* out, int64_t M, int64_t N, int64_t K, int32_t E,
                        void* ws, size_t ws_bytes, const geg_opts* opts, hipStream_t stream,
-                       int32_t glu = 0, const LoraIn& lora = LoraIn{}) {
+                       int32_t glu = 0, const LoraIn& lora = LoraIn{}, const Scratch& scratch = Scratch{}) {
   CuScope cu_scope(opts);
   geg_status st = check_shape(M, N, K, E, fmt == geg::NF4 ? 64 : 32);
   if (st != GEG_OK) return st;
@@ -295,7 +302,8 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
                                        std::to_string(p.total_bytes));
   if ((st = check_device()) != GEG_OK) return st;
   for (auto [ptr, name] : {std::pair<const void*, const char*>{a, "a"}, {sizes, "sizes"},
-                           {wq, "weights"}, {scales, "scales"}, {out, "out"}, {ws, "workspace"}})
+                           {wq, "weights"}, {scales, "scales"}, {out, "out"},
+                           {scratch.library ? nullptr : ws, "workspace"}, {scratch.err_word, "error_word"}})
     if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
 
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
@@ -313,7 +321,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.split = p.split;
   g.cb = p.cb;
   g.vec_rows = p.vec_rows;
-  g.err = reinterpret_cast<uint32_t*>(wsb);
+  g.err = scratch.err_word ? scratch.err_word : reinterpret_cast<uint32_t*>(wsb);
   g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
@@ -495,6 +503,40 @@ geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t*
                              const geg_opts* opts, hipStream_t stream) {
   return gemm_common(geg::NF4, a, sizes, w, absmax, out, M, N, K, E, workspace, workspace_bytes,
                      opts, stream);
+}
+
+geg_status gnf4_grouped_gemm_noalloc(const void* a, const int32_t* sizes, const uint8_t* w, const float* absmax,
+                                     void* out, int64_t M, int64_t N, int64_t K, int32_t E, uint32_t* error_word,
+                                     const geg_opts* opts, hipStream_t stream) {
+  // Every check that needs no device data first (nothing is enqueued when one
+  // fails), then the library-held scratch in place of a workspace.
+  CuScope cu_scope(opts);
+  geg_status st = check_shape(M, N, K, E, 64);
+  if (st != GEG_OK) return st;
+  Plan p;
+  if ((st = make_plan(GEG_OP_NF4_FWD, M, N, K, E, opts, p)) != GEG_OK) return st;
+  if (M == 0) return GEG_OK;
+  if (p.total_bytes > geg::kNoallocScratchBytes)
+    return fail(GEG_ERR_WORKSPACE, "this call needs " + std::to_string(p.total_bytes) +
+                                       " bytes of scratch; the library-held array holds " +
+                                       std::to_string(geg::kNoallocScratchBytes) +
+                                       " (144 MiB): call gnf4_grouped_gemm with a workspace");
+  if (!a || !sizes || !w || !absmax || !out) return fail(GEG_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(sizes, 4) || !aligned(absmax, 4) ||
+      (error_word && !aligned(error_word, 4)))
+    return fail(GEG_ERR_MISALIGNED, "a, w and out must be 16-byte aligned, sizes, absmax and error_word 4-byte");
+  if ((st = check_device()) != GEG_OK) return st;
+  for (auto [ptr, name] : {std::pair<const void*, const char*>{a, "a"}, {sizes, "sizes"}, {w, "weights"},
+                           {absmax, "absmax"}, {out, "out"}, {error_word, "error_word"}})
+    if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
+  void* ws = nullptr;
+  hipError_t e = geg::noalloc_scratch(&ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "library-held scratch");
+  Scratch sc;
+  sc.library = true;
+  sc.err_word = error_word;
+  return gemm_common(geg::NF4, a, sizes, w, absmax, out, M, N, K, E, ws, geg::kNoallocScratchBytes, opts, stream, 0,
+                     LoraIn{}, sc);
 }
 
 geg_status gmxfp4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t* blocks,

@@ -112,4 +112,11 @@ hipError_t launch_route_combine(const uint16_t* y, int64_t N, const int32_t* row
 hipError_t launch_to_f16_rows(const uint16_t* a, uint16_t* a16, int32_t* rexp, int64_t M, int64_t C,
                               uint32_t* err, int cus, hipStream_t s);
 
+// Library-held scratch of gnf4_grouped_gemm_noalloc: the device address of this
+// GPU's static array (looked up and its first kNoallocZeroBytes zeroed on `stream`
+// at the first call on each device).
+constexpr size_t kNoallocScratchBytes = size_t(144) << 20;
+constexpr size_t kNoallocZeroBytes = 256 + (size_t(4) << 20);   // header + split-K counters
+hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
+
 }  // namespace geg

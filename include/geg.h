@@ -158,6 +158,29 @@ geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t*
                              const geg_opts* opts, hipStream_t stream);
 
 /*
+ * gnf4_grouped_gemm_noalloc — gnf4_grouped_gemm for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same operation, arguments and paths, without the
+ * workspace. The call allocates nothing. Its scratch (split-K counters and
+ * partials, the row-scaled fp16 activations and their row exponents) lives in a
+ * library-held static device array of 144 MiB per GPU, created when the
+ * library's code is loaded on that GPU and held until the process ends; its first
+ * 4 MiB + 256 bytes are zeroed by a fill kernel on `stream` at the first call on
+ * each GPU and left at zero by every completed call.
+ *   error_word  device uint32 (4-B aligned) that receives the GEG_DEVERR_* bits of
+ *               this call (OR-ed in; the caller clears it), or NULL to drop them
+ *   A call whose scratch (geg_workspace_bytes(GEG_OP_NF4_FWD, M, N, K, E, opts))
+ *   exceeds 144 MiB is refused with GEG_ERR_WORKSPACE before anything is enqueued
+ *   (for example M * K * 2 + M * 4 > 140 MiB on the tiled path).
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents: calls ordered on one stream are safe; calls that overlap on one GPU
+ *   (unordered streams, several host threads) race on it.
+ */
+geg_status gnf4_grouped_gemm_noalloc(const void* a, const int32_t* sizes, const uint8_t* w, const float* absmax,
+                                     void* out, int64_t M, int64_t N, int64_t K, int32_t E, uint32_t* error_word,
+                                     const geg_opts* opts, hipStream_t stream);
+
+/*
  * gmxfp4_grouped_gemm — the same operation on MXFP4 weights exactly as released:
  *   blocks  u8 [E, N, K/2] e2m1 codes (low nibble = even k), 16-B aligned
  *   scales  u8 [E, N, K/32] e8m0
