@@ -370,20 +370,21 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
 // touches a row outside [0, M); both conditions are flagged in the error word.
 // 8 consecutive fp32 values of a row (two 16-byte buffer loads; `ok` false or a
 // record past the end reads zeros) as two bf16x8 MFMA operands: hi = bf16(v) and
-// lo = bf16(v - hi), about 16 significant bits together (v scaled first).
+// lo = bf16(v - hi), about 16 significant bits together (v multiplied by
+// scale, then by 2^sexp, first).
 struct Split8 {
   u32x4 hi, lo;
 };
 __device__ __forceinline__ Split8 load8_split(const __amdgpu_buffer_rsrc_t& R, uint32_t elem_off, bool ok,
-                                              float scale = 1.0f) {
+                                              float scale = 1.0f, int sexp = 0) {
   const uint32_t b = (elem_off * 4u) | ((uint32_t)!ok << 31);   // bit 31: past every record
   const u32x4 p = __builtin_amdgcn_raw_buffer_load_b128(R, b, 0, 0);
   const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(R, b + 16u, 0, 0);
   Split8 s;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float v0 = scale * __uint_as_float(i < 2 ? p[2 * i] : q[2 * i - 4]);
-    const float v1 = scale * __uint_as_float(i < 2 ? p[2 * i + 1] : q[2 * i - 3]);
+    const float v0 = __builtin_amdgcn_ldexpf(scale * __uint_as_float(i < 2 ? p[2 * i] : q[2 * i - 4]), sexp);
+    const float v1 = __builtin_amdgcn_ldexpf(scale * __uint_as_float(i < 2 ? p[2 * i + 1] : q[2 * i - 3]), sexp);
     const uint32_t h = pack_bf16x2(v0, v1);
     s.hi[i] = h;
     s.lo[i] = pack_bf16x2(v0 - __uint_as_float(h << 16), v1 - __uint_as_float(h & 0xFFFF0000u));

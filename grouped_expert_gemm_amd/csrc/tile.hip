@@ -339,7 +339,9 @@ struct Ops {
 //   barrier Y after group 13 publishes the next stage's buffers; groups 14-15
 //   read its first operands ahead and build the first half of the table of the
 //   stage after it (entries 0-7, from the raw scale already in registers)
-//   barrier X at the end frees the current buffers.
+// Y is the stage's only barrier: every read of the current buffers is issued by
+// group 12 and has completed when a wavefront passes Y, so the next stage's
+// staging may overwrite them as soon as all wavefronts are past it.
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
 template <Fmt F, bool DG, bool TAIL, int H, int P>
 __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
@@ -408,13 +410,6 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-#ifndef GEG_TILE_BARRIER_X
-#define GEG_TILE_BARRIER_X 1
-#endif
-#if GEG_TILE_BARRIER_X
-  // X: every wavefront is done with the current buffers.
-  __syncthreads();
-#endif
 }
 
 // Main loop over the K stages of one tile (H = the wavefront's active 64-row
@@ -472,9 +467,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
       tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff,
                                     m4, base);
   }
-#if !GEG_TILE_BARRIER_X
   __syncthreads();   // the epilogue reuses the stage buffers
-#endif
 }
 
 // Forward (DG = false): out[M, N] = a . W^T per expert. dgrad (DG = true):
@@ -553,24 +546,22 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     else
       run_tile_h<F, DG, TAIL, 0>(L, src, C, g.K, wave, lane, acc);
 
-    if constexpr (F == NF4) {
-      // The fp16 operand rows were multiplied by 2^-rexp[row] (exact); multiply
-      // the rows' fp32 results by 2^rexp[row] (exact) before anything else.
-      // acc[i][j][q] is row 16 i + 4 (lane / 16) + q of the wavefront's block;
-      // rows past the expert read 0 and are never stored.
-      const int brows = max(0, rows - 128 * wm);
-      const __amdgpu_buffer_rsrc_t RE = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<int32_t*>(g.rexp + row0 + 128 * wm), (short)0, brows * 4, 0x00020000);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ex = (int)__builtin_amdgcn_raw_buffer_load_b32(RE, (uint32_t)((16 * i + 4 * (lane >> 4) + q) * 4),
-                                                                   0, 0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j][q] = __builtin_amdgcn_ldexpf(acc[i][j][q], ex);
-        }
-    }
+    // NF4: the fp16 operand rows were multiplied by 2^-rexp[row] (exact), so each
+    // result is multiplied by 2^rexp[row] (exact) where it is read out for its
+    // bf16 rounding, and the adapter delta joins the accumulators at the same
+    // 2^-rexp[row] scale. Rows past the expert read exponent 0 and are never
+    // stored. MXFP4 operands are not scaled.
+    const __amdgpu_buffer_rsrc_t RE = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(F == NF4 ? g.rexp + row0 + 128 * wm : g.sizes), (short)0,
+        F == NF4 ? max(0, rows - 128 * wm) * 4 : 0, 0x00020000);
+    auto rowexp = [&](int r) -> int {   // r: row of the wavefront's 128-row block
+      if constexpr (F == NF4) return (int)__builtin_amdgcn_raw_buffer_load_b32(RE, (uint32_t)(r * 4), 0, 0);
+      return 0;
+    };
+    auto unscale = [](float v, int ex) -> float {
+      if constexpr (F == NF4) return __builtin_amdgcn_ldexpf(v, ex);
+      return v;
+    };
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores
@@ -599,7 +590,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
         for (int j = 0; j < 4; ++j) bq[j] = load8_split(RQ, (uint32_t)((16 * j + r16) * r + jj), ok);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const Split8 au = load8_split(RU, (uint32_t)((16 * i + r16) * r + jj), ok, g.lora_s);
+          const Split8 au = load8_split(RU, (uint32_t)((16 * i + r16) * r + jj), ok, g.lora_s,
+                                        -rowexp(16 * i + r16));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].hi, acc[i][j]);
@@ -619,10 +611,15 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       const bool odd = lane & 1;
       uint16_t* base = E + (4 * (lane >> 4) + (odd ? 2 : 0)) * kEpiLd + ((lane & 15) >> 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        int ex[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ex[q] = rowexp(16 * i + 4 * (lane >> 4) + q);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 v = acc[i][j];
+          f32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = unscale(acc[i][j][q], ex[q]);
           const float r0 = lane_pair_swap(odd ? v[0] : v[2]);
           const float r1 = lane_pair_swap(odd ? v[1] : v[3]);
           const float a0 = odd ? swiglu(r0, v[2]) : swiglu(v[0], r0);
@@ -630,6 +627,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
           base[(16 * i) * kEpiLd + 8 * j] = to_bf16(a0);
           base[(16 * i + 1) * kEpiLd + 8 * j] = to_bf16(a1);
         }
+      }
       __syncthreads();
       const int chunk = lane & 3;
       const int64_t O2 = O >> 1;
@@ -658,9 +656,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int q = 0; q < 4; ++q) {
+          const int ex = rowexp(16 * i + 4 * (lane >> 4) + q);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) base[(16 * i + q) * kEpiLd + 16 * j] = to_bf16(acc[i][j][q]);
+          for (int j = 0; j < 4; ++j) base[(16 * i + q) * kEpiLd + 16 * j] = to_bf16(unscale(acc[i][j][q], ex));
+        }
     }
     __syncthreads();
     {
