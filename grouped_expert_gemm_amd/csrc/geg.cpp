@@ -116,20 +116,13 @@ struct Plan {
   bool run_skinny;
   bool run_tile;
   int64_t rc_bound;        // bound on skinny row chunks
-  size_t counters_off, counters_bytes;
   size_t partials_off, partials_bytes;
   size_t a16_off, a16_bytes;   // NF4 tile path: fp16 copy of the row-scaled activations
   size_t rexp_off;             // ... followed by the rows' int32 exponents
   size_t total_bytes;
 };
 
-constexpr size_t kHeader = 256;
-// Split-K arrival counters live in a fixed region right after the header, so a
-// workspace shared by calls of different shapes never sees another call's
-// partial sums where it expects zeroed counters (the last arriver of every
-// group resets its counter to 0).
-constexpr size_t kCounterBytes = size_t(4) << 20;
-constexpr int64_t kMaxCounters = int64_t(kCounterBytes / 4);
+constexpr size_t kHeader = 256;   // the device error word, then padding
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -142,19 +135,16 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
   std::memset(&p, 0, sizeof(p));
   p.split = 1;
   if (op == GEG_OP_NF4_DGRAD) {
-    // row-scaled dY as fp16 for the tiled kernel and the rows' exponents,
-    // outside the counter region
+    // row-scaled dY as fp16 for the tiled kernel and the rows' exponents
     p.run_tile = M > 0;
-    p.a16_off = kHeader + kCounterBytes;
+    p.a16_off = kHeader;
     p.a16_bytes = round256((size_t)M * (size_t)N * 2) + round256((size_t)M * 4);
     p.rexp_off = p.a16_off + round256((size_t)M * (size_t)N * 2);
     p.total_bytes = p.a16_off + p.a16_bytes;
     return GEG_OK;
   }
-  // Scratch of every op starts past the split-K counters, which must stay zero
-  // between calls that share a workspace.
   if (op == GEG_OP_MXFP4_W4A8) {   // e4m3 codes [M, K] and their scales [M, K/32]
-    p.a16_off = kHeader + kCounterBytes;
+    p.a16_off = kHeader;
     // scales step-major, 4 per row and 128-wide k step
     p.a16_bytes = round256((size_t)M * (size_t)K) + round256((size_t)M * (size_t)((K / 32 + 3) & ~3));
     p.total_bytes = p.a16_off + p.a16_bytes;
@@ -208,20 +198,15 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
       split = std::min<int64_t>(split, std::max<int64_t>(1, ksteps / 4));
     }
     split = std::max<int64_t>(1, std::min<int64_t>(split, ksteps));
-    if (p.rc_bound * n_chunks > kMaxCounters) split = 1;
     p.split = (int32_t)split;
     if (p.split > 1) {
-      p.counters_off = kHeader;
-      p.counters_bytes = kCounterBytes;
-      p.partials_off = p.counters_off + p.counters_bytes;
+      p.partials_off = kHeader;
       p.partials_bytes = round256((size_t)p.split * (size_t)M * (size_t)N * 4);
     }
   }
-  p.total_bytes = kHeader + p.counters_bytes + p.partials_bytes;
+  p.total_bytes = kHeader + p.partials_bytes;
   if (p.run_tile && op == GEG_OP_NF4_FWD) {
-    // Never inside the counter region, even when this call has no split-K: a
-    // later split-K call on the same workspace expects its counters at zero.
-    p.a16_off = kHeader + kCounterBytes + p.partials_bytes;
+    p.a16_off = kHeader + p.partials_bytes;
     p.a16_bytes = round256((size_t)M * (size_t)K * 2) + round256((size_t)M * 4);
     p.rexp_off = p.a16_off + round256((size_t)M * (size_t)K * 2);
     p.total_bytes = p.a16_off + p.a16_bytes;
@@ -322,7 +307,6 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.cb = p.cb;
   g.vec_rows = p.vec_rows;
   g.err = scratch.err_word ? scratch.err_word : reinterpret_cast<uint32_t*>(wsb);
-  g.counters = p.split > 1 ? reinterpret_cast<int32_t*>(wsb + p.counters_off) : nullptr;
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
   g.rexp = p.a16_bytes ? reinterpret_cast<const int32_t*>(wsb + p.rexp_off) : nullptr;
@@ -370,9 +354,15 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     const int64_t bound = p.rc_bound * n_chunks * p.split;
     hipError_t e = p.run_vec ? hipSuccess : record_event(opts, 2, stream);
     if (e == hipSuccess) e = geg::launch_skinny(fmt, g, persistent_grid(bound, 2), stream);
-    if (e == hipSuccess) e = record_event(opts, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "skinny kernel launch");
     ++g_launches;
+    if (p.split > 1) {
+      e = geg::launch_splitk_reduce(g, persistent_grid(p.rc_bound, 4), stream);
+      if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
+      ++g_launches;
+    }
+    e = record_event(opts, 3, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel event");
   }
   return GEG_OK;
 }
@@ -387,8 +377,8 @@ geg_status block_layout(int fmt, int64_t M, int64_t H, int64_t I, int32_t E, con
   geg_status st;
   if ((st = make_plan(op, M, 2 * I, H, E, o, p1)) != GEG_OK) return st;
   if ((st = make_plan(op, M, H, I, E, o, p2)) != GEG_OK) return st;
-  // past both GEMMs' scratch and never inside the split-K counter region
-  act_off = round256(std::max({p1.total_bytes, p2.total_bytes, kHeader + kCounterBytes}));
+  // past both GEMMs' scratch
+  act_off = round256(std::max(p1.total_bytes, p2.total_bytes));
   total = act_off + round256((size_t)M * (size_t)I * 2);
   return GEG_OK;
 }
@@ -653,7 +643,7 @@ size_t geg_lora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int
   }
   if (op != GEG_OP_NF4_DGRAD && op != GEG_OP_MXFP4_DGRAD) return 0;
   if (make_plan(op, M, N, K, E, nullptr, p) != GEG_OK) return 0;
-  return std::max(p.total_bytes, kHeader + kCounterBytes) + round256((size_t)E * r * N * 4) +
+  return p.total_bytes + round256((size_t)E * r * N * 4) +
          round256((size_t)E * K * r * 4) + round256((size_t)M * r * 4);
 }
 
@@ -727,8 +717,8 @@ geg_status dgrad_lora(int fmt, const void* dy, const int32_t* sizes, const uint8
     return st;
   uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
   uint32_t* err = reinterpret_cast<uint32_t*>(wsb);
-  // adapter scratch past the dgrad's own and past the split-K counter region
-  const size_t lb = std::max(p.total_bytes, kHeader + kCounterBytes);
+  // adapter scratch past the dgrad's own
+  const size_t lb = p.total_bytes;
   float* Bt = reinterpret_cast<float*>(wsb + lb);                                    // [E, r, N]
   float* At = reinterpret_cast<float*>(wsb + lb + round256((size_t)E * r * N * 4));  // [E, K, r]
   float* g = reinterpret_cast<float*>(wsb + lb + round256((size_t)E * r * N * 4) +
@@ -808,9 +798,8 @@ geg_status gmxfp4_grouped_dgrad_lora(const void* dy, const int32_t* sizes, const
 size_t geg_route_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0 || E > geg::kMaxExperts) return 0;
   const int64_t nchunks = (T * k + geg::kThreads - 1) / geg::kThreads;
-  // chunk counts past the split-K counter region (a workspace shared with the
-  // grouped GEMM keeps its counters at zero)
-  return kHeader + kCounterBytes + round256((size_t)std::max<int64_t>(nchunks, 1) * (size_t)E * 4);
+  // per-chunk expert counts after the header
+  return kHeader + round256((size_t)std::max<int64_t>(nchunks, 1) * (size_t)E * 4);
 }
 
 geg_status geg_route_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
@@ -839,7 +828,7 @@ geg_status geg_route_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t
     if ((st = check_device_ptr(ptr, name)) != GEG_OK) return st;
   uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
   const int64_t n = T * k;
-  hipError_t e = geg::launch_route_sort(topk_ids, n, E, reinterpret_cast<int32_t*>(wsb + kHeader + kCounterBytes), sizes,
+  hipError_t e = geg::launch_route_sort(topk_ids, n, E, reinterpret_cast<int32_t*>(wsb + kHeader), sizes,
                                         row_of, src_of, reinterpret_cast<uint32_t*>(wsb), stream);
   if (e != hipSuccess) return hip_fail(e, "routing sort launch");
   g_launches += n > 0 ? 3 : 1;
@@ -893,8 +882,8 @@ geg_status geg_workspace_init(void* workspace, size_t workspace_bytes, hipStream
   geg_status st;
   if ((st = check_device()) != GEG_OK) return st;
   if ((st = check_device_ptr(workspace, "workspace")) != GEG_OK) return st;
-  // Only the error word and the split-K counters must start at zero.
-  const size_t zero_bytes = std::min(workspace_bytes, kHeader + kCounterBytes) & ~size_t(3);
+  // Only the error word must start at zero.
+  const size_t zero_bytes = kHeader;
   hipError_t e = geg::launch_zero(workspace, zero_bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "workspace zero launch");
   ++g_launches;

@@ -56,7 +56,6 @@ struct GemmArgs {
   int32_t vec_rows;       // vector path takes experts with 1..vec_rows rows (0: none);
                           // the skinny path takes vec_rows+1..thresh
   uint32_t* err;          // device error word
-  int32_t* counters;      // split-K arrival counters
   float* partials;        // split-K partials [split, M, N]
   int32_t glu;            // 1: columns 2i, 2i+1 are (gate, up) of unit i and out is
                           // [M, N/2] with out[m, i] = bf16(silu(gate) * up)
@@ -72,6 +71,7 @@ struct GemmArgs {
 
 // Each launcher returns the hipError_t of its launch.
 hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s);
+hipError_t launch_splitk_reduce(const GemmArgs& g, int grid, hipStream_t s);   // after a skinny split > 1
 hipError_t launch_vec(int fmt, const GemmArgs& g, int cus, hipStream_t s);      // sizes its own grid
 hipError_t launch_narrow(int fmt, const GemmArgs& g, int cus, hipStream_t s);   // sizes its own grid
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
@@ -116,7 +116,7 @@ hipError_t launch_to_f16_rows(const uint16_t* a, uint16_t* a16, int32_t* rexp, i
 // GPU's static array (looked up and its first kNoallocZeroBytes zeroed on `stream`
 // at the first call on each device).
 constexpr size_t kNoallocScratchBytes = size_t(144) << 20;
-constexpr size_t kNoallocZeroBytes = 256 + (size_t(4) << 20);   // header + split-K counters
+constexpr size_t kNoallocZeroBytes = 256;   // the header (error word)
 hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
 
 }  // namespace geg

@@ -35,9 +35,8 @@ hipError_t noalloc_scratch(void** ptr, hipStream_t stream) {
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
-    // The split-K counters (and the unused header word) must start at zero; every
-    // completed call leaves them at zero afterwards. A fill kernel, not a memset,
-    // so that a first call under graph capture records a plain kernel node.
+    // The header's error word starts at zero. A fill kernel, not a memset, so
+    // that a first call under graph capture records a plain kernel node.
     e = launch_zero(p, kNoallocZeroBytes, stream);
     if (e != hipSuccess) return e;
     g_ptr[dev] = p;

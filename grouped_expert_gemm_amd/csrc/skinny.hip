@@ -17,9 +17,9 @@
 // weight bytes (in groups of D steps, the next group in flight while the current
 // one is decoded), so one pass over the grid keeps the whole weight stream in
 // flight. With S > 1 (split-K across workgroups, listed by the capability index
-// under system_manifest.owns) every unit writes fp32 partials and the last unit
-// of a group to arrive adds the S partials in order s = 0..S-1, so results never
-// depend on arrival order.
+// under system_manifest.owns) every unit writes fp32 partials of its K range and
+// a second launch adds the S partials in order s = 0..S-1, so results never
+// depend on which workgroup finished first.
 //
 // NF4: codes decode through an unscaled fp16 copy of the table; the fp32 absmax
 // multiplies the fp32 MFMA partial sum of each 64-wide block (all 32 k of an MFMA
@@ -308,7 +308,6 @@ template <Fmt F, int CB>
 __global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) uint16_t As[kALdsHalves];
-  __shared__ int s_last;
   // After the K loop the activation buffer holds the cross-wavefront partial sums.
   f32x4 (*red)[2 * CB][64] = reinterpret_cast<f32x4 (*)[2 * CB][64]>(As);
   static_assert((kWaves - 1) * 2 * CB * 64 * sizeof(f32x4) <= sizeof(As), "reduction buffer");
@@ -342,7 +341,6 @@ __global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
     lu /= S;
     const int chunk = lu % n_chunks;
     const int rcl = lu / n_chunks;
-    const int32_t rc_global = plan.upre[e] / (n_chunks * S) + rcl;
     const int64_t row0 = (int64_t)plan.off[e] + (int64_t)rcl * kSkinnyRows;
     const int rows = min(kSkinnyRows, (int)(plan.off[e + 1] - row0));
     const int r8 = (rows + 7) & ~7;
@@ -363,31 +361,40 @@ __global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
       unit_store<CB, 2>(g, acc, red, wave, lane, kg, row0, rows, n0, ks);
     }
 
-    if (S > 1) {
-      __threadfence();
-      __syncthreads();
-      int32_t* ctr = g.counters + (int64_t)rc_global * n_chunks + chunk;
-      if (threadIdx.x == 0) s_last = (atomicAdd(ctr, 1) == S - 1);
-      __syncthreads();
-      if (s_last) {
-        __threadfence();
-        const int64_t c0 = (int64_t)chunk * cols;
-        for (int q = threadIdx.x; q < rows * cols; q += kThreads) {
-          const int lr = q / cols;
-          const int64_t c = c0 + q % cols;
-          if (c < g.N) {
-            float sum = 0.f;
-            for (int s = 0; s < S; ++s) sum += g.partials[((int64_t)s * g.M + row0 + lr) * g.N + c];
-            g.out[(row0 + lr) * g.N + c] = to_bf16(sum);
-          }
-        }
-        if (threadIdx.x == 0) *ctr = 0;  // ready for the next call on this workspace
-      }
-    }
-    __syncthreads();  // red[] and s_last are reused by the next unit
+    __syncthreads();  // red[] is reused by the next unit
   }
   if constexpr (F == NF4) {
     if (range_overflowed(range)) atomicOr(g.err, kErrFp16Range);
+  }
+}
+
+// Split-K reduce (S > 1): out[row, n] = bf16(partials[0, row, n] + ... +
+// partials[S - 1, row, n]), added in that order, for every row of the experts the
+// skinny kernel took. A launch of its own: the kernel boundary orders every
+// partial store before these loads on all XCDs, where a reduction by the last
+// workgroup to arrive would need a device-scope release, a write-back of its
+// XCD's L2, from every unit. One unit = one chunk of kSkinnyRows rows of one
+// expert, all N columns.
+__global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(GemmArgs g) {
+  __shared__ Plan plan;
+  const int32_t thresh = g.thresh;
+  const int64_t lo = max<int64_t>(1, (int64_t)g.vec_rows + 1);
+  const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
+    return (s < lo || s > thresh) ? 0 : (s + kSkinnyRows - 1) / kSkinnyRows;
+  });
+  const int S = g.split;
+  const int64_t slice = g.M * g.N;
+  for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int e = find_expert(plan, g.E, u);
+    const int64_t row0 = (int64_t)plan.off[e] + (int64_t)(u - plan.upre[e]) * kSkinnyRows;
+    const int64_t n_el = min<int64_t>(kSkinnyRows, plan.off[e + 1] - row0) * g.N;
+    const float* p = g.partials + row0 * g.N;
+    uint16_t* o = g.out + row0 * g.N;
+    for (int64_t q = threadIdx.x; q < n_el; q += kThreads) {
+      float sum = p[q];
+      for (int s = 1; s < S; ++s) sum += p[s * slice + q];
+      o[q] = to_bf16(sum);
+    }
   }
 }
 
@@ -405,6 +412,11 @@ hipError_t launch_fmt(const GemmArgs& g, int grid, hipStream_t s) {
 
 hipError_t launch_skinny(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
   return fmt == NF4 ? launch_fmt<NF4>(g, grid, s) : launch_fmt<MXFP4>(g, grid, s);
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& g, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
 }
 
 }  // namespace geg

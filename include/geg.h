@@ -59,16 +59,14 @@
  *    be below 2^31.
  *  - Workspace: `workspace` is a caller-allocated device buffer of at least
  *    geg_workspace_bytes(...) bytes, 256-byte aligned, zeroed once by
- *    geg_workspace_init before its first use. It holds the device error word,
- *    split-K arrival counters (a fixed 4 MiB region after the 256-byte header,
- *    left zeroed by every completed call, and never written by any other op,
- *    so one workspace can serve every entry point), split-K partials and, for
- *    the NF4 tiled path, an fp16 copy of the row-scaled activations (M * K * 2
- *    bytes; dgrad: of dY, M * N * 2 bytes) and the rows' int32 exponents (M * 4
- *    bytes), both rewritten by every call; every op's other
- *    scratch also lies past the counter region; calls
- *    on one workspace must be ordered (same stream); concurrent calls must not
- *    share one.
+ *    geg_workspace_init before its first use. It holds the device error word
+ *    (in a 256-byte header), then the call's scratch, all of it written before
+ *    it is read by every call, so one workspace can serve every entry point:
+ *    split-K partials (fp32 [split, M, N]) and, for the NF4 tiled path, an fp16
+ *    copy of the row-scaled activations (M * K * 2 bytes; dgrad: of dY,
+ *    M * N * 2 bytes) and the rows' int32 exponents (M * 4 bytes). Calls on one
+ *    workspace must be ordered (same stream); concurrent calls must not share
+ *    one.
  */
 #ifndef GEG_H_
 #define GEG_H_
@@ -81,7 +79,7 @@
 extern "C" {
 #endif
 
-#define GEG_VERSION 110 /* 1.1.0 */
+#define GEG_VERSION 111 /* 1.1.1 */
 
 typedef enum {
   GEG_OK = 0,
@@ -161,12 +159,12 @@ geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t*
  * gnf4_grouped_gemm_noalloc — gnf4_grouped_gemm for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same operation, arguments and paths, without the
- * workspace. The call allocates nothing. Its scratch (split-K counters and
- * partials, the row-scaled fp16 activations and their row exponents) lives in a
- * library-held static device array of 144 MiB per GPU, created when the
- * library's code is loaded on that GPU and held until the process ends; its first
- * 4 MiB + 256 bytes are zeroed by a fill kernel on `stream` at the first call on
- * each GPU and left at zero by every completed call.
+ * workspace. The call allocates nothing. Its scratch (split-K partials, the
+ * row-scaled fp16 activations and their row exponents) lives in a library-held
+ * static device array of 144 MiB per GPU, created when the library's code is
+ * loaded on that GPU and held until the process ends; its 256-byte header is
+ * zeroed by a fill kernel on `stream` at the first call on each GPU, and every
+ * call writes the rest before reading it.
  *   error_word  device uint32 (4-B aligned) that receives the GEG_DEVERR_* bits of
  *               this call (OR-ed in; the caller clears it), or NULL to drop them
  *   A call whose scratch (geg_workspace_bytes(GEG_OP_NF4_FWD, M, N, K, E, opts))
@@ -371,7 +369,7 @@ geg_status gmxfp4_grouped_dgrad_lora(const void* dy, const int32_t* sizes, const
 size_t geg_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t E,
                            const geg_opts* opts);
 
-/* Zero a workspace (error word and counters) on `stream`; call once after allocating it. */
+/* Zero a workspace's error word on `stream`; call once after allocating it. */
 geg_status geg_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Synchronise `stream`, then copy the device error word (GEG_DEVERR_* bits) to *code. */

@@ -25,7 +25,7 @@ def test_library_exports_every_header_function():
 
 
 def test_version_and_status_strings():
-    assert L().geg_version() == 110
+    assert L().geg_version() == 111
     assert L().geg_status_string(0) == b"GEG_OK"
     assert L().geg_status_string(5) == b"GEG_ERR_WORKSPACE"
 
@@ -105,23 +105,22 @@ def test_misaligned_pointers_are_refused():
 def test_small_workspace_is_refused():
     o = geg.Opts(1, 4)                              # skinny path, 4 K splits
     need = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, o)
-    assert need > 256                               # split-K needs counters and partials
+    assert need > 256                               # split-K needs its partials
     assert _gemm(M=8, N=2048, K=2048, E=64, ws_bytes=need - 256, opts=o) == 5
     assert b"workspace" in L().geg_last_error()
 
 
 def test_workspace_sizes():
-    # NF4 prefill: the 256-byte header (error word), the split-K counter region
-    # (kept clear of other data) and the fp16 copy of the activations that the
-    # tiled path reads; MXFP4 reads bf16 activations as given
-    # (plus the rows' int32 exponents of the row-scaled copy)
+    # NF4 prefill: the 256-byte header (error word), then the fp16 copy of the
+    # activations that the tiled path reads and the rows' int32 exponents;
+    # MXFP4 reads bf16 activations as given
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == \
-        256 + (4 << 20) + 16384 * 2048 * 2 + 16384 * 4
+        256 + 16384 * 2048 * 2 + 16384 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == \
-        256 + (4 << 20) + 8192 * 28672 * 2 + 8192 * 4
+        256 + 8192 * 28672 * 2 + 8192 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 3000, 2048, 64, 4) == \
-        256 + (4 << 20) + 3000 * 64 * 2 + ((3000 * 4 + 255) & ~255)
+        256 + 3000 * 64 * 2 + ((3000 * 4 + 255) & ~255)
     # skinny split-K partials; a small batch on the automatic path goes to the
     # vector path, which needs nothing beyond the header
     one = geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8, 2048, 2048, 64, geg.Opts(1, 1))
@@ -178,9 +177,10 @@ def test_python_binding_checks_operand_types_and_shapes():
         geg.gmxfp4_grouped_dgrad(dy, sizes, w, mx_s)
 
 
-def test_scratch_lies_past_the_counter_region():
-    # routing counts and the adapter backward's scratch never share bytes with the
-    # split-K counters [256, 256 + 4 MiB)
-    assert geg.lib().geg_route_workspace_bytes(64, 8, 64) >= 256 + (4 << 20) + 2 * 64 * 4   # 512 entries: 2 chunks
-    assert geg.lib().geg_lora_workspace_bytes(geg.GEG_OP_MXFP4_DGRAD, 64, 128, 256, 4, 8) >= 256 + (4 << 20)
-    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_W4A8, 64, 128, 256, 4) >= 256 + (4 << 20) + 64 * 256
+def test_scratch_lies_past_the_header():
+    # routing counts, the adapter backward's scratch and the W4A8 codes start
+    # after the 256-byte header that holds the error word
+    assert geg.lib().geg_route_workspace_bytes(64, 8, 64) == 256 + 2 * 64 * 4   # 512 entries: 2 chunks
+    assert geg.lib().geg_lora_workspace_bytes(geg.GEG_OP_MXFP4_DGRAD, 64, 128, 256, 4, 8) == \
+        256 + 4 * 8 * 128 * 4 + 4 * 256 * 8 * 4 + 64 * 8 * 4
+    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_W4A8, 64, 128, 256, 4) >= 256 + 64 * 256

@@ -1,8 +1,8 @@
 """One workspace shared by every entry point that writes scratch (W4A8 codes,
 routing chunk counts, the fused block's intermediate, the adapter backward's
-transposed weights), then a split-K decode GEMM on the same workspace: its
-arrival counters must still be zero, so its output matches the oracle.
-Regression test for scratch that once overlapped the counter region."""
+transposed weights), then a split-K decode GEMM on the same workspace: whatever
+the earlier calls left there, its output matches the oracle (every call writes
+its scratch before reading it)."""
 import numpy as np
 import pytest
 
@@ -13,12 +13,12 @@ from gpu_util import assert_close, bf16_to_f64, log, up, up_u16_as_bf16
 pytestmark = pytest.mark.gpu
 
 
-def test_shared_workspace_keeps_split_k_counters(geg_mod):
+def test_shared_workspace_then_split_k(geg_mod):
     geg = geg_mod
     import torch
     rng = np.random.default_rng(31)
     ws = geg.Workspace(64 << 20)
-    # W4A8 (codes right after the counters), routing sort, adapter backward
+    # W4A8 (codes right after the header), routing sort, adapter backward
     E, K, N, M = 4, 256, 128, 64
     sizes = np.array([20, 0, 30, 14], np.int32)
     a = up_u16_as_bf16(synthetic.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
