@@ -27,8 +27,9 @@ Prints ONE JSON line:
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
 Other workloads time one configuration's prefill and decode calls (olmoe,
-qwen3, ...), the fused expert block (*_block), the adapter step (olmoe_lora) or
-the W4A8 variant (*_w4a8).
+qwen3, ...), the fused expert block (*_block), the adapter step (olmoe_lora),
+the W4A8 variant (*_w4a8), or every decode path on the headline decode cases
+(decode_paths: vector, narrow, skinny with K split 1, 2, 4 and 8 ways).
 """
 from __future__ import annotations
 
@@ -779,13 +780,61 @@ def main_headline(args, torch, geg, synthetic):
     print(json.dumps(result), flush=True)
 
 
+DECODE_PATHS = [("auto", 0, 0), ("vector", 3, 0), ("narrow", 4, 0), ("skinny_s1", 1, 1), ("skinny_s2", 1, 2),
+                ("skinny_s4", 1, 4), ("skinny_s8", 1, 8)]
+
+
+def main_decode_paths(args, torch, geg, synthetic):
+    """Every decode path on every headline decode case: the automatic choice, the
+    vector and narrow kernels, and the skinny kernel with K split S = 1, 2, 4, 8
+    ways (S > 1 adds the fixed-order reduce launch), beside a copy of the same
+    bytes; per-call time from a HIP graph of back-to-back calls."""
+    dev = torch.device("cuda", 0)
+    steps = max(args.steps, 50)
+    cases = {}
+    for name in HEADLINE_DECODE:
+        c = synthetic.case(name)
+        a_bits, sizes = synthetic.rows_bf16(c, args.seed)
+        a = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        sz = torch.from_numpy(sizes).to(dev)
+        cps = rotated_copies(make_weights(c, args.seed, torch, geg, dev, np.nonzero(sizes)[0]))
+        out = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+        ws = geg.Workspace(64 << 20)
+        fn = geg.gnf4_grouped_gemm if c.fmt == "nf4" else geg.gmxfp4_grouped_gemm
+        nbytes = touched_weight_bytes(c, sizes)
+        res = {"weight_bytes": nbytes, "max_rows": int(sizes.max())}
+        for vname, fp, sk in DECODE_PATHS:
+            if vname == "vector" and int(sizes.max()) > 8:
+                continue   # the vector kernel takes experts of at most 8 rows
+            o = geg.Opts(force_path=fp, split_k=sk, kernel_events=None, cu_limit=0)
+
+            def call(wc, opts=None, o=o):
+                fn(a, sz, wc[0], wc[1], out=out, workspace=ws, opts=o)
+            call(cps[0])
+            torch.cuda.synchronize()
+            assert ws.read_error() == 0, f"device error word set ({name}, {vname})"
+            ms, _ = time_calls(call, cps, steps, args.warmup, torch)
+            res[vname] = {"us": round(float(np.mean(ms)) * 1e3, 3),
+                          "gbps": round(nbytes / (float(np.mean(ms)) * 1e-3) / 1e9, 1)}
+        res["copy_of_same_bytes_us"] = round(copy_floor_ms(nbytes, steps, args.warmup, torch, dev) * 1e3, 3)
+        cases[name] = res
+        print(f"bench.py: {name} " + json.dumps(res), file=sys.stderr, flush=True)
+        del cps
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode call time per path (us)", "value": None, "unit": "us", "n_gpus": 1,
+                      "steps": steps, "warmup": args.warmup, "higher_is_better": False, "data": "synthetic",
+                      "timing": f"hip graph of {steps} calls, 5 replays", "cases": cases,
+                      "kernel_sha": kernel_sha()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
-                    choices=["headline"] + sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS) + sorted(LORA_WORKLOADS))
+                    choices=["headline", "decode_paths"] + sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS)
+                    + sorted(LORA_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -816,6 +865,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "headline":
         main_headline(args, torch, geg, synthetic)
+        return
+    if args.workload == "decode_paths":
+        main_decode_paths(args, torch, geg, synthetic)
         return
     if args.workload in BLOCK_WORKLOADS:
         main_block(args, torch, geg, synthetic)

@@ -52,7 +52,7 @@ class GegError(RuntimeError):
 
 class Opts(ctypes.Structure):
     """geg_opts: force_path 0 auto / 1 skinny / 2 tiled / 3 vector / 4 narrow; split_k 0
-    auto / 1..16 (skinny); kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end,
+    or 1 none / 2..16 (skinny); kernel_events: NULL or a pointer to 4 hipEvent_t (tile start/end,
     decode start/end) recorded around the call's kernels; cu_limit 0, or n > 0 to size every
     grid for at most n compute units (persistent loops then run more rounds; for tests)."""
     _fields_ = [("force_path", ctypes.c_int32), ("split_k", ctypes.c_int32),

@@ -175,8 +175,6 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
   const int64_t ksteps = (K + geg::kKStep - 1) / geg::kKStep;
   if (p.run_skinny && !p.narrow) {
     const int64_t skinny_experts = std::min<int64_t>(E, M);
-    // Widest column block (fewest re-reads of the staged activations) that still
-    // gives about one workgroup per compute unit.
     // The narrowest column block whose units still fit in one round of resident
     // workgroups (two per CU): smaller units finish sooner, a second round costs
     // a whole unit's latency chain. When none fits, the widest (fewest units).
@@ -187,16 +185,13 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
         break;
       }
     }
-    const int64_t n_chunks = (N + 16 * p.cb - 1) / (16 * p.cb);
     p.rc_bound = (M + geg::kSkinnyRows - 1) / geg::kSkinnyRows + skinny_experts;
-    int64_t split = split_req;
-    if (split == 0) {
-      // Split K across workgroups only when there are too few units to fill
-      // the chip (each workgroup already splits K over its 4 wavefronts).
-      const int64_t units = skinny_experts * n_chunks;
-      split = (M <= 1024 && units < 128) ? std::min<int64_t>(8, (256 + units - 1) / units) : 1;
-      split = std::min<int64_t>(split, std::max<int64_t>(1, ksteps / 4));
-    }
+    // K is split across workgroups only on request: on every decode shape
+    // measured (T = 1 and 64 of OLMoE, Qwen3 and gpt-oss) each split of 2, 4 or
+    // 8 was slower than no split (its reduce launch and the partials' round
+    // trip cost more than the shorter per-unit chains save), and the skinny
+    // kernel itself is slower there than the vector and narrow kernels.
+    int64_t split = split_req == 0 ? 1 : split_req;
     split = std::max<int64_t>(1, std::min<int64_t>(split, ksteps));
     p.split = (int32_t)split;
     if (p.split > 1) {

@@ -108,7 +108,8 @@ typedef struct {
    * expert on the vector path (experts with more than 4 rows in chunks of 4);
    * 4 every expert on the narrow kernel (in chunks of 16 or 32 rows) */
   int32_t force_path;
-  int32_t split_k;    /* 0 auto; 1..16 K splits of the skinny kernel (force_path 1)            */
+  int32_t split_k;    /* 0 or 1: no split; 2..16 K splits of the skinny kernel (force_path 1),  */
+                      /* summed in a fixed order by a second launch                          */
   /* Optional kernel timing: NULL, or 4 events (entries may be NULL) that the call
    * records on `stream` right before and after its tiled kernel (dgrad: the dgrad
    * kernel) and right before and after its decode kernels (vector and skinny, in
