@@ -352,7 +352,8 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     if (e != hipSuccess) return hip_fail(e, "skinny kernel launch");
     ++g_launches;
     if (p.split > 1) {
-      e = geg::launch_splitk_reduce(g, persistent_grid(p.rc_bound, 4), stream);
+      // units: (row of a skinny expert, 256 columns); at most M rows
+      e = geg::launch_splitk_reduce(g, persistent_grid(M * ((N + geg::kThreads - 1) / geg::kThreads), 8), stream);
       if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
       ++g_launches;
     }

@@ -373,28 +373,34 @@ __global__ __launch_bounds__(kThreads, 2) void skinny_kernel(GemmArgs g) {
 // skinny kernel took. A launch of its own: the kernel boundary orders every
 // partial store before these loads on all XCDs, where a reduction by the last
 // workgroup to arrive would need a device-scope release, a write-back of its
-// XCD's L2, from every unit. One unit = one chunk of kSkinnyRows rows of one
-// expert, all N columns.
+// XCD's L2, from every unit. One unit = one row and kThreads consecutive
+// columns; each thread issues the S loads of its element before adding them.
+constexpr int kMaxSplit = 16;
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(GemmArgs g) {
   __shared__ Plan plan;
   const int32_t thresh = g.thresh;
   const int64_t lo = max<int64_t>(1, (int64_t)g.vec_rows + 1);
+  const int32_t n_blk = (int32_t)((g.N + kThreads - 1) / kThreads);
   const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
-    return (s < lo || s > thresh) ? 0 : (s + kSkinnyRows - 1) / kSkinnyRows;
+    return (s < lo || s > thresh) ? 0 : s * n_blk;
   });
   const int S = g.split;
   const int64_t slice = g.M * g.N;
   for (int32_t u = blockIdx.x; u < total; u += gridDim.x) {
     const int e = find_expert(plan, g.E, u);
-    const int64_t row0 = (int64_t)plan.off[e] + (int64_t)(u - plan.upre[e]) * kSkinnyRows;
-    const int64_t n_el = min<int64_t>(kSkinnyRows, plan.off[e + 1] - row0) * g.N;
-    const float* p = g.partials + row0 * g.N;
-    uint16_t* o = g.out + row0 * g.N;
-    for (int64_t q = threadIdx.x; q < n_el; q += kThreads) {
-      float sum = p[q];
-      for (int s = 1; s < S; ++s) sum += p[s * slice + q];
-      o[q] = to_bf16(sum);
-    }
+    const int32_t lu = u - plan.upre[e];
+    const int64_t row = (int64_t)plan.off[e] + lu / n_blk;
+    const int64_t n = (int64_t)(lu % n_blk) * kThreads + threadIdx.x;
+    if (n >= g.N) continue;
+    const float* p = g.partials + row * g.N + n;
+    float v[kMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) v[s] = s < S ? p[s * slice] : 0.f;
+    float sum = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplit; ++s)
+      if (s < S) sum += v[s];
+    g.out[row * g.N + n] = to_bf16(sum);
   }
 }
 

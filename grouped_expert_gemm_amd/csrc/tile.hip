@@ -38,17 +38,17 @@ constexpr int kXcds = 8;
 constexpr int kTileThreads = 512;
 constexpr int kTileWaves = kTileThreads / 64;
 constexpr int kEpiLd = 64 + 8;  // epilogue row stride in halves (144 B)
-constexpr int kLdT = 80;        // dgrad weight rows in LDS: 64 halves + 16 pad (160 B)
+constexpr int kLdB = BN + 16;   // dgrad weight-tile row stride in halves (544 B)
 
 // LDS of one workgroup: two stages of activation and weight tiles, or the
-// epilogue's result blocks. The dgrad weight tile is written transposed (one
-// contraction index per lane, scattered over 256 rows), so its rows are padded
-// instead of swizzled (a 160-byte stride keeps the operand reads conflict-free).
+// epilogue's result blocks. Forward weight tiles hold 256 weight rows of 64 k;
+// dgrad weight tiles hold the stage's 64 weight rows (the contraction) of 256
+// output columns, both as written by the staging threads.
 template <bool DG>
 union TileLds {
   struct {
     uint16_t a[2][BM * BK];
-    uint16_t b[2][BN * (DG ? kLdT : BK)];
+    uint16_t b[2][DG ? BK * kLdB : BN * BK];
   };
   uint16_t epi[kTileWaves][128 * kEpiLd];  // per-wavefront bf16 result block
 };
@@ -65,12 +65,23 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * BK + ((chunk ^ (row & 7)) << 3);
 }
 
-// Weight-tile offset of (row, chunk): swizzled rows for the forward pass, padded
-// rows for dgrad.
-template <bool DG>
-__device__ __forceinline__ int bpos(int row, int chunk) {
-  return DG ? row * kLdT + chunk * 8 : swz(row, chunk);
-}
+// dgrad weight tile: rows of 256 output columns plus 16 halves of padding
+// (544 B), one per weight row of the stage (contraction slot s, 0..63) at row
+// position dg_pos(s). The MFMA operand needs the transpose (8 contraction rows of
+// one output column per lane), which gfx950's transposing LDS read provides:
+// within each 16-lane group, lane L reads 8 bytes, and lane i receives element
+// i % 4 of the reads of lanes 4 j + i / 4, j = 0..3 (measured). So lane L of a
+// group reads slot s0 + L / 4 at columns c0 + 4 (L % 4); lane i then holds
+// column c0 + i of slots s0..s0+3. A 32-lane pass reads slots 8 g + 4 h + i
+// (g = 0, 1; i = 0..3) of one column block: dg_pos swaps bits 2 and 3 of the
+// slot so that they are 8 consecutive positions, which the 544-byte stride
+// spreads over the 8 disjoint 32-byte bank groups; column blocks and substeps
+// are plain offsets. (The 16-byte stores of 16 consecutive slots meet 2-way.)
+__device__ __forceinline__ int dg_pos(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
+// dgrad output column of MFMA column c (0..15) within a 16-column block: NF4
+// stages each 8-column chunk in the slot order [0, 2, 4, 6, 1, 3, 5, 7].
+__device__ __forceinline__ int dg_col(int c) { return (c & 8) | ((c & 3) << 1) | ((c >> 2) & 1); }
 
 // Where a tile's operands come from. Loads go through buffer resources whose
 // record count bounds every access: rows past the expert's last row and weight
@@ -257,27 +268,21 @@ __device__ __forceinline__ u32x2 nf4_half_out(const Lut16& t, const NF4Half& h) 
   return u32x2{perm(hi, h.lo, 0x05010400u), perm(hi, h.lo, 0x07030602u)};
 }
 
-// dgrad: the four values of a half go to LDS rows k = 32 (t/64) + 8 q + 2 i + odd
-// (i = 0..3) at the thread's column `bcol` (2-byte stores).
-__device__ __forceinline__ void dg_store_half(uint16_t* Bs, int q, int odd, int bcol, u32x2 v) {
-  uint16_t* p = Bs + (32 * (threadIdx.x >> 6) + 8 * q + odd) * kLdT + bcol;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[2 * i * kLdT] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
-}
-
 // Staging step r (0..2) of the thread's weight piece q (its 8 codes r.c[q]):
 // NF4 r = 0 selects the even-k codes and looks up their low bytes, r = 1
 // finishes them and selects the odd-k codes, r = 2 finishes the piece and stores
 // it; MXFP4 decodes and stores the whole piece at r = 0. Each step is 7-8 VALU
 // instructions, so that two steps fit under the four MFMAs of a group.
 // Forward: row t/2, chunk 4 (t%2) + q, one 16-byte store in slot order. dgrad:
-// the codes are columns k = 32 (t/64) + 8 q + j of weight row n = t%64; each
-// value goes to LDS row k at the slot of n.
+// the codes are output columns 32 (t/64) + 8 q + j of weight row n = t%64, one
+// 16-byte store into chunk 4 (t/64) + q of the weight row's LDS row `brow` (the
+// row's contraction slot).
 template <Fmt F, bool DG>
 __device__ __forceinline__ void b_step(int q, int r, const RawB& rb, const BDec<F>& d, NF4Half& h,
-                                       u32x2& even, uint16_t* Bs, int bcol, uint32_t m4,
+                                       u32x2& even, uint16_t* Bs, int brow, uint32_t m4,
                                        uint32_t base) {
   const int t = threadIdx.x;
+  const int bo = DG ? dg_pos(brow) * kLdB + (4 * (t >> 6) + q) * 8 : swz(t >> 1, 4 * (t & 1) + q);
   if constexpr (F == NF4) {
     const uint32_t x = rb.c[q];
     if (r == 0) {
@@ -285,31 +290,46 @@ __device__ __forceinline__ void b_step(int q, int r, const RawB& rb, const BDec<
       nf4_half_lo(d.lut, h);
     } else if (r == 1) {
       even = nf4_half_out(d.lut, h);
-      if constexpr (DG) dg_store_half(Bs, q, 0, bcol, even);
       nf4_half_select<false>(x, m4, base, h);
     } else {
       nf4_half_lo(d.lut, h);
       const u32x2 odd = nf4_half_out(d.lut, h);
-      if constexpr (DG)
-        dg_store_half(Bs, q, 1, bcol, odd);
-      else
-        *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = u32x4{even[0], even[1], odd[0], odd[1]};
+      *reinterpret_cast<u32x4*>(&Bs[bo]) = u32x4{even[0], even[1], odd[0], odd[1]};
     }
   } else if (r == 0) {
-    const u32x4 v = mxfp4_decode8(rb.c[q], d.sc);   // k = 8q + j, natural order
-    if constexpr (DG) {
-      // column n of rows k = 32 (t/64) + 8 q + j (2-byte stores)
-      uint16_t* p = Bs + (32 * (t >> 6) + 8 * q) * kLdT + bcol;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p[j * kLdT] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
-    } else {
-      *reinterpret_cast<u32x4*>(&Bs[swz(t >> 1, 4 * (t & 1) + q)]) = v;
-    }
+    *reinterpret_cast<u32x4*>(&Bs[bo]) = mxfp4_decode8(rb.c[q], d.sc);   // k = 8q + j, natural order
   }
 }
 
 __device__ __forceinline__ u32x4 lds_frag(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ u32x2 lds_tr4(lds_u16* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A wavefront's weight-operand read offsets (halves, from a stage buffer).
+// Forward: the fragment of substep s and column block j is one 16-byte read at
+// off ^ 32 s + 16 j rows. dgrad: two transposing reads (contraction slots
+// 8 g + 0..3 and 8 g + 4..7 of the substep, g = lane / 16) per column block j,
+// at off[h] + 16 j (+ 32 rows in substep 1).
+template <bool DG> struct BRd { uint32_t off; };
+template <> struct BRd<true> { uint32_t off[2]; };
+
+template <bool DG>
+__device__ __forceinline__ u32x4 b_frag(const uint16_t* Bbuf, const BRd<DG>& br, int sub, int j) {
+  if constexpr (DG) {
+    lds_u16* p = (lds_u16*)const_cast<uint16_t*>(Bbuf);   // the stage buffer, as an LDS address
+    const u32x2 lo = lds_tr4(p + br.off[0] + (sub * (32 * kLdB) + 16 * j));
+    const u32x2 hi = lds_tr4(p + br.off[1] + (sub * (32 * kLdB) + 16 * j));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    return lds_frag(Bbuf + (sub ? br.off ^ 32u : br.off) + 16 * BK * j);
+  }
 }
 
 // The 4 MFMAs of one 16-row A fragment with the substep's 4 B fragments.
@@ -345,21 +365,17 @@ struct Ops {
 // H = number of the wavefront's 64-row halves that hold rows of the expert.
 template <Fmt F, bool DG, bool TAIL, int H, int P>
 __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
-                                           int st, int nst, int wave, int lane, int bcol,
+                                           int st, int nst, int wave, int lane, int brow,
                                            RawA& ra, RawB (&rb)[2], BDec<F>& dec, Ops& ops,
-                                           f32x4 (&acc)[8][4], uint32_t aoff, uint32_t boff,
+                                           f32x4 (&acc)[8][4], uint32_t aoff, const BRd<DG>& br,
                                            uint32_t m4, uint32_t base) {
   constexpr int cur = P, nxt = P ^ 1;   // st % 2 == P
   const int64_t k1 = (int64_t)(st + 1) * BK;
   // Substep 1 reads chunk 4 + c where substep 0 reads chunk c: the swizzled
-  // chunk differs in bit 2, i.e. the half offset differs in bit 5 (the padded
-  // dgrad weight rows are plainly 32 halves further).
+  // chunk differs in bit 2, i.e. the half offset differs in bit 5.
   const uint16_t* A0 = L.a[cur] + aoff;
   const uint16_t* A1 = L.a[cur] + (aoff ^ 32u);
-  const uint16_t* B1 = L.b[cur] + (DG ? boff + 32u : boff ^ 32u);
   const uint16_t* An = L.a[nxt] + aoff;
-  const uint16_t* Bn = L.b[nxt] + boff;
-  constexpr int BR = 16 * (DG ? kLdT : BK);   // B fragment stride (16 rows)
   constexpr int NI = 4 * H;                   // A fragments per substep
   u32x4 af[16];      // A fragment of group g (substep g / 8, rows 16 (g % 8))
   u32x4 b1[4];
@@ -379,11 +395,11 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
     }
     if (NI > 0 && g == 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b1[j] = lds_frag(B1 + BR * j);
+      for (int j = 0; j < 4; ++j) b1[j] = b_frag<DG>(L.b[cur], br, 1, j);
     }
     if (NI > 0 && g == 14) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(Bn + BR * j);
+      for (int j = 0; j < 4; ++j) ops.b[j] = b_frag<DG>(L.b[nxt], br, 0, j);
     }
     if (g == 14 && NI > 0) ops.a[0] = lds_frag(An);
     if (g == 15 && NI > 1) ops.a[1] = lds_frag(An + 16 * BK);
@@ -397,7 +413,7 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
     }
     if (g == 0 || g == 1) b_setup<F, DG>(dec, g + 2, rb[P ^ 1], k1, K);
     if (g >= 2 && g < 14) {
-      b_step<F, DG>((g - 2) / 3, (g - 2) % 3, rb[P ^ 1], dec, h, even, L.b[nxt], bcol, m4, base);
+      b_step<F, DG>((g - 2) / 3, (g - 2) % 3, rb[P ^ 1], dec, h, even, L.b[nxt], brow, m4, base);
       if (g == 13) load_b<F>(rb[P ^ 1], src, st + 3, st + 3 < nst);
     }
     if (g == 13) __syncthreads();   // Y: the next stage's buffers are complete
@@ -420,11 +436,18 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
-  const uint32_t boff = (uint32_t)bpos<DG>(64 * wn + r16, lane >> 4);
-  // dgrad staging column: the weight row's contraction slot (NF4 slot order, or
+  BRd<DG> br;
+  if constexpr (DG) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      br.off[h] = (uint32_t)(dg_pos(8 * g + 4 * h + (r16 >> 2)) * kLdB + 64 * wn + 4 * (r16 & 3));
+  } else {
+    br.off = (uint32_t)swz(64 * wn + r16, lane >> 4);
+  }
+  // dgrad staging row: the weight row's contraction slot (NF4 slot order, or
   // natural order for MXFP4's bf16 operands)
-  const int bcol = F == NF4 ? ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7) : (threadIdx.x & 63);
-  constexpr int BR = 16 * (DG ? kLdT : BK);
+  const int brow = F == NF4 ? ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7) : (threadIdx.x & 63);
   const int nst = (int)((C + BK - 1) / BK);
   uint32_t m4 = 0x04040404u, base = 0x03020100u;
   asm volatile("" : "+v"(base));
@@ -448,7 +471,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int r = 0; r < 3; ++r) b_step<F, DG>(q, r, rb[0], dec, h, even, L.b[0], bcol, m4, base);
+      for (int r = 0; r < 3; ++r) b_step<F, DG>(q, r, rb[0], dec, h, even, L.b[0], brow, m4, base);
   }
   load_a(ra, src, 1, nst > 1);
   load_b<F>(rb[0], src, 2, nst > 2);
@@ -457,14 +480,14 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   __syncthreads();
   if constexpr (H > 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ops.b[j] = lds_frag(L.b[0] + boff + BR * j);
+    for (int j = 0; j < 4; ++j) ops.b[j] = b_frag<DG>(L.b[0], br, 0, j);
 #pragma unroll
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
   for (int st = 0; st < nst; st += 2) {
-    tile_stage<F, DG, TAIL, H, 0>(L, src, C, K, st, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff, m4, base);
+    tile_stage<F, DG, TAIL, H, 0>(L, src, C, K, st, nst, wave, lane, brow, ra, rb, dec, ops, acc, aoff, br, m4, base);
     if (st + 1 < nst)
-      tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, bcol, ra, rb, dec, ops, acc, aoff, boff,
+      tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, brow, ra, rb, dec, ops, acc, aoff, br,
                                     m4, base);
   }
   __syncthreads();   // the epilogue reuses the stage buffers
@@ -586,8 +609,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
         const int jj = j0 + 8 * kg;
         const bool ok = jj < r;
         Split8 bq[4];
+        // NF4 dgrad: MFMA column c of a block is output column dg_col(c)
+        const int qc = (DG && F == NF4) ? dg_col(r16) : r16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bq[j] = load8_split(RQ, (uint32_t)((16 * j + r16) * r + jj), ok);
+        for (int j = 0; j < 4; ++j) bq[j] = load8_split(RQ, (uint32_t)((16 * j + qc) * r + jj), ok);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const Split8 au = load8_split(RU, (uint32_t)((16 * i + r16) * r + jj), ok, g.lora_s,
@@ -652,7 +677,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       continue;
     }
     {
-      uint16_t* base = E + (4 * (lane >> 4)) * kEpiLd + (lane & 15);
+      uint16_t* base = E + (4 * (lane >> 4)) * kEpiLd + ((DG && F == NF4) ? dg_col(lane & 15) : (lane & 15));
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll

@@ -134,7 +134,47 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(uint32_t* __restrict__ p
 // a row's result is what unbounded fp16 range would give. Converting once here
 // rather than in every output-column tile that reads a row leaves the tiled
 // kernel a plain copy of the operand.
-//
+
+// Largest |x| of 8 bf16 values as magnitude bits (ordered like the values;
+// 0x7F80 and above are inf and NaN), folded into m.
+__device__ __forceinline__ uint32_t absmax8(const u32x4& x, uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(x[i] & 0x7FFFu, (x[i] >> 16) & 0x7FFFu));
+  return m;
+}
+
+// The row exponent floor(log2 max|x|) - 14 from the magnitude bits; a non-finite
+// row is converted unscaled and flagged.
+__device__ __forceinline__ int row_exponent(uint32_t mx, uint32_t& bad) {
+  if (mx >= 0x7F80u) {
+    bad = 1;
+    return 0;
+  }
+  if (mx >= 0x80u) return (int)(mx >> 7) - 127 - 14;
+  if (mx > 0u) return (31 - __builtin_clz(mx)) - 133 - 14;   // bf16 subnormal: mantissa * 2^-133
+  return 0;
+}
+
+// 8 bf16 values times 2^-ex as fp16, in the NF4 slot order [0, 2, 4, 6, 1, 3, 5, 7].
+__device__ __forceinline__ u32x4 conv8(const u32x4& x, int ex) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, x[i] << 16), -ex);
+    f[2 * i + 1] = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, x[i] & 0xFFFF0000u), -ex);
+  }
+  constexpr int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 h;
+    h[0] = (_Float16)f[order[2 * i]];
+    h[1] = (_Float16)f[order[2 * i + 1]];
+    r[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
+}
+
 // One row per TP = 2^tp_log2 lanes of a wavefront (64 / TP rows per wavefront);
 // lane j of a row's group takes the row's 16-byte chunks j, j + TP, ... With
 // CPL > 0 each lane holds its (at most CPL) chunks in registers between the
@@ -156,15 +196,8 @@ __global__ __launch_bounds__(kThreads) void to_f16_rows_kernel(const u32x4* __re
     const bool live = row < M;
     const u32x4* src = a + row * chunks;
     u32x4* dst = a16 + row * chunks;
-    // largest |x| of the row as bf16 magnitude bits (ordered like the values;
-    // 0x7F80 and above are inf and NaN)
     uint32_t mx = 0;
     u32x4 v[CPL > 0 ? CPL : 1];
-    auto absmax8 = [](const u32x4& x, uint32_t m) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = max(m, max(x[i] & 0x7FFFu, (x[i] >> 16) & 0x7FFFu));
-      return m;
-    };
     if constexpr (CPL > 0) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
@@ -176,42 +209,56 @@ __global__ __launch_bounds__(kThreads) void to_f16_rows_kernel(const u32x4* __re
       for (int64_t j = sub; j < chunks; j += TP) mx = absmax8(src[j], mx);
     }
     for (int o = TP >> 1; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    // exponent of the largest magnitude: floor(log2 |x|)
-    int ex = 0;
-    if (mx >= 0x7F80u) {
-      bad = 1;   // inf or NaN: converted unscaled, flagged
-    } else if (mx >= 0x80u) {
-      ex = (int)(mx >> 7) - 127 - 14;
-    } else if (mx > 0u) {
-      ex = (31 - __builtin_clz(mx)) - 133 - 14;   // bf16 subnormal: mantissa * 2^-133
-    }
+    const int ex = row_exponent(mx, bad);
     if (live && sub == 0) rexp[row] = ex;
-    auto conv = [ex](const u32x4& x) {
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, x[i] << 16), -ex);
-        f[2 * i + 1] = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, x[i] & 0xFFFF0000u), -ex);
-      }
-      constexpr int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};   // the NF4 slot order
-      u32x4 r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f16x2 h;
-        h[0] = (_Float16)f[order[2 * i]];
-        h[1] = (_Float16)f[order[2 * i + 1]];
-        r[i] = __builtin_bit_cast(uint32_t, h);
-      }
-      return r;
-    };
     if constexpr (CPL > 0) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int64_t j = sub + (int64_t)i * TP;
-        if (live && j < chunks) dst[j] = conv(v[i]);
+        if (live && j < chunks) dst[j] = conv8(v[i], ex);
       }
     } else if (live) {
-      for (int64_t j = sub; j < chunks; j += TP) dst[j] = conv(src[j]);
+      for (int64_t j = sub; j < chunks; j += TP) dst[j] = conv8(src[j], ex);
+    }
+  }
+  if (bad) atomicOr(err, kErrFp16Range);
+}
+
+// Rows of more than 64 x 16 chunks: one row per workgroup, thread t holding
+// chunks t, t + 256, ... (at most CPL) in registers; the row maximum goes
+// through LDS across the four wavefronts. One read and one write per element.
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void to_f16_rows_wg_kernel(const u32x4* __restrict__ a,
+                                                                  u32x4* __restrict__ a16,
+                                                                  int32_t* __restrict__ rexp, int64_t M,
+                                                                  int64_t chunks, uint32_t* __restrict__ err) {
+  __shared__ uint32_t wmax[2][kThreads / 64];
+  const int t = threadIdx.x;
+  uint32_t bad = 0;
+  int par = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, par ^= 1) {
+    const u32x4* src = a + row * chunks;
+    u32x4* dst = a16 + row * chunks;
+    uint32_t mx = 0;
+    u32x4 v[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t j = t + (int64_t)i * kThreads;
+      v[i] = j < chunks ? src[j] : u32x4{0u, 0u, 0u, 0u};
+      mx = absmax8(v[i], mx);
+    }
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    // alternate the two slots from row to row: one barrier per row suffices
+    if ((t & 63) == 0) wmax[par][t >> 6] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) mx = max(mx, wmax[par][w]);
+    const int ex = row_exponent(mx, bad);
+    if (t == 0) rexp[row] = ex;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t j = t + (int64_t)i * kThreads;
+      if (j < chunks) dst[j] = conv8(v[i], ex);
     }
   }
   if (bad) atomicOr(err, kErrFp16Range);
@@ -257,6 +304,19 @@ hipError_t launch_to_f16_rows(const uint16_t* a, uint16_t* a16, int32_t* rexp, i
 #define GEG_TO_F16(CPL)                                                                                        \
   hipLaunchKernelGGL(to_f16_rows_kernel<CPL>, dim3((int)grid), dim3(kThreads), 0, s, src, dst, rexp, M, chunks, \
                      tp_log2, err)
+  const int64_t per_thread_wg = (chunks + kThreads - 1) / kThreads;   // one row per workgroup
+  if (per_lane > 16 && per_thread_wg <= 16) {
+    const int64_t wgrid = std::max<int64_t>(1, std::min<int64_t>(M, (int64_t)cus * 8));
+#define GEG_TO_F16_WG(CPL)                                                                                      \
+  hipLaunchKernelGGL(to_f16_rows_wg_kernel<CPL>, dim3((int)wgrid), dim3(kThreads), 0, s, src, dst, rexp, M, chunks, \
+                     err)
+    if (per_thread_wg <= 8)
+      GEG_TO_F16_WG(8);
+    else
+      GEG_TO_F16_WG(16);
+#undef GEG_TO_F16_WG
+    return hipGetLastError();
+  }
   if (per_lane <= 1)
     GEG_TO_F16(1);
   else if (per_lane <= 2)

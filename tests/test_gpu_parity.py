@@ -256,6 +256,34 @@ def test_nf4_dgrad_row_scaling_keeps_small_and_large_gradients(geg, scale):
     assert rel <= 1e-2 and row_rel <= 1e-2
 
 
+@pytest.mark.parametrize("N", [9000, 20000])
+def test_nf4_dgrad_long_rows(geg, N):
+    # dY rows of more than 8192 values take the one-workgroup-per-row conversion
+    # (up to 8 or 16 chunks per thread); one row four decades smaller than the rest
+    log(f"case: nf4 dgrad with dY rows of {N} values")
+    c, d = custom_case("nf4", 3, 128, N, [21, 0, 50], seed=14)
+    rng = np.random.default_rng(15)
+    dyf = rng.standard_normal((71, N)).astype(np.float32)
+    dyf[30, :] *= 1e-4
+    dy = synthetic.f32_to_bf16_bits(dyf)
+    g = upload_case(d)
+    dx = geg.gnf4_grouped_dgrad(up_u16_as_bf16(dy), g["sizes"], g["w"], g["s"], check_errors=True)
+    ref = oracle.dgrad_ref(dy, d["sizes"], C.weight_fn(d), c.K)
+    got = bf16_to_f64(dx)
+    assert_close(got, ref, f"dgrad N={N}")
+    row_rel = float(np.max(np.abs(got[30] - ref[30])) / np.max(np.abs(ref[30])))
+    log(f"  small row max|err|/max|ref| = {row_rel:.2e}")
+    assert row_rel <= 1e-2
+
+
+def test_nf4_forward_long_rows(geg):
+    # activation rows of 9216 values: the one-workgroup-per-row conversion
+    log("case: nf4 tiled forward with K = 9216")
+    c, d = custom_case("nf4", 2, 9216, 96, [33, 60], seed=16)
+    out = run_fwd(geg, c, upload_case(d), "tiled")
+    assert_close(bf16_to_f64(out), ref_of(d), "forward K=9216")
+
+
 @pytest.mark.parametrize("scale", [1e-7, 1e4])
 def test_nf4_forward_row_scaling(geg, scale):
     # the same on the forward tiled path: activations far below or above fp16's
