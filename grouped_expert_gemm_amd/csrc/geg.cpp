@@ -119,12 +119,25 @@ struct Plan {
   size_t partials_off, partials_bytes;
   size_t a16_off, a16_bytes;   // NF4 tile path: fp16 copy of the row-scaled activations
   size_t rexp_off;             // ... followed by the rows' int32 exponents
+  size_t tail_off, tail_bytes; // tiled path, long contractions: partials of split remainder tiles
   size_t total_bytes;
 };
 
+
 constexpr size_t kHeader = 256;   // the device error word, then padding
+constexpr int32_t kTailSplitMax = 4;   // contraction pieces per split remainder tile
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Tiled ops with a contraction of at least kTailMinContraction may split their
+// remainder tiles over the contraction (see tile.hip); their partial sums take
+// a fixed region at the end of the workspace.
+void plan_tail(Plan& p, int64_t contraction) {
+  if (!p.run_tile || contraction < geg::kTailMinContraction) return;
+  p.tail_off = round256(p.total_bytes);
+  p.tail_bytes = (size_t)geg::kMaxTailPieces * geg::kTailPieceFloats * 4;
+  p.total_bytes = p.tail_off + p.tail_bytes;
+}
 
 geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const geg_opts* o, Plan& p) {
   const int32_t force = o ? o->force_path : 0;
@@ -141,6 +154,7 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.a16_bytes = round256((size_t)M * (size_t)N * 2) + round256((size_t)M * 4);
     p.rexp_off = p.a16_off + round256((size_t)M * (size_t)N * 2);
     p.total_bytes = p.a16_off + p.a16_bytes;
+    plan_tail(p, N);
     return GEG_OK;
   }
   if (op == GEG_OP_MXFP4_W4A8) {   // e4m3 codes [M, K] and their scales [M, K/32]
@@ -153,6 +167,7 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
   if (op == GEG_OP_MXFP4_DGRAD) {   // bf16 dY feeds the MFMAs as it is
     p.run_tile = M > 0;
     p.total_bytes = kHeader;
+    plan_tail(p, N);
     return GEG_OK;
   }
   // A decode-class batch (at most kDecodeAvgRows routed rows per expert on
@@ -206,6 +221,7 @@ geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const g
     p.rexp_off = p.a16_off + round256((size_t)M * (size_t)K * 2);
     p.total_bytes = p.a16_off + p.a16_bytes;
   }
+  plan_tail(p, K);
   return GEG_OK;
 }
 
@@ -303,6 +319,8 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
   g.vec_rows = p.vec_rows;
   g.err = scratch.err_word ? scratch.err_word : reinterpret_cast<uint32_t*>(wsb);
   g.partials = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_off) : nullptr;
+  g.tail_part = p.tail_bytes ? reinterpret_cast<float*>(wsb + p.tail_off) : nullptr;
+  g.tail_split = p.tail_bytes ? kTailSplitMax : 1;
   g.a16 = p.a16_bytes ? reinterpret_cast<const uint16_t*>(wsb + p.a16_off) : nullptr;
   g.rexp = p.a16_bytes ? reinterpret_cast<const int32_t*>(wsb + p.rexp_off) : nullptr;
   g.glu = glu;
@@ -325,11 +343,18 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
     const int64_t n_tiles = (N + geg::kTileN - 1) / geg::kTileN;
     const int64_t tile_experts = std::min<int64_t>(E, M / (std::max<int64_t>(p.thresh, 0) + 1));
     const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + tile_experts) * n_tiles;
+    const int grid = persistent_grid(bound, 1);
     hipError_t e = record_event(opts, 0, stream);
-    if (e == hipSuccess) e = geg::launch_tile(fmt, g, persistent_grid(bound, 1), stream);
-    if (e == hipSuccess) e = record_event(opts, 1, stream);
+    if (e == hipSuccess) e = geg::launch_tile(fmt, g, grid, stream);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     ++g_launches;
+    if (g.tail_split > 1) {
+      e = geg::launch_tile_fixup(g, false, grid, stream);
+      if (e != hipSuccess) return hip_fail(e, "tile fixup launch");
+      ++g_launches;
+    }
+    e = record_event(opts, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel event");
   }
   if (p.run_vec) {
     hipError_t e = record_event(opts, 2, stream);
@@ -459,6 +484,9 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
   g.lora_r = lora.r;
   g.lora_s = lora.s;
   g.split = 1;
+  g.glu = 0;
+  g.tail_part = p.tail_bytes ? reinterpret_cast<float*>(wsb + p.tail_off) : nullptr;
+  g.tail_split = p.tail_bytes ? kTailSplitMax : 1;
   g.err = reinterpret_cast<uint32_t*>(wsb);
   hipError_t e = hipSuccess;
   if (lora.pre && (e = lora.pre()) != hipSuccess) return hip_fail(e, "adapter launch");
@@ -470,11 +498,18 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
   }
   const int64_t k_tiles = (K + geg::kTileN - 1) / geg::kTileN;
   const int64_t bound = ((M + geg::kTileM - 1) / geg::kTileM + std::min<int64_t>(E, M)) * k_tiles;
+  const int grid = persistent_grid(bound, 1);
   e = record_event(opts, 0, stream);
-  if (e == hipSuccess) e = geg::launch_tile_dgrad(fmt, g, persistent_grid(bound, 1), stream);
-  if (e == hipSuccess) e = record_event(opts, 1, stream);
+  if (e == hipSuccess) e = geg::launch_tile_dgrad(fmt, g, grid, stream);
   if (e != hipSuccess) return hip_fail(e, "dgrad kernel launch");
   ++g_launches;
+  if (g.tail_split > 1) {
+    e = geg::launch_tile_fixup(g, true, grid, stream);
+    if (e != hipSuccess) return hip_fail(e, "dgrad fixup launch");
+    ++g_launches;
+  }
+  e = record_event(opts, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel event");
   if (lora.post && (e = lora.post()) != hipSuccess) return hip_fail(e, "adapter launch");
   return GEG_OK;
 }

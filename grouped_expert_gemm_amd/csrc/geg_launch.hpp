@@ -57,6 +57,13 @@ struct GemmArgs {
                           // the skinny path takes vec_rows+1..thresh
   uint32_t* err;          // device error word
   float* partials;        // split-K partials [split, M, N]
+  // Tiled kernel: remainder tiles (at most 128 rows) split over the contraction
+  // into at most tail_split pieces (1: never) when they would otherwise run
+  // alone in a last persistent round; each piece writes fp32 partial sums to
+  // tail_part (kTailPieceFloats per piece, at most kMaxTailPieces pieces) and
+  // the fixup launch adds them.
+  float* tail_part;
+  int32_t tail_split;
   int32_t glu;            // 1: columns 2i, 2i+1 are (gate, up) of unit i and out is
                           // [M, N/2] with out[m, i] = bf16(silu(gate) * up)
   // Low-rank adapter delta added to the tiled kernel's accumulators before the
@@ -76,6 +83,12 @@ hipError_t launch_vec(int fmt, const GemmArgs& g, int cus, hipStream_t s);      
 hipError_t launch_narrow(int fmt, const GemmArgs& g, int cus, hipStream_t s);   // sizes its own grid
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s);
 hipError_t launch_tile_dgrad(int fmt, const GemmArgs& g, int grid, hipStream_t s);
+// After a tiled launch with tail_split > 1 (same arguments and grid): sums the
+// partials of the split remainder tiles into `out` (exits when nothing was split).
+hipError_t launch_tile_fixup(const GemmArgs& g, bool dgrad, int tile_grid, hipStream_t s);
+constexpr int kMaxTailPieces = 256;
+constexpr int kTailPieceFloats = 128 * 256;   // a remainder tile's rows x columns
+constexpr int64_t kTailMinContraction = 8192; // contraction length from which tail splits pay
 hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,
                           uint16_t* bf16, uint16_t* f16, int64_t rows, int64_t K, hipStream_t s);
 hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,

@@ -24,6 +24,8 @@
 // Tiles are assigned XCD-aware: workgroup b runs on XCD b % 8, and each XCD
 // takes a contiguous run of tiles (same expert and row block, neighbouring column
 // blocks), so an activation block is fetched into one XCD's L2 and reused there.
+#include <algorithm>
+
 #include "geg_device.hpp"
 #include "geg_launch.hpp"
 
@@ -369,7 +371,7 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
                                            RawA& ra, RawB (&rb)[2], BDec<F>& dec, Ops& ops,
                                            f32x4 (&acc)[8][4], uint32_t aoff, const BRd<DG>& br,
                                            uint32_t m4, uint32_t base) {
-  constexpr int cur = P, nxt = P ^ 1;   // st % 2 == P
+  constexpr int cur = P, nxt = P ^ 1;   // (st - the tile's first stage) % 2 == P
   const int64_t k1 = (int64_t)(st + 1) * BK;
   // Substep 1 reads chunk 4 + c where substep 0 reads chunk c: the swizzled
   // chunk differs in bit 2, i.e. the half offset differs in bit 5.
@@ -428,11 +430,12 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
   }
 }
 
-// Main loop over the K stages of one tile (H = the wavefront's active 64-row
-// halves; every wavefront runs the same barriers whatever its H).
+// Main loop over the contraction stages st0 .. st1-1 of one tile (H = the
+// wavefront's active 64-row halves; every wavefront runs the same barriers
+// whatever its H).
 template <Fmt F, bool DG, bool TAIL, int H>
 __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
-                                           int wave, int lane, f32x4 (&acc)[8][4]) {
+                                           int st0, int st1, int wave, int lane, f32x4 (&acc)[8][4]) {
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
@@ -448,7 +451,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   // dgrad staging row: the weight row's contraction slot (NF4 slot order, or
   // natural order for MXFP4's bf16 operands)
   const int brow = F == NF4 ? ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7) : (threadIdx.x & 63);
-  const int nst = (int)((C + BK - 1) / BK);
+  const int nst = st1;   // loads of stages past the range are switched off
   uint32_t m4 = 0x04040404u, base = 0x03020100u;
   asm volatile("" : "+v"(base));
   asm volatile("" : "+s"(m4));
@@ -456,27 +459,29 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   RawB rb[2];
   BDec<F> dec;
   Ops ops;
-  // Prologue: stage 0 into buffer 0; raw data of stages 1 (activations) and
-  // 1, 2 (codes) in flight; the first half of stage 1's decode state.
-  load_a(ra, src, 0, true);
-  load_b<F>(rb[0], src, 0, true);
-  load_b<F>(rb[1], src, 1, nst > 1);
+  // Prologue: stage st0 into buffer 0; raw data of stages st0+1 (activations)
+  // and st0+1, st0+2 (codes) in flight; the first half of stage st0+1's decode
+  // state.
+  const int64_t k0 = (int64_t)st0 * BK;
+  load_a(ra, src, st0, true);
+  load_b<F>(rb[0], src, st0, true);
+  load_b<F>(rb[1], src, st0 + 1, st0 + 1 < nst);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], 0, C, wave, lane);
+  for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], k0, C, wave, lane);
   {
     NF4Half h;
     u32x2 even;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b_setup<F, DG>(dec, j, rb[0], 0, K);
+    for (int j = 0; j < 4; ++j) b_setup<F, DG>(dec, j, rb[0], k0, K);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int r = 0; r < 3; ++r) b_step<F, DG>(q, r, rb[0], dec, h, even, L.b[0], brow, m4, base);
   }
-  load_a(ra, src, 1, nst > 1);
-  load_b<F>(rb[0], src, 2, nst > 2);
-  b_setup<F, DG>(dec, 0, rb[1], BK, K);
-  b_setup<F, DG>(dec, 1, rb[1], BK, K);
+  load_a(ra, src, st0 + 1, st0 + 1 < nst);
+  load_b<F>(rb[0], src, st0 + 2, st0 + 2 < nst);
+  b_setup<F, DG>(dec, 0, rb[1], k0 + BK, K);
+  b_setup<F, DG>(dec, 1, rb[1], k0 + BK, K);
   __syncthreads();
   if constexpr (H > 0) {
 #pragma unroll
@@ -484,7 +489,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
 #pragma unroll
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
-  for (int st = 0; st < nst; st += 2) {
+  for (int st = st0; st < nst; st += 2) {
     tile_stage<F, DG, TAIL, H, 0>(L, src, C, K, st, nst, wave, lane, brow, ra, rb, dec, ops, acc, aoff, br, m4, base);
     if (st + 1 < nst)
       tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, brow, ra, rb, dec, ops, acc, aoff, br,
@@ -506,6 +511,25 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
 // more than 128 rows) comes first, expert by expert; class 1 (the smaller
 // remainders) follows, so the persistent rounds end on the cheapest tiles
 // instead of leaving whole tiles for a last, mostly idle round.
+// Work units of an expert with s rows: class 0 (c = 0) and class 1 (c = 1) tiles.
+__device__ __forceinline__ int32_t tile_units(int32_t s, int c, int32_t thresh, int n_tiles) {
+  if (s <= thresh) return 0;
+  const int32_t full = s / BM, rem = s % BM;
+  if (c == 0) return (full + (rem > BM / 2 ? 1 : 0)) * n_tiles;
+  return rem > 0 && rem <= BM / 2 ? n_tiles : 0;
+}
+
+// Contraction pieces per class-1 tile. The class-1 tiles follow the class-0
+// ones round by round; when they do not fit into the free slots of the last
+// class-0 round they would form a round of their own on a few CUs, so each is
+// split into up to `smax` pieces of consecutive stages that fill the chip.
+__device__ __forceinline__ int tail_pieces(int32_t total0, int32_t total1, int G, int smax, int nst) {
+  if (smax <= 1 || total1 <= 0) return 1;
+  const int32_t free_slots = (G - total0 % G) % G;
+  if (total1 <= free_slots) return 1;
+  return max(1, min(min(smax, nst), min(G / total1, kMaxTailPieces / total1)));
+}
+
 template <Fmt F, bool DG, bool TAIL>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   __shared__ int32_t p_off[kMaxExperts + 1];
@@ -516,14 +540,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   const int64_t C = DG ? g.N : g.K;   // contraction length
   const int64_t O = DG ? g.K : g.N;   // output width
   const int n_tiles = (int)((O + BN - 1) / BN);
+  const int nst = (int)((C + BK - 1) / BK);
   const int32_t thresh = g.thresh;
   const int32_t total0 = build_plan2(p_off, p_u0, p_u1, g.sizes, g.E, g.M, g.err, [&](int32_t s, int c) -> int32_t {
-    if (s <= thresh) return 0;
-    const int32_t full = s / BM, rem = s % BM;
-    if (c == 0) return (full + (rem > BM / 2 ? 1 : 0)) * n_tiles;
-    return rem > 0 && rem <= BM / 2 ? n_tiles : 0;
+    return tile_units(s, c, thresh, n_tiles);
   });
-  const int32_t total = total0 + p_u1[g.E];
+  const int32_t total1 = p_u1[g.E];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -534,25 +556,32 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   const int per_xcd = G / kXcds;
   const int slot = (G % kXcds == 0) ? (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds
                                     : blockIdx.x;
+  const int S = tail_pieces(total0, total1, G, g.tail_split, nst);
+  const int32_t total = total0 + total1 * S;
 
   for (int32_t base = 0; base < total; base += G) {
     const int32_t u = base + slot;
     if (u >= total) break;
-    int e, mt, nt;
+    int e, mt, nt, piece = 0;
     if (u < total0) {
       e = find_expert(p_u0, g.E, u);
       const int32_t lu = u - p_u0[e];
       mt = lu / n_tiles;
       nt = lu % n_tiles;
     } else {
-      const int32_t u1 = u - total0;
-      e = find_expert(p_u1, g.E, u1);
+      const int32_t t1 = (u - total0) / S;
+      piece = (u - total0) % S;
+      e = find_expert(p_u1, g.E, t1);
       mt = (p_off[e + 1] - p_off[e]) / BM;   // the remainder block
-      nt = u1 - p_u1[e];
+      nt = t1 - p_u1[e];
     }
     const int64_t row0 = (int64_t)p_off[e] + (int64_t)mt * BM;
     const int rows = min(BM, (int)(p_off[e + 1] - row0));
     const int64_t n0 = (int64_t)nt * BN;
+    // contraction stages of this unit: all, or piece `piece` of S
+    const bool split = S > 1 && u >= total0;
+    const int st0 = split ? piece * nst / S : 0;
+    const int st1 = split ? (piece + 1) * nst / S : nst;
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -563,11 +592,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, DG, TAIL, 2>(L, src, C, g.K, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 2>(L, src, C, g.K, st0, st1, wave, lane, acc);
     else if (vrows > 0)
-      run_tile_h<F, DG, TAIL, 1>(L, src, C, g.K, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 1>(L, src, C, g.K, st0, st1, wave, lane, acc);
     else
-      run_tile_h<F, DG, TAIL, 0>(L, src, C, g.K, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 0>(L, src, C, g.K, st0, st1, wave, lane, acc);
 
     // NF4: the fp16 operand rows were multiplied by 2^-rexp[row] (exact), so each
     // result is multiplied by 2^rexp[row] (exact) where it is read out for its
@@ -591,7 +620,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     // whole 16-byte row pieces. acc[i][j][q] is row 16i + 4(lane/16) + q,
     // column 16j + lane%16 of the block; every write offset is a constant from
     // the lane's base.
-    if (g.lora_r > 0 && rows > 128 * wm) {
+    if (g.lora_r > 0 && rows > 128 * wm && piece == 0) {   // a split tile adds the delta once
       // Low-rank adapter delta into the accumulators before their bf16 rounding:
       // block (i, j) += s U[rows 16 i .., 32 of r] Q[columns 16 j .., 32 of r]^T,
       // the fp32 operands split into bf16 pairs (hi x hi + hi x lo + lo x hi; s
@@ -625,6 +654,26 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
           }
         }
       }
+    }
+    if (split) {
+      // fp32 partial sums of this piece (rows < 128: wave row 0 only), output
+      // columns in final order, row factor 2^rexp already applied; the fixup
+      // launch adds the S pieces in order. No LDS use: the next tile's prologue
+      // may follow directly.
+      if (wm == 0) {
+        float* P = g.tail_part + (int64_t)(u - total0) * kTailPieceFloats;
+        const int c16 = (DG && F == NF4) ? dg_col(lane & 15) : (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 16 * i + 4 * (lane >> 4) + q;
+            const int ex = rowexp(r);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) P[r * BN + 64 * wn + 16 * j + c16] = unscale(acc[i][j][q], ex);
+          }
+      }
+      continue;
     }
     uint16_t* E = L.epi[wave];
     if (!DG && g.glu) {
@@ -712,7 +761,68 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   }
 }
 
+// Split class-1 tiles (see tile_kernel): out = bf16 of the S pieces' partial
+// sums added in piece order; with the gated epilogue, of silu(gate) * up over
+// the column pairs (2c, 2c + 1). Recomputes the tiled kernel's plan and S from
+// the same arguments and grid; exits when no tile was split.
+__global__ __launch_bounds__(kThreads) void tile_fixup_kernel(GemmArgs g, int dgrad, int tile_grid) {
+  __shared__ int32_t p_off[kMaxExperts + 1];
+  __shared__ int32_t p_u0[kMaxExperts + 1];
+  __shared__ int32_t p_u1[kMaxExperts + 1];
+  const int64_t C = dgrad ? g.N : g.K;
+  const int64_t O = dgrad ? g.K : g.N;
+  const int n_tiles = (int)((O + BN - 1) / BN);
+  const int nst = (int)((C + BK - 1) / BK);
+  const int32_t thresh = g.thresh;
+  const int32_t total0 = build_plan2(p_off, p_u0, p_u1, g.sizes, g.E, g.M, g.err, [&](int32_t s, int c) -> int32_t {
+    return tile_units(s, c, thresh, n_tiles);
+  });
+  const int32_t total1 = p_u1[g.E];
+  const int S = tail_pieces(total0, total1, tile_grid, g.tail_split, nst);
+  if (S <= 1) return;
+  const bool glu = !dgrad && g.glu;
+  for (int32_t t1 = blockIdx.x; t1 < total1; t1 += gridDim.x) {
+    const int e = find_expert(p_u1, g.E, t1);
+    const int64_t row0 = (int64_t)p_off[e] + (int64_t)((p_off[e + 1] - p_off[e]) / BM) * BM;
+    const int rows = (int)(p_off[e + 1] - row0);
+    const int64_t n0 = (int64_t)(t1 - p_u1[e]) * BN;
+    const float* P = g.tail_part + (int64_t)t1 * S * kTailPieceFloats;
+    if (glu) {
+      const int64_t O2 = O >> 1;
+      for (int idx = threadIdx.x; idx < rows * (BN / 2); idx += kThreads) {
+        const int r = idx / (BN / 2), c = idx % (BN / 2);
+        const int64_t col = (n0 >> 1) + c;
+        if (col >= O2) continue;
+        const float* p = P + r * BN + 2 * c;
+        float gate = p[0], up = p[1];
+        for (int s = 1; s < S; ++s) {
+          gate += p[s * kTailPieceFloats];
+          up += p[s * kTailPieceFloats + 1];
+        }
+        g.out[(row0 + r) * O2 + col] = to_bf16(swiglu(gate, up));
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < rows * BN; idx += kThreads) {
+        const int r = idx / BN, c = idx % BN;
+        if (n0 + c >= O) continue;
+        float v = P[idx];
+        for (int s = 1; s < S; ++s) v += P[s * kTailPieceFloats + idx];
+        g.out[(row0 + r) * O + n0 + c] = to_bf16(v);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_fixup(const GemmArgs& g, bool dgrad, int tile_grid, hipStream_t s) {
+  // at most E x n_tiles class-1 tiles; two workgroups per CU is plenty
+  const int64_t O = dgrad ? g.K : g.N;
+  const int64_t tiles = (int64_t)g.E * ((O + BN - 1) / BN);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, 2 * (int64_t)tile_grid));
+  hipLaunchKernelGGL(tile_fixup_kernel, dim3(grid), dim3(kThreads), 0, s, g, dgrad ? 1 : 0, tile_grid);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
   if (fmt == NF4)

@@ -117,8 +117,16 @@ def test_workspace_sizes():
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == \
         256 + 16384 * 2048 * 2 + 16384 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
+    # contraction >= 8192: plus the fp32 partials of up to 256 split remainder
+    # tiles (128 x 256 values each)
+    tail = 256 * 128 * 256 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == \
-        256 + 8192 * 28672 * 2 + 8192 * 4
+        256 + 8192 * 28672 * 2 + 8192 * 4 + tail
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 4096, 14336, 8) == \
+        256 + 8192 * 4096 * 2 + 8192 * 4
+    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_DGRAD, 64, 8192, 256, 4) == 256 + tail
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8192, 4096, 14336, 8) == \
+        256 + 8192 * 14336 * 2 + 8192 * 4 + tail
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 3000, 2048, 64, 4) == \
         256 + 3000 * 64 * 2 + ((3000 * 4 + 255) & ~255)
     # skinny split-K partials; a small batch on the automatic path goes to the
