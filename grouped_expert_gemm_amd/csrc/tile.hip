@@ -530,7 +530,10 @@ __device__ __forceinline__ int tail_pieces(int32_t total0, int32_t total1, int G
   return max(1, min(min(smax, nst), min(G / total1, kMaxTailPieces / total1)));
 }
 
-template <Fmt F, bool DG, bool TAIL>
+// SPL: the instantiation for long contractions, which may split remainder
+// tiles; every other launch runs SPL = false, where the stage range is the
+// whole contraction at compile time.
+template <Fmt F, bool DG, bool TAIL, bool SPL>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   __shared__ int32_t p_off[kMaxExperts + 1];
   __shared__ int32_t p_u0[kMaxExperts + 1];
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   const int per_xcd = G / kXcds;
   const int slot = (G % kXcds == 0) ? (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds
                                     : blockIdx.x;
-  const int S = tail_pieces(total0, total1, G, g.tail_split, nst);
+  const int S = SPL ? tail_pieces(total0, total1, G, g.tail_split, nst) : 1;
   const int32_t total = total0 + total1 * S;
 
   for (int32_t base = 0; base < total; base += G) {
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     const int rows = min(BM, (int)(p_off[e + 1] - row0));
     const int64_t n0 = (int64_t)nt * BN;
     // contraction stages of this unit: all, or piece `piece` of S
-    const bool split = S > 1 && u >= total0;
+    const bool split = SPL && S > 1 && u >= total0;
     const int st0 = split ? piece * nst / S : 0;
     const int st1 = split ? (piece + 1) * nst / S : nst;
 
@@ -824,27 +827,28 @@ hipError_t launch_tile_fixup(const GemmArgs& g, bool dgrad, int tile_grid, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
-  if (fmt == NF4)
-    hipLaunchKernelGGL((tile_kernel<NF4, false, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
-  else if (g.K % BK)
-    hipLaunchKernelGGL((tile_kernel<MXFP4, false, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
+template <Fmt F, bool DG, bool TAIL>
+hipError_t launch_tile_t(const GemmArgs& g, int grid, hipStream_t s) {
+  if (g.tail_split > 1)
+    hipLaunchKernelGGL((tile_kernel<F, DG, TAIL, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
   else
-    hipLaunchKernelGGL((tile_kernel<MXFP4, false, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+    hipLaunchKernelGGL((tile_kernel<F, DG, TAIL, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
   return hipGetLastError();
+}
+
+hipError_t launch_tile(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
+  if (fmt == NF4) return launch_tile_t<NF4, false, false>(g, grid, s);
+  if (g.K % BK) return launch_tile_t<MXFP4, false, true>(g, grid, s);
+  return launch_tile_t<MXFP4, false, false>(g, grid, s);
 }
 
 hipError_t launch_tile_dgrad(int fmt, const GemmArgs& g, int grid, hipStream_t s) {
   if (fmt == MXFP4) {
-    if (g.N % BK)
-      hipLaunchKernelGGL((tile_kernel<MXFP4, true, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
-    else
-      hipLaunchKernelGGL((tile_kernel<MXFP4, true, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
-  } else if (g.N % BK)
-    hipLaunchKernelGGL((tile_kernel<NF4, true, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((tile_kernel<NF4, true, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
-  return hipGetLastError();
+    if (g.N % BK) return launch_tile_t<MXFP4, true, true>(g, grid, s);
+    return launch_tile_t<MXFP4, true, false>(g, grid, s);
+  }
+  if (g.N % BK) return launch_tile_t<NF4, true, true>(g, grid, s);
+  return launch_tile_t<NF4, true, false>(g, grid, s);
 }
 
 }  // namespace geg
