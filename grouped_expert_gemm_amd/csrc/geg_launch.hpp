@@ -57,9 +57,9 @@ struct GemmArgs {
                           // the skinny path takes vec_rows+1..thresh
   uint32_t* err;          // device error word
   float* partials;        // split-K partials [split, M, N]
-  // Tiled kernel: remainder tiles (at most 128 rows) split over the contraction
-  // into at most tail_split pieces (1: never) when they would otherwise run
-  // alone in a last persistent round; each piece writes fp32 partial sums to
+  // Tiled kernel: the remainder tiles (at most 128 rows) left over for a last,
+  // partial persistent round split over the contraction into at most
+  // tail_split pieces (1: never); each piece writes fp32 partial sums to
   // tail_part (kTailPieceFloats per piece, at most kMaxTailPieces pieces) and
   // the fixup launch adds them.
   float* tail_part;
@@ -88,7 +88,7 @@ hipError_t launch_tile_dgrad(int fmt, const GemmArgs& g, int grid, hipStream_t s
 hipError_t launch_tile_fixup(const GemmArgs& g, bool dgrad, int tile_grid, hipStream_t s);
 constexpr int kMaxTailPieces = 256;
 constexpr int kTailPieceFloats = 128 * 256;   // a remainder tile's rows x columns
-constexpr int64_t kTailMinContraction = 8192; // contraction length from which tail splits pay
+constexpr int64_t kTailMinContraction = 1024; // contraction length from which tail splits pay
 hipError_t launch_dequant(int fmt, const uint8_t* wq, const void* scales, float* f32,
                           uint16_t* bf16, uint16_t* f16, int64_t rows, int64_t K, hipStream_t s);
 hipError_t launch_quantize_nf4(const float* w, uint8_t* codes, float* absmax, int64_t rows,

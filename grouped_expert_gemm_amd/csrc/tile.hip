@@ -116,52 +116,59 @@ struct RawB {
   float s;         // NF4: absmax of the row's 64-block; MXFP4: e8m0 byte of the 32-block
 };
 
-// Operand sources of the tile (expert e, rows row0.., output columns o0..).
+// Operand sources of the tile (expert e, rows row0.., output columns o0..),
+// starting at contraction stage st0 (a piece of a split tile: every base moves
+// st0 stages on and every window ends where the tile's does, so the piece reads
+// like a tile of the remaining contraction).
 // Forward: out = A . W^T contracts over K; thread t stages codes of weight row t/2
 // (32 k per stage half t%2). dgrad: dX = dY . W contracts over N; thread t stages
 // weight row n = t%64 of the stage's 64, columns o0 + 32 (t/64) .. +32.
 template <Fmt F, bool DG>
 __device__ __forceinline__ TileSrc tile_src(const GemmArgs& g, int e, int64_t row0, int rows,
-                                            int64_t o0, int wave, int lane) {
+                                            int64_t o0, int wave, int lane, int st0) {
   const int64_t K = g.K, N = g.N;
   const int64_t C = DG ? N : K;   // contraction length = activation row length
+  const int64_t k0 = (int64_t)st0 * BK;
   TileSrc t;
   // NF4 reads the fp16 copy of the activations (already in the NF4 slot order).
-  t.a = (F == NF4 ? g.a16 : g.a) + row0 * C;
-  t.na = clamp_bytes((int64_t)rows * C * 2);
+  t.a = (F == NF4 ? g.a16 : g.a) + row0 * C + k0;
+  t.na = clamp_bytes((int64_t)rows * C * 2 - k0 * 2);
   t.a_off = (uint32_t)(((32 * wave + (lane >> 3)) * C + 8 * (lane & 7)) * 2);
   t.a_rows8 = (uint32_t)(8 * C * 2);
   const int tid = threadIdx.x;
   if constexpr (DG) {
-    t.w = g.wq + (int64_t)e * N * (K >> 1);
-    t.nw = clamp_bytes(N * (K >> 1));
+    // stage st0 starts at weight row k0
+    t.w = g.wq + (int64_t)e * N * (K >> 1) + k0 * (K >> 1);
+    t.nw = clamp_bytes((N - k0) * (K >> 1));
     const int n = tid & 63, kc = tid >> 6;
     const int64_t kcol = o0 + 32 * kc;    // past K: never stored
     t.w_off = (uint32_t)(n * (K >> 1) + (kcol >> 1));
     t.w_step = (uint32_t)(BK * (K >> 1));
     if constexpr (F == NF4) {
-      t.s = reinterpret_cast<const float*>(g.scales) + (int64_t)e * N * (K >> 6);
-      t.ns = clamp_bytes(N * (K >> 6) * 4);
+      t.s = reinterpret_cast<const float*>(g.scales) + ((int64_t)e * N + k0) * (K >> 6);
+      t.ns = clamp_bytes((N - k0) * (K >> 6) * 4);
       t.s_off = (uint32_t)((n * (K >> 6) + (kcol >> 6)) * 4);
       t.s_step = (uint32_t)(BK * (K >> 6) * 4);
     } else {
       // the thread's 32 columns are exactly one 32-block of the weight row
-      t.s = reinterpret_cast<const uint8_t*>(g.scales) + (int64_t)e * N * (K >> 5);
-      t.ns = clamp_bytes(N * (K >> 5));
+      t.s = reinterpret_cast<const uint8_t*>(g.scales) + ((int64_t)e * N + k0) * (K >> 5);
+      t.ns = clamp_bytes((N - k0) * (K >> 5));
       t.s_off = (uint32_t)(n * (K >> 5) + (kcol >> 5));
       t.s_step = (uint32_t)(BK * (K >> 5));
     }
   } else {
+    // stage st0 starts k0 into every weight row (st0 scales of a 64-block each,
+    // or 2 st0 of a 32-block)
     const int64_t nrows = min<int64_t>(BN, N - o0);
     const int64_t wrow0 = (int64_t)e * N + o0;
-    t.w = g.wq + wrow0 * (K >> 1);
-    t.nw = clamp_bytes(nrows * (K >> 1));
+    t.w = g.wq + wrow0 * (K >> 1) + (k0 >> 1);
+    t.nw = clamp_bytes(nrows * (K >> 1) - (k0 >> 1));
     if constexpr (F == NF4) {
-      t.s = reinterpret_cast<const float*>(g.scales) + wrow0 * (K >> 6);
-      t.ns = clamp_bytes(nrows * (K >> 6) * 4);
+      t.s = reinterpret_cast<const float*>(g.scales) + wrow0 * (K >> 6) + st0;
+      t.ns = clamp_bytes((nrows * (K >> 6) - st0) * 4);
     } else {
-      t.s = reinterpret_cast<const uint8_t*>(g.scales) + wrow0 * (K >> 5);
-      t.ns = clamp_bytes(nrows * (K >> 5));
+      t.s = reinterpret_cast<const uint8_t*>(g.scales) + wrow0 * (K >> 5) + 2 * (int64_t)st0;
+      t.ns = clamp_bytes(nrows * (K >> 5) - 2 * (int64_t)st0);
     }
     t.w_off = (uint32_t)((tid >> 1) * (K >> 1) + 16 * (tid & 1));
     t.w_step = BK / 2;
@@ -371,7 +378,7 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
                                            RawA& ra, RawB (&rb)[2], BDec<F>& dec, Ops& ops,
                                            f32x4 (&acc)[8][4], uint32_t aoff, const BRd<DG>& br,
                                            uint32_t m4, uint32_t base) {
-  constexpr int cur = P, nxt = P ^ 1;   // (st - the tile's first stage) % 2 == P
+  constexpr int cur = P, nxt = P ^ 1;   // st % 2 == P
   const int64_t k1 = (int64_t)(st + 1) * BK;
   // Substep 1 reads chunk 4 + c where substep 0 reads chunk c: the swizzled
   // chunk differs in bit 2, i.e. the half offset differs in bit 5.
@@ -430,12 +437,11 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
   }
 }
 
-// Main loop over the contraction stages st0 .. st1-1 of one tile (H = the
-// wavefront's active 64-row halves; every wavefront runs the same barriers
-// whatever its H).
+// Main loop over the K stages of one tile (H = the wavefront's active 64-row
+// halves; every wavefront runs the same barriers whatever its H).
 template <Fmt F, bool DG, bool TAIL, int H>
 __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
-                                           int st0, int st1, int wave, int lane, f32x4 (&acc)[8][4]) {
+                                           int wave, int lane, f32x4 (&acc)[8][4]) {
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
@@ -451,7 +457,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   // dgrad staging row: the weight row's contraction slot (NF4 slot order, or
   // natural order for MXFP4's bf16 operands)
   const int brow = F == NF4 ? ((threadIdx.x & 63) & ~7) + nf4_slot(threadIdx.x & 7) : (threadIdx.x & 63);
-  const int nst = st1;   // loads of stages past the range are switched off
+  const int nst = (int)((C + BK - 1) / BK);
   uint32_t m4 = 0x04040404u, base = 0x03020100u;
   asm volatile("" : "+v"(base));
   asm volatile("" : "+s"(m4));
@@ -459,29 +465,27 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   RawB rb[2];
   BDec<F> dec;
   Ops ops;
-  // Prologue: stage st0 into buffer 0; raw data of stages st0+1 (activations)
-  // and st0+1, st0+2 (codes) in flight; the first half of stage st0+1's decode
-  // state.
-  const int64_t k0 = (int64_t)st0 * BK;
-  load_a(ra, src, st0, true);
-  load_b<F>(rb[0], src, st0, true);
-  load_b<F>(rb[1], src, st0 + 1, st0 + 1 < nst);
+  // Prologue: stage 0 into buffer 0; raw data of stages 1 (activations) and
+  // 1, 2 (codes) in flight; the first half of stage 1's decode state.
+  load_a(ra, src, 0, true);
+  load_b<F>(rb[0], src, 0, true);
+  load_b<F>(rb[1], src, 1, nst > 1);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], k0, C, wave, lane);
+  for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], 0, C, wave, lane);
   {
     NF4Half h;
     u32x2 even;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b_setup<F, DG>(dec, j, rb[0], k0, K);
+    for (int j = 0; j < 4; ++j) b_setup<F, DG>(dec, j, rb[0], 0, K);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int r = 0; r < 3; ++r) b_step<F, DG>(q, r, rb[0], dec, h, even, L.b[0], brow, m4, base);
   }
-  load_a(ra, src, st0 + 1, st0 + 1 < nst);
-  load_b<F>(rb[0], src, st0 + 2, st0 + 2 < nst);
-  b_setup<F, DG>(dec, 0, rb[1], k0 + BK, K);
-  b_setup<F, DG>(dec, 1, rb[1], k0 + BK, K);
+  load_a(ra, src, 1, nst > 1);
+  load_b<F>(rb[0], src, 2, nst > 2);
+  b_setup<F, DG>(dec, 0, rb[1], BK, K);
+  b_setup<F, DG>(dec, 1, rb[1], BK, K);
   __syncthreads();
   if constexpr (H > 0) {
 #pragma unroll
@@ -489,7 +493,7 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
 #pragma unroll
     for (int i = 0; i < 3; ++i) ops.a[i] = lds_frag(L.a[0] + aoff + 16 * BK * i);
   }
-  for (int st = st0; st < nst; st += 2) {
+  for (int st = 0; st < nst; st += 2) {
     tile_stage<F, DG, TAIL, H, 0>(L, src, C, K, st, nst, wave, lane, brow, ra, rb, dec, ops, acc, aoff, br, m4, base);
     if (st + 1 < nst)
       tile_stage<F, DG, TAIL, H, 1>(L, src, C, K, st + 1, nst, wave, lane, brow, ra, rb, dec, ops, acc, aoff, br,
@@ -519,21 +523,27 @@ __device__ __forceinline__ int32_t tile_units(int32_t s, int c, int32_t thresh, 
   return rem > 0 && rem <= BM / 2 ? n_tiles : 0;
 }
 
-// Contraction pieces per class-1 tile. The class-1 tiles follow the class-0
-// ones round by round; when they do not fit into the free slots of the last
-// class-0 round they would form a round of their own on a few CUs, so each is
-// split into up to `smax` pieces of consecutive stages that fill the chip.
-__device__ __forceinline__ int tail_pieces(int32_t total0, int32_t total1, int G, int smax, int nst) {
-  if (smax <= 1 || total1 <= 0) return 1;
+// Split of the last round. The class-1 tiles follow the class-0 ones round by
+// round; the r of them that are left over for a last, partial round would run
+// there on r CUs while the rest idle, so each of those r is split into S pieces
+// of consecutive contraction stages (S <= smax, S r <= G). The first `unsplit`
+// class-1 tiles run whole; S = 1 when nothing is split.
+struct TailPlan {
+  int32_t unsplit;
+  int S;
+};
+__device__ __forceinline__ TailPlan tail_plan(int32_t total0, int32_t total1, int G, int smax, int nst) {
+  const TailPlan none{total1, 1};
+  if (smax <= 1 || total1 <= 0) return none;
   const int32_t free_slots = (G - total0 % G) % G;
-  if (total1 <= free_slots) return 1;
-  return max(1, min(min(smax, nst), min(G / total1, kMaxTailPieces / total1)));
+  if (total1 <= free_slots) return none;
+  const int32_t r = (total1 - free_slots) % G;
+  if (r == 0) return none;
+  const int S = min(min(smax, nst), min(G / r, kMaxTailPieces / r));
+  return S > 1 ? TailPlan{total1 - r, S} : none;
 }
 
-// SPL: the instantiation for long contractions, which may split remainder
-// tiles; every other launch runs SPL = false, where the stage range is the
-// whole contraction at compile time.
-template <Fmt F, bool DG, bool TAIL, bool SPL>
+template <Fmt F, bool DG, bool TAIL>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   __shared__ int32_t p_off[kMaxExperts + 1];
   __shared__ int32_t p_u0[kMaxExperts + 1];
@@ -559,21 +569,29 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   const int per_xcd = G / kXcds;
   const int slot = (G % kXcds == 0) ? (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds
                                     : blockIdx.x;
-  const int S = SPL ? tail_pieces(total0, total1, G, g.tail_split, nst) : 1;
-  const int32_t total = total0 + total1 * S;
+  const TailPlan tp = tail_plan(total0, total1, G, g.tail_split, nst);
+  const int S = tp.S;
+  const int32_t total = total0 + tp.unsplit + (total1 - tp.unsplit) * S;
 
   for (int32_t base = 0; base < total; base += G) {
     const int32_t u = base + slot;
     if (u >= total) break;
     int e, mt, nt, piece = 0;
+    bool split = false;
+    int32_t w = 0;   // split units: partial-sum slot
     if (u < total0) {
       e = find_expert(p_u0, g.E, u);
       const int32_t lu = u - p_u0[e];
       mt = lu / n_tiles;
       nt = lu % n_tiles;
     } else {
-      const int32_t t1 = (u - total0) / S;
-      piece = (u - total0) % S;
+      int32_t t1 = u - total0;
+      if (t1 >= tp.unsplit) {
+        split = true;
+        w = t1 - tp.unsplit;
+        piece = w % S;
+        t1 = tp.unsplit + w / S;
+      }
       e = find_expert(p_u1, g.E, t1);
       mt = (p_off[e + 1] - p_off[e]) / BM;   // the remainder block
       nt = t1 - p_u1[e];
@@ -581,10 +599,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     const int64_t row0 = (int64_t)p_off[e] + (int64_t)mt * BM;
     const int rows = min(BM, (int)(p_off[e + 1] - row0));
     const int64_t n0 = (int64_t)nt * BN;
-    // contraction stages of this unit: all, or piece `piece` of S
-    const bool split = SPL && S > 1 && u >= total0;
+    // A piece reads like a tile of a shorter contraction: stages piece nst / S ..
+    // (piece + 1) nst / S - 1, the last piece running to the end (with the
+    // contraction's own tail).
     const int st0 = split ? piece * nst / S : 0;
-    const int st1 = split ? (piece + 1) * nst / S : nst;
+    const int64_t Cp = !split ? C : piece == S - 1 ? C - (int64_t)st0 * BK : (int64_t)((piece + 1) * nst / S - st0) * BK;
+    const int64_t Kp = DG ? g.K : Cp;
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -592,14 +612,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane);
+    const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane, st0);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, DG, TAIL, 2>(L, src, C, g.K, st0, st1, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 2>(L, src, Cp, Kp, wave, lane, acc);
     else if (vrows > 0)
-      run_tile_h<F, DG, TAIL, 1>(L, src, C, g.K, st0, st1, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 1>(L, src, Cp, Kp, wave, lane, acc);
     else
-      run_tile_h<F, DG, TAIL, 0>(L, src, C, g.K, st0, st1, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 0>(L, src, Cp, Kp, wave, lane, acc);
 
     // NF4: the fp16 operand rows were multiplied by 2^-rexp[row] (exact), so each
     // result is multiplied by 2^rexp[row] (exact) where it is read out for its
@@ -664,7 +684,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       // launch adds the S pieces in order. No LDS use: the next tile's prologue
       // may follow directly.
       if (wm == 0) {
-        float* P = g.tail_part + (int64_t)(u - total0) * kTailPieceFloats;
+        float* P = g.tail_part + (int64_t)w * kTailPieceFloats;
         const int c16 = (DG && F == NF4) ? dg_col(lane & 15) : (lane & 15);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -766,8 +786,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 
 // Split class-1 tiles (see tile_kernel): out = bf16 of the S pieces' partial
 // sums added in piece order; with the gated epilogue, of silu(gate) * up over
-// the column pairs (2c, 2c + 1). Recomputes the tiled kernel's plan and S from
-// the same arguments and grid; exits when no tile was split.
+// the column pairs (2c, 2c + 1). Recomputes the tiled kernel's plan and split
+// from the same arguments and grid; exits when no tile was split.
 __global__ __launch_bounds__(kThreads) void tile_fixup_kernel(GemmArgs g, int dgrad, int tile_grid) {
   __shared__ int32_t p_off[kMaxExperts + 1];
   __shared__ int32_t p_u0[kMaxExperts + 1];
@@ -781,36 +801,51 @@ __global__ __launch_bounds__(kThreads) void tile_fixup_kernel(GemmArgs g, int dg
     return tile_units(s, c, thresh, n_tiles);
   });
   const int32_t total1 = p_u1[g.E];
-  const int S = tail_pieces(total0, total1, tile_grid, g.tail_split, nst);
+  const TailPlan tp = tail_plan(total0, total1, tile_grid, g.tail_split, nst);
+  const int S = tp.S;
   if (S <= 1) return;
   const bool glu = !dgrad && g.glu;
-  for (int32_t t1 = blockIdx.x; t1 < total1; t1 += gridDim.x) {
+  // Work items: 8 rows of one split tile; thread t sums columns 8 (t % 32) .. +8
+  // of row t / 32, with the 2 S float4 loads of its pieces in flight together.
+  const int32_t items = (total1 - tp.unsplit) * (BM / 2 / 8);
+  const int tr = threadIdx.x >> 5, tc = 8 * (threadIdx.x & 31);
+  for (int32_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int32_t x = it / (BM / 2 / 8);
+    const int r = 8 * (it % (BM / 2 / 8)) + tr;
+    const int32_t t1 = tp.unsplit + x;
     const int e = find_expert(p_u1, g.E, t1);
     const int64_t row0 = (int64_t)p_off[e] + (int64_t)((p_off[e + 1] - p_off[e]) / BM) * BM;
     const int rows = (int)(p_off[e + 1] - row0);
+    if (r >= rows) continue;
     const int64_t n0 = (int64_t)(t1 - p_u1[e]) * BN;
-    const float* P = g.tail_part + (int64_t)t1 * S * kTailPieceFloats;
+    const float* P = g.tail_part + (int64_t)x * S * kTailPieceFloats + r * BN + tc;
+    f32x4 v0 = *reinterpret_cast<const f32x4*>(P), v1 = *reinterpret_cast<const f32x4*>(P + 4);
+    for (int s = 1; s < S; ++s) {
+      v0 += *reinterpret_cast<const f32x4*>(P + s * kTailPieceFloats);
+      v1 += *reinterpret_cast<const f32x4*>(P + s * kTailPieceFloats + 4);
+    }
     if (glu) {
+      // columns (2c, 2c + 1) = (gate, up) of unit c: 4 units per thread
       const int64_t O2 = O >> 1;
-      for (int idx = threadIdx.x; idx < rows * (BN / 2); idx += kThreads) {
-        const int r = idx / (BN / 2), c = idx % (BN / 2);
-        const int64_t col = (n0 >> 1) + c;
-        if (col >= O2) continue;
-        const float* p = P + r * BN + 2 * c;
-        float gate = p[0], up = p[1];
-        for (int s = 1; s < S; ++s) {
-          gate += p[s * kTailPieceFloats];
-          up += p[s * kTailPieceFloats + 1];
-        }
-        g.out[(row0 + r) * O2 + col] = to_bf16(swiglu(gate, up));
-      }
+      const int64_t col = (n0 + tc) >> 1;
+      uint16_t* dst = g.out + (row0 + r) * O2 + col;
+      const float u[4] = {swiglu(v0[0], v0[1]), swiglu(v0[2], v0[3]), swiglu(v1[0], v1[1]), swiglu(v1[2], v1[3])};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (col + k < O2) dst[k] = to_bf16(u[k]);
     } else {
-      for (int idx = threadIdx.x; idx < rows * BN; idx += kThreads) {
-        const int r = idx / BN, c = idx % BN;
-        if (n0 + c >= O) continue;
-        float v = P[idx];
-        for (int s = 1; s < S; ++s) v += P[s * kTailPieceFloats + idx];
-        g.out[(row0 + r) * O + n0 + c] = to_bf16(v);
+      const int64_t col = n0 + tc;
+      uint16_t* dst = g.out + (row0 + r) * O + col;
+      const float u[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      if ((O & 7) == 0 && col + 8 <= O) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (uint32_t)to_bf16(u[2 * k]) | ((uint32_t)to_bf16(u[2 * k + 1]) << 16);
+        *reinterpret_cast<u32x4*>(dst) = w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (col + k < O) dst[k] = to_bf16(u[k]);
       }
     }
   }
@@ -819,20 +854,15 @@ __global__ __launch_bounds__(kThreads) void tile_fixup_kernel(GemmArgs g, int dg
 }  // namespace
 
 hipError_t launch_tile_fixup(const GemmArgs& g, bool dgrad, int tile_grid, hipStream_t s) {
-  // at most E x n_tiles class-1 tiles; two workgroups per CU is plenty
-  const int64_t O = dgrad ? g.K : g.N;
-  const int64_t tiles = (int64_t)g.E * ((O + BN - 1) / BN);
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, 2 * (int64_t)tile_grid));
+  // at most tile_grid split tiles of 16 work items each; two workgroups per CU
+  const int grid = std::max(1, 2 * tile_grid);
   hipLaunchKernelGGL(tile_fixup_kernel, dim3(grid), dim3(kThreads), 0, s, g, dgrad ? 1 : 0, tile_grid);
   return hipGetLastError();
 }
 
 template <Fmt F, bool DG, bool TAIL>
 hipError_t launch_tile_t(const GemmArgs& g, int grid, hipStream_t s) {
-  if (g.tail_split > 1)
-    hipLaunchKernelGGL((tile_kernel<F, DG, TAIL, true>), dim3(grid), dim3(kTileThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((tile_kernel<F, DG, TAIL, false>), dim3(grid), dim3(kTileThreads), 0, s, g);
+  hipLaunchKernelGGL((tile_kernel<F, DG, TAIL>), dim3(grid), dim3(kTileThreads), 0, s, g);
   return hipGetLastError();
 }
 

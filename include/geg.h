@@ -65,7 +65,7 @@
  *    split-K partials (fp32 [split, M, N]); for the NF4 tiled path, an fp16
  *    copy of the row-scaled activations (M * K * 2 bytes; dgrad: of dY,
  *    M * N * 2 bytes) and the rows' int32 exponents (M * 4 bytes); and, when
- *    the tiled path's contraction (K, dgrad: N) is at least 8192, 32 MiB for
+ *    the tiled path's contraction (K, dgrad: N) is at least 1024, 32 MiB for
  *    the fp32 partial sums of remainder tiles split over the contraction.
  *    Calls on one workspace must be ordered (same stream); concurrent calls
  *    must not share one.
@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define GEG_VERSION 111 /* 1.1.1 */
+#define GEG_VERSION 112 /* 1.1.2 */
 
 typedef enum {
   GEG_OK = 0,
@@ -173,7 +173,7 @@ geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t*
  *   A call whose scratch (geg_workspace_bytes(GEG_OP_NF4_FWD, M, N, K, E, opts))
  *   exceeds 144 MiB is refused with GEG_ERR_WORKSPACE before anything is enqueued
  *   (for example M * K * 2 + M * 4 > 140 MiB on the tiled path, or > 108 MiB
- *   when K >= 8192 adds the 32 MiB of split remainder tiles).
+ *   when K >= 1024 adds the 32 MiB of split remainder tiles).
  *   Every call on one GPU shares that GPU's array, which keeps the last call's
  *   contents: calls ordered on one stream are safe; calls that overlap on one GPU
  *   (unordered streams, several host threads) race on it.

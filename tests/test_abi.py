@@ -25,7 +25,7 @@ def test_library_exports_every_header_function():
 
 
 def test_version_and_status_strings():
-    assert L().geg_version() == 111
+    assert L().geg_version() == 112
     assert L().geg_status_string(0) == b"GEG_OK"
     assert L().geg_status_string(5) == b"GEG_ERR_WORKSPACE"
 
@@ -114,16 +114,20 @@ def test_workspace_sizes():
     # NF4 prefill: the 256-byte header (error word), then the fp16 copy of the
     # activations that the tiled path reads and the rows' int32 exponents;
     # MXFP4 reads bf16 activations as given
-    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == \
-        256 + 16384 * 2048 * 2 + 16384 * 4
-    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256
-    # contraction >= 8192: plus the fp32 partials of up to 256 split remainder
+    # contraction >= 1024: plus the fp32 partials of up to 256 split remainder
     # tiles (128 x 256 values each)
     tail = 256 * 128 * 256 * 4
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 16384, 2048, 2048, 64) == \
+        256 + 16384 * 2048 * 2 + 16384 * 4 + tail
+    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 2880, 32) == 256 + tail
+    assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_FWD, 8192, 5760, 992, 32) == 256
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8192, 2048, 768, 128) == 256 + 8192 * 768 * 2 + 8192 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 28672, 4096, 8) == \
         256 + 8192 * 28672 * 2 + 8192 * 4 + tail
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 4096, 14336, 8) == \
-        256 + 8192 * 4096 * 2 + 8192 * 4
+        256 + 8192 * 4096 * 2 + 8192 * 4 + tail
+    assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_DGRAD, 8192, 512, 14336, 8) == \
+        256 + 8192 * 512 * 2 + 8192 * 4
     assert geg.geg_workspace_bytes(geg.GEG_OP_MXFP4_DGRAD, 64, 8192, 256, 4) == 256 + tail
     assert geg.geg_workspace_bytes(geg.GEG_OP_NF4_FWD, 8192, 4096, 14336, 8) == \
         256 + 8192 * 14336 * 2 + 8192 * 4 + tail

@@ -1,15 +1,15 @@
 """GPU parity of split remainder tiles, on every output element.
 
-With a contraction of at least 8192, the tiled kernel splits its remainder
-tiles (blocks of at most 128 rows) into up to four pieces of consecutive
-contraction stages when they would otherwise run alone in a last persistent
-round; every piece writes fp32 partial sums and a second launch adds them in
-piece order (with the gated epilogue applied there in the fused block). The
-number of pieces follows from the plan and the grid, so `cu_limit` picks it:
-sizes [1024, 5] give 4 full row blocks and one 5-row remainder per expert pair;
-with 2 output-column tiles that is 8 class-0 tiles and 2 remainder tiles, so a
-grid of 8 splits each remainder tile 4 ways, a grid of 4 splits it 2 ways, and
-a grid of 14 runs the remainder tiles beside the last class-0 round unsplit.
+With a contraction of at least 1024, the tiled kernel splits the remainder
+tiles (blocks of at most 128 rows) that are left over for a last, partial
+persistent round into up to four pieces of consecutive contraction stages;
+every piece writes fp32 partial sums and a second launch adds them in piece
+order (with the gated epilogue applied there in the fused block). The number of
+pieces follows from the plan and the grid, so `cu_limit` picks it: sizes
+[1024, 5] give 4 full row blocks and one 5-row remainder per expert pair; with
+2 output-column tiles that is 8 class-0 tiles and 2 remainder tiles, so a grid
+of 8 splits each remainder tile 4 ways, a grid of 4 splits it 2 ways, and a grid
+of 14 runs the remainder tiles beside the last class-0 round unsplit.
 
 Definition of the result: "grouped-nf4-gemm releases", v0.2.6 "The patch point"
 (the per-expert loop); tolerance |gpu - ref| <= 1e-2 max(1, |ref|).
@@ -40,10 +40,10 @@ def geg():
     return g
 
 
-def _case(fmt, K, N, seed):
+def _case(fmt, K, N, seed, sizes=SIZES):
     rng = np.random.default_rng(seed)
-    sizes = np.array(SIZES, np.int32)
-    E, M = len(SIZES), int(sizes.sum())
+    E, M = len(sizes), int(np.sum(sizes))
+    sizes = np.array(sizes, np.int32)
     a = synthetic.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     if fmt == "nf4":
         codes = np.zeros((E, N, K // 2), np.uint8)
@@ -150,3 +150,37 @@ def test_block_gated_epilogue_on_split_tiles(geg):
         assert np.all(err <= plain + allow)
         # the split remainder rows (expert 1) carry no ambiguity at this size
         assert np.all(err[1024:] <= plain[1024:])
+
+
+# Three experts of one full block each and two 5- and 7-row remainders, over 2
+# output-column tiles: 6 class-0 tiles, then 4 remainder tiles. A grid of 4
+# leaves 2 free slots in the second round, so the first 2 remainder tiles run
+# whole there and the last 2 split in 2 pieces; a grid of 3 has no free slot and
+# 1 tile left over, which splits in 3 pieces of uneven stage counts.
+MIXED = [256, 256, 256, 5, 7]
+
+
+@pytest.mark.parametrize("fmt,K", [("nf4", 2048), ("mxfp4", 2080)])
+@pytest.mark.parametrize("cu", [4, 3])
+def test_forward_whole_and_split_remainder_tiles(geg, fmt, K, cu):
+    log(f"case: tiled forward {fmt}, K={K} N=512 sizes={MIXED} cu_limit={cu}")
+    c, d = _case(fmt, K, 512, seed=57, sizes=MIXED)
+    g = upload_case(d)
+    fn = geg.gnf4_grouped_gemm if fmt == "nf4" else geg.gmxfp4_grouped_gemm
+    out = fn(g["a"], g["sizes"], g["w"], g["s"], opts=geg.Opts(2, 0, None, cu), check_errors=True)
+    assert_close(bf16_to_f64(out), oracle.grouped_ref(d["a_bits"], d["sizes"], C.weight_fn(d), c.N),
+                 f"forward {fmt} K={K} cu={cu}")
+
+
+@pytest.mark.parametrize("fmt,N", [("nf4", 2048), ("mxfp4", 2056)])
+@pytest.mark.parametrize("cu", [4, 3])
+def test_dgrad_whole_and_split_remainder_tiles(geg, fmt, N, cu):
+    log(f"case: dgrad {fmt}, K=512 N={N} sizes={MIXED} cu_limit={cu}")
+    c, d = _case(fmt, 512, N, seed=58, sizes=MIXED)
+    rng = np.random.default_rng(59)
+    M = int(np.sum(MIXED))
+    dy = synthetic.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    g = upload_case(d)
+    fn = geg.gnf4_grouped_dgrad if fmt == "nf4" else geg.gmxfp4_grouped_dgrad
+    dx = fn(up_u16_as_bf16(dy), g["sizes"], g["w"], g["s"], opts=geg.Opts(0, 0, None, cu), check_errors=True)
+    assert_close(bf16_to_f64(dx), oracle.dgrad_ref(dy, d["sizes"], C.weight_fn(d), 512), f"dgrad {fmt} N={N} cu={cu}")
