@@ -361,23 +361,16 @@ hipError_t launch_n(const GemmArgs& g, int cus, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef NARROW_NS1
-#define NARROW_NS1 4
-#endif
-
 template <Fmt F>
 hipError_t launch_narrow_fmt(const GemmArgs& g, int cus, hipStream_t s) {
   // 32-row units (two 16-row blocks per wavefront, 128 weight rows per unit) when
   // the batch's experts are expected to hold more than 16 rows; otherwise 16-row
   // units over 64 weight rows (more, smaller units keep more wavefronts busy).
   if (g.thresh > 16 && g.M > 16 * (int64_t)std::min<int64_t>(g.E, g.M)) return launch_n<F, 2, 2, 3>(g, cus, s);
-#ifndef NARROW_CBW1
-#define NARROW_CBW1 1
-#endif
   if constexpr (F == NF4) {
-    if (g.K <= 2048) return launch_n<F, 1, NARROW_CBW1, NARROW_NS1, true>(g, cus, s);
+    if (g.K <= 2048) return launch_n<F, 1, 1, 4, true>(g, cus, s);
   }
-  return launch_n<F, 1, 1, NARROW_NS1>(g, cus, s);
+  return launch_n<F, 1, 1, 4>(g, cus, s);
 }
 
 }  // namespace
