@@ -186,16 +186,26 @@ __device__ __forceinline__ void step_barrier() {
 // Wavefront (wm, wn) computes rows 64 wm .. +63 and columns 64 wn .. +63: 4 x 4
 // blocks of the 16x16x128 instruction per step. Scale bytes go straight from
 // memory to the lanes that use them.
+//
+// Work order: class 0 (every full 256-row block, and remainders of more than
+// 128 rows) first, expert by expert; class 1 (remainders of at most 128 rows,
+// whose idle wavefront rows skip their instructions, so they cost half a tile
+// or less) after it, so that the last persistent rounds hold the cheap tiles.
 __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
-  __shared__ Plan plan;
+  __shared__ int32_t p_off[kMaxExperts + 1];
+  __shared__ int32_t p_u0[kMaxExperts + 1];
+  __shared__ int32_t p_u1[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
   const int64_t K = g.K, N = g.N, KS = K >> 5, M = g.M;
   const int n_tiles = (int)((N + QBN - 1) / QBN);
-  const int32_t total = build_plan(plan, g.sizes, g.E, g.M, g.err, [&](int32_t s) -> int32_t {
-    return ((s + QBM - 1) / QBM) * n_tiles;
+  const int32_t total0 = build_plan2(p_off, p_u0, p_u1, g.sizes, g.E, g.M, g.err, [&](int32_t s, int c) -> int32_t {
+    const int32_t full = s / QBM, rem = s % QBM;
+    if (c == 0) return (full + (rem > QBM / 2 ? 1 : 0)) * n_tiles;
+    return rem > 0 && rem <= QBM / 2 ? n_tiles : 0;
   });
+  const int32_t total = total0 + p_u1[g.E];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -226,11 +236,21 @@ __global__ __launch_bounds__(QThreads, 1) void w4a8_kernel(W4A8Args g) {
   for (int32_t base = 0; base < total; base += G) {
     const int32_t u = base + slot;
     if (u >= total) break;
-    const int e = find_expert(plan, g.E, u);
-    const int32_t lu = u - plan.upre[e];
-    const int64_t row0 = plan.off[e] + (int64_t)(lu / n_tiles) * QBM;
-    const int rows = (int)min<int64_t>(QBM, plan.off[e + 1] - row0);
-    const int64_t n0 = (int64_t)(lu % n_tiles) * QBN;
+    int e, mt, nt;
+    if (u < total0) {
+      e = find_expert(p_u0, g.E, u);
+      const int32_t lu = u - p_u0[e];
+      mt = lu / n_tiles;
+      nt = lu % n_tiles;
+    } else {
+      const int32_t t1 = u - total0;
+      e = find_expert(p_u1, g.E, t1);
+      mt = (p_off[e + 1] - p_off[e]) / QBM;   // the remainder block
+      nt = t1 - p_u1[e];
+    }
+    const int64_t row0 = p_off[e] + (int64_t)mt * QBM;
+    const int rows = (int)min<int64_t>(QBM, p_off[e + 1] - row0);
+    const int64_t n0 = (int64_t)nt * QBN;
     const int ncols = (int)min<int64_t>(QBN, N - n0);
     // rows past the expert's last row and columns past N read as zeros
     const __amdgpu_buffer_rsrc_t RA = qrsrc(g.aq + row0 * K, (int64_t)rows * K);
