@@ -139,6 +139,16 @@ void plan_tail(Plan& p, int64_t contraction) {
   p.total_bytes = p.tail_off + p.tail_bytes;
 }
 
+// The split region is optional: a workspace that holds everything before it
+// runs the call with no tile split (the same results up to the fp32 summation
+// order of the split tiles).
+void fit_tail(Plan& p, size_t ws_bytes) {
+  if (p.tail_bytes && ws_bytes < p.total_bytes && ws_bytes >= p.tail_off) {
+    p.tail_bytes = 0;
+    p.total_bytes = p.tail_off;
+  }
+}
+
 geg_status make_plan(int op, int64_t M, int64_t N, int64_t K, int32_t E, const geg_opts* o, Plan& p) {
   const int32_t force = o ? o->force_path : 0;
   const int32_t split_req = o ? o->split_k : 0;
@@ -293,6 +303,7 @@ geg_status gemm_common(int fmt, const void* a, const int32_t* sizes, const uint8
       (fmt == geg::NF4 && !aligned(scales, 4)))
     return fail(GEG_ERR_MISALIGNED, "a, w/blocks and out must be 16-byte aligned");
   if (!aligned(ws, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  fit_tail(p, ws_bytes);
   if (ws_bytes < p.total_bytes)
     return fail(GEG_ERR_WORKSPACE, "workspace smaller than geg_workspace_bytes(): need " +
                                        std::to_string(p.total_bytes));
@@ -459,6 +470,7 @@ geg_status dgrad_common(int fmt, const void* dy, const int32_t* sizes, const uin
       !aligned(sizes, 4))
     return fail(GEG_ERR_MISALIGNED, "dy, w and dx must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(GEG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  fit_tail(p, workspace_bytes);
   if (workspace_bytes < p.total_bytes) return fail(GEG_ERR_WORKSPACE, "workspace too small");
   if ((st = check_device()) != GEG_OK) return st;
   for (auto [ptr, name] : {std::pair<const void*, const char*>{dy, "dy"}, {sizes, "sizes"},
@@ -537,6 +549,7 @@ geg_status gnf4_grouped_gemm_noalloc(const void* a, const int32_t* sizes, const 
   Plan p;
   if ((st = make_plan(GEG_OP_NF4_FWD, M, N, K, E, opts, p)) != GEG_OK) return st;
   if (M == 0) return GEG_OK;
+  fit_tail(p, geg::kNoallocScratchBytes);
   if (p.total_bytes > geg::kNoallocScratchBytes)
     return fail(GEG_ERR_WORKSPACE, "this call needs " + std::to_string(p.total_bytes) +
                                        " bytes of scratch; the library-held array holds " +

@@ -66,7 +66,10 @@
  *    copy of the row-scaled activations (M * K * 2 bytes; dgrad: of dY,
  *    M * N * 2 bytes) and the rows' int32 exponents (M * 4 bytes); and, when
  *    the tiled path's contraction (K, dgrad: N) is at least 1024, 32 MiB for
- *    the fp32 partial sums of remainder tiles split over the contraction.
+ *    the fp32 partial sums of remainder tiles split over the contraction. That
+ *    last region is optional for the grouped GEMM and dgrad entry points: a
+ *    workspace that holds everything before it runs the call without the split
+ *    (results equal up to the fp32 summation order of the split tiles).
  *    Calls on one workspace must be ordered (same stream); concurrent calls
  *    must not share one.
  */
@@ -81,7 +84,7 @@
 extern "C" {
 #endif
 
-#define GEG_VERSION 112 /* 1.1.2 */
+#define GEG_VERSION 113 /* 1.1.3 */
 
 typedef enum {
   GEG_OK = 0,
@@ -170,10 +173,11 @@ geg_status gnf4_grouped_gemm(const void* a, const int32_t* sizes, const uint8_t*
  * call writes the rest before reading it.
  *   error_word  device uint32 (4-B aligned) that receives the GEG_DEVERR_* bits of
  *               this call (OR-ed in; the caller clears it), or NULL to drop them
- *   A call whose scratch (geg_workspace_bytes(GEG_OP_NF4_FWD, M, N, K, E, opts))
- *   exceeds 144 MiB is refused with GEG_ERR_WORKSPACE before anything is enqueued
- *   (for example M * K * 2 + M * 4 > 140 MiB on the tiled path, or > 108 MiB
- *   when K >= 1024 adds the 32 MiB of split remainder tiles).
+ *   A call whose scratch (geg_workspace_bytes(GEG_OP_NF4_FWD, M, N, K, E, opts),
+ *   less the optional 32 MiB of split remainder tiles) exceeds 144 MiB is refused
+ *   with GEG_ERR_WORKSPACE before anything is enqueued (for example
+ *   M * K * 2 + M * 4 > 140 MiB on the tiled path); when only the split region
+ *   does not fit, the call runs without the split.
  *   Every call on one GPU shares that GPU's array, which keeps the last call's
  *   contents: calls ordered on one stream are safe; calls that overlap on one GPU
  *   (unordered streams, several host threads) race on it.

@@ -25,7 +25,7 @@ def test_library_exports_every_header_function():
 
 
 def test_version_and_status_strings():
-    assert L().geg_version() == 112
+    assert L().geg_version() == 113
     assert L().geg_status_string(0) == b"GEG_OK"
     assert L().geg_status_string(5) == b"GEG_ERR_WORKSPACE"
 
@@ -108,6 +108,23 @@ def test_small_workspace_is_refused():
     assert need > 256                               # split-K needs its partials
     assert _gemm(M=8, N=2048, K=2048, E=64, ws_bytes=need - 256, opts=o) == 5
     assert b"workspace" in L().geg_last_error()
+
+
+def test_split_region_of_the_workspace_is_optional():
+    # a workspace that holds everything but the 32 MiB of split remainder tiles
+    # passes the workspace check (the call then runs unsplit; here it stops at
+    # the device check), one byte less than that is refused
+    tail = 256 * 128 * 256 * 4
+    for name, op, M, N, K in (("gnf4_grouped_gemm", geg.GEG_OP_NF4_FWD, 4096, 2048, 2048),
+                              ("gmxfp4_grouped_gemm", geg.GEG_OP_MXFP4_FWD, 4096, 2048, 2048),
+                              ("gnf4_grouped_dgrad", geg.GEG_OP_NF4_DGRAD, 4096, 2048, 1024),
+                              ("gmxfp4_grouped_dgrad", geg.GEG_OP_MXFP4_DGRAD, 4096, 2048, 1024)):
+        need = geg.geg_workspace_bytes(op, M, N, K, 8)
+        base = need - tail
+        assert base >= 256 and base % 256 == 0, name
+        assert _gemm(name, M=M, N=N, K=K, E=8, ws_bytes=base) not in (0, 5), name
+        assert _gemm(name, M=M, N=N, K=K, E=8, ws_bytes=base - 256) == 5, name
+        assert b"workspace" in L().geg_last_error(), name
 
 
 def test_workspace_sizes():

@@ -14,6 +14,8 @@ of 14 runs the remainder tiles beside the last class-0 round unsplit.
 Definition of the result: "grouped-nf4-gemm releases", v0.2.6 "The patch point"
 (the per-expert loop); tolerance |gpu - ref| <= 1e-2 max(1, |ref|).
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -184,3 +186,33 @@ def test_dgrad_whole_and_split_remainder_tiles(geg, fmt, N, cu):
     fn = geg.gnf4_grouped_dgrad if fmt == "nf4" else geg.gmxfp4_grouped_dgrad
     dx = fn(up_u16_as_bf16(dy), g["sizes"], g["w"], g["s"], opts=geg.Opts(0, 0, None, cu), check_errors=True)
     assert_close(bf16_to_f64(dx), oracle.dgrad_ref(dy, d["sizes"], C.weight_fn(d), 512), f"dgrad {fmt} N={N} cu={cu}")
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+def test_workspace_without_split_region_runs_unsplit(geg, fmt):
+    # a workspace that holds everything but the split partials: the call that
+    # would split each remainder tile 4 ways (grid of 8) runs it whole instead
+    import torch
+    K, N = 8192, 320
+    log(f"case: tiled forward {fmt}, K={K} N={N} sizes={SIZES} cu_limit=8, workspace without the split region")
+    c, d = _case(fmt, K, N, seed=51)
+    g = upload_case(d)
+    M = int(np.sum(SIZES))
+    op = geg.GEG_OP_NF4_FWD if fmt == "nf4" else geg.GEG_OP_MXFP4_FWD
+    o = geg.Opts(2, 0, None, 8)
+    need = geg.geg_workspace_bytes(op, M, N, K, 2, o)
+    tail = 256 * 128 * 256 * 4
+    ws = geg.Workspace(need)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=g["a"].device)
+    fn = getattr(geg.lib(), "gnf4_grouped_gemm" if fmt == "nf4" else "gmxfp4_grouped_gemm")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = fn(p(g["a"]), p(g["sizes"]), p(g["w"]), p(g["s"]), p(out), M, N, K, 2, p(ws.buf), need - tail,
+            ctypes.byref(o), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, geg.lib().geg_last_error()
+    assert ws.read_error() == 0
+    ref = oracle.grouped_ref(d["a_bits"], d["sizes"], C.weight_fn(d), c.N)
+    assert_close(bf16_to_f64(out), ref, f"forward {fmt} without the split region")
+    # the same call with the whole workspace splits and agrees within fp32 order
+    full = geg.gnf4_grouped_gemm if fmt == "nf4" else geg.gmxfp4_grouped_gemm
+    split = full(g["a"], g["sizes"], g["w"], g["s"], workspace=ws, opts=o, check_errors=True)
+    assert_close(bf16_to_f64(split), ref, f"forward {fmt} split")

@@ -88,7 +88,7 @@ def test_noalloc_refuses_scratch_past_its_array(geg):
     st = geg.lib().gnf4_grouped_gemm_noalloc(P, P, P, P, P, 40000, 256, 2048, 4, None, None, None)
     assert st == 5
     assert b"144 MiB" in geg.lib().geg_last_error()
-    # within the array (fp16 rows plus the 32 MiB of split remainder tiles) the
-    # same sizes go on to the pointer checks
-    st = geg.lib().gnf4_grouped_gemm_noalloc(P, P, P, P, P, 25000, 256, 2048, 4, None, None, None)
+    # within the array (117 MiB of fp16 rows; the optional 32 MiB of split
+    # remainder tiles left out) the same sizes go on to the pointer checks
+    st = geg.lib().gnf4_grouped_gemm_noalloc(P, P, P, P, P, 30000, 256, 2048, 4, None, None, None)
     assert st not in (0, 5)
