@@ -441,7 +441,8 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
 // halves; every wavefront runs the same barriers whatever its H).
 template <Fmt F, bool DG, bool TAIL, int H>
 __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
-                                           int wave, int lane, f32x4 (&acc)[8][4]) {
+                                           int wave, int lane, f32x4 (&acc)[8][4],
+                                           const __amdgpu_buffer_rsrc_t& RX, int32_t* rx) {
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
@@ -466,12 +467,19 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   BDec<F> dec;
   Ops ops;
   // Prologue: stage 0 into buffer 0; raw data of stages 1 (activations) and
-  // 1, 2 (codes) in flight; the first half of stage 1's decode state.
+  // 1, 2 (codes) in flight; the first half of stage 1's decode state. NF4: the
+  // tile's row exponents go to LDS for the epilogue (their load is issued first,
+  // so the wait for stage 0's activations covers it).
+  int32_t rxv = 0;
+  if constexpr (F == NF4)
+    if (threadIdx.x < BM) rxv = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(RX, threadIdx.x * 4u, 0, 0);
   load_a(ra, src, 0, true);
   load_b<F>(rb[0], src, 0, true);
   load_b<F>(rb[1], src, 1, nst > 1);
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], 0, C, wave, lane);
+  if constexpr (F == NF4)
+    if (threadIdx.x < BM) rx[threadIdx.x] = rxv;
   {
     NF4Half h;
     u32x2 even;
@@ -549,6 +557,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   __shared__ int32_t p_u0[kMaxExperts + 1];
   __shared__ int32_t p_u1[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) TileLds<DG> L;
+  __shared__ __attribute__((aligned(16))) int32_t rx[F == NF4 ? BM : 1];   // NF4 row exponents of the tile
 
   const int64_t C = DG ? g.N : g.K;   // contraction length
   const int64_t O = DG ? g.K : g.N;   // output width
@@ -613,24 +622,24 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane, st0);
+    // NF4 row exponents of the tile (rows past the expert read 0)
+    const __amdgpu_buffer_rsrc_t RX = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(F == NF4 ? g.rexp + row0 : g.sizes), (short)0, F == NF4 ? rows * 4 : 0, 0x00020000);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, DG, TAIL, 2>(L, src, Cp, Kp, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 2>(L, src, Cp, Kp, wave, lane, acc, RX, rx);
     else if (vrows > 0)
-      run_tile_h<F, DG, TAIL, 1>(L, src, Cp, Kp, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 1>(L, src, Cp, Kp, wave, lane, acc, RX, rx);
     else
-      run_tile_h<F, DG, TAIL, 0>(L, src, Cp, Kp, wave, lane, acc);
+      run_tile_h<F, DG, TAIL, 0>(L, src, Cp, Kp, wave, lane, acc, RX, rx);
 
     // NF4: the fp16 operand rows were multiplied by 2^-rexp[row] (exact), so each
     // result is multiplied by 2^rexp[row] (exact) where it is read out for its
     // bf16 rounding, and the adapter delta joins the accumulators at the same
     // 2^-rexp[row] scale. Rows past the expert read exponent 0 and are never
     // stored. MXFP4 operands are not scaled.
-    const __amdgpu_buffer_rsrc_t RE = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int32_t*>(F == NF4 ? g.rexp + row0 + 128 * wm : g.sizes), (short)0,
-        F == NF4 ? max(0, rows - 128 * wm) * 4 : 0, 0x00020000);
     auto rowexp = [&](int r) -> int {   // r: row of the wavefront's 128-row block
-      if constexpr (F == NF4) return (int)__builtin_amdgcn_raw_buffer_load_b32(RE, (uint32_t)(r * 4), 0, 0);
+      if constexpr (F == NF4) return rx[128 * wm + r];
       return 0;
     };
     auto unscale = [](float v, int ex) -> float {
@@ -681,8 +690,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
     if (split) {
       // fp32 partial sums of this piece (rows < 128: wave row 0 only), output
       // columns in final order, row factor 2^rexp already applied; the fixup
-      // launch adds the S pieces in order. No LDS use: the next tile's prologue
-      // may follow directly.
+      // launch adds the S pieces in order. The barrier after it keeps the next
+      // tile's prologue from rewriting the row exponents while they are read.
       if (wm == 0) {
         float* P = g.tail_part + (int64_t)w * kTailPieceFloats;
         const int c16 = (DG && F == NF4) ? dg_col(lane & 15) : (lane & 15);
@@ -696,6 +705,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
             for (int j = 0; j < 4; ++j) P[r * BN + 64 * wn + 16 * j + c16] = unscale(acc[i][j][q], ex);
           }
       }
+      __syncthreads();
       continue;
     }
     uint16_t* E = L.epi[wave];
