@@ -341,11 +341,21 @@ __device__ __forceinline__ u32x4 b_frag(const uint16_t* Bbuf, const BRd<DG>& br,
   }
 }
 
+// Accumulator layout. With the weight fragment as the instruction's first
+// operand and the activation fragment as its second (TR), block (i, j) comes out
+// transposed: lane l holds row 16 i + l % 16, columns 16 j + 4 (l / 16) + q,
+// q = 0..3, i.e. four adjacent outputs of one row (one row exponent, one 8-byte
+// LDS write). The NF4 dgrad keeps the other order (lane l: rows
+// 16 i + 4 (l / 16) + q, column 16 j + l % 16), because its MFMA columns are in
+// the NF4 slot order and four adjacent ones are not adjacent outputs.
+template <Fmt F, bool DG>
+constexpr bool kTr = !(DG && F == NF4);
+
 // The 4 MFMAs of one 16-row A fragment with the substep's 4 B fragments.
-template <Fmt F>
+template <Fmt F, bool TR>
 __device__ __forceinline__ void mfma_row(const u32x4& a, const u32x4 (&b)[4], f32x4 (&acc)[4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = mfma16<F>(a, b[j], acc[j]);
+  for (int j = 0; j < 4; ++j) acc[j] = TR ? mfma16<F>(b[j], a, acc[j]) : mfma16<F>(a, b[j], acc[j]);
 }
 
 // Operand registers carried from one stage into the next: the first substep's
@@ -413,7 +423,7 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
     if (g == 14 && NI > 0) ops.a[0] = lds_frag(An);
     if (g == 15 && NI > 1) ops.a[1] = lds_frag(An + 16 * BK);
     if (g == 15 && NI > 2) ops.a[2] = lds_frag(An + 32 * BK);
-    if (i < NI) mfma_row<F>(af[g], sub ? b1 : ops.b, acc[i]);
+    if (i < NI) mfma_row<F, kTr<F, DG>>(af[g], sub ? b1 : ops.b, acc[i]);
     // staging of the next stage (on the last stage it writes stale data into the
     // free buffer, which nothing reads; this keeps the groups free of branches)
     if (g < 4) {
@@ -649,8 +659,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 
     // Epilogue through LDS: each wavefront writes its 128x64 block as bf16
     // (row-major, rows padded to 144 B) over the idle stage buffers, then stores
-    // whole 16-byte row pieces. acc[i][j][q] is row 16i + 4(lane/16) + q,
-    // column 16j + lane%16 of the block; every write offset is a constant from
+    // whole 16-byte row pieces. acc[i][j][q] is row 16i + lane%16, column
+    // 16j + 4(lane/16) + q of the block (kTr), or row 16i + 4(lane/16) + q,
+    // column 16j + lane%16 (NF4 dgrad); every write offset is a constant from
     // the lane's base.
     if (g.lora_r > 0 && rows > 128 * wm && piece == 0) {   // a split tile adds the delta once
       // Low-rank adapter delta into the accumulators before their bf16 rounding:
@@ -680,9 +691,16 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
                                         -rowexp(16 * i + r16));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].hi, acc[i][j]);
-            acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].lo, acc[i][j]);
-            acc[i][j] = mfma16<MXFP4>(au.lo, bq[j].hi, acc[i][j]);
+            // the same operand order as the main loop, so the layouts agree
+            if constexpr (kTr<F, DG>) {
+              acc[i][j] = mfma16<MXFP4>(bq[j].hi, au.hi, acc[i][j]);
+              acc[i][j] = mfma16<MXFP4>(bq[j].lo, au.hi, acc[i][j]);
+              acc[i][j] = mfma16<MXFP4>(bq[j].hi, au.lo, acc[i][j]);
+            } else {
+              acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].hi, acc[i][j]);
+              acc[i][j] = mfma16<MXFP4>(au.hi, bq[j].lo, acc[i][j]);
+              acc[i][j] = mfma16<MXFP4>(au.lo, bq[j].hi, acc[i][j]);
+            }
           }
         }
       }
@@ -694,45 +712,56 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       // tile's prologue from rewriting the row exponents while they are read.
       if (wm == 0) {
         float* P = g.tail_part + (int64_t)w * kTailPieceFloats;
-        const int c16 = (DG && F == NF4) ? dg_col(lane & 15) : (lane & 15);
+        if constexpr (kTr<F, DG>) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 16 * i + 4 * (lane >> 4) + q;
+          for (int i = 0; i < 8; ++i) {
+            const int r = 16 * i + (lane & 15);
             const int ex = rowexp(r);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) P[r * BN + 64 * wn + 16 * j + c16] = unscale(acc[i][j][q], ex);
+            for (int j = 0; j < 4; ++j) {
+              f32x4 v;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = unscale(acc[i][j][q], ex);
+              *reinterpret_cast<f32x4*>(&P[r * BN + 64 * wn + 16 * j + 4 * (lane >> 4)]) = v;
+            }
           }
+        } else {
+          const int c16 = dg_col(lane & 15);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 16 * i + 4 * (lane >> 4) + q;
+              const int ex = rowexp(r);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) P[r * BN + 64 * wn + 16 * j + c16] = unscale(acc[i][j][q], ex);
+            }
+        }
       }
       __syncthreads();
       continue;
     }
     uint16_t* E = L.epi[wave];
+    auto bf16x2 = [](float x, float y) -> uint32_t {
+      return (uint32_t)to_bf16(x) | ((uint32_t)to_bf16(y) << 16);
+    };
     if (!DG && g.glu) {
-      // Fused expert block: columns 2c, 2c+1 (lanes l, l ^ 1) are the gate and
-      // up of unit c. Each lane of a pair computes two of the four rows' units:
-      // the even lane rows q = 0, 1, the odd lane rows q = 2, 3, trading the
-      // missing halves with its neighbour. The wavefront's 128 x 32 unit block
-      // goes through LDS like the plain epilogue.
-      const bool odd = lane & 1;
-      uint16_t* base = E + (4 * (lane >> 4) + (odd ? 2 : 0)) * kEpiLd + ((lane & 15) >> 1);
+      // Fused expert block: columns 2c, 2c+1 are the gate and up of unit c, so a
+      // lane's four adjacent columns (transposed layout) are units
+      // 8 j + 2 (l / 16) and the next one of its row, written as one bf16 pair.
+      // The wavefront's 128 x 32 unit block goes through LDS like the plain
+      // epilogue.
+      uint16_t* base = E + (lane & 15) * kEpiLd + 2 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        int ex[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ex[q] = rowexp(16 * i + 4 * (lane >> 4) + q);
+        const int ex = rowexp(16 * i + (lane & 15));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           f32x4 v;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = unscale(acc[i][j][q], ex[q]);
-          const float r0 = lane_pair_swap(odd ? v[0] : v[2]);
-          const float r1 = lane_pair_swap(odd ? v[1] : v[3]);
-          const float a0 = odd ? swiglu(r0, v[2]) : swiglu(v[0], r0);
-          const float a1 = odd ? swiglu(r1, v[3]) : swiglu(v[1], r1);
-          base[(16 * i) * kEpiLd + 8 * j] = to_bf16(a0);
-          base[(16 * i + 1) * kEpiLd + 8 * j] = to_bf16(a1);
+          for (int q = 0; q < 4; ++q) v[q] = unscale(acc[i][j][q], ex);
+          *reinterpret_cast<uint32_t*>(base + (16 * i) * kEpiLd + 8 * j) =
+              bf16x2(swiglu(v[0], v[1]), swiglu(v[2], v[3]));
         }
       }
       __syncthreads();
@@ -758,8 +787,20 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
       __syncthreads();   // the stage buffers are reused by the next tile
       continue;
     }
-    {
-      uint16_t* base = E + (4 * (lane >> 4)) * kEpiLd + ((DG && F == NF4) ? dg_col(lane & 15) : (lane & 15));
+    if constexpr (kTr<F, DG>) {
+      // four adjacent outputs of one row per block: one 8-byte write
+      uint16_t* base = E + (lane & 15) * kEpiLd + 4 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ex = rowexp(16 * i + (lane & 15));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x2*>(base + (16 * i) * kEpiLd + 16 * j) =
+              u32x2{bf16x2(unscale(acc[i][j][0], ex), unscale(acc[i][j][1], ex)),
+                    bf16x2(unscale(acc[i][j][2], ex), unscale(acc[i][j][3], ex))};
+      }
+    } else {
+      uint16_t* base = E + (4 * (lane >> 4)) * kEpiLd + dg_col(lane & 15);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
