@@ -764,7 +764,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
               bf16x2(swiglu(v[0], v[1]), swiglu(v[2], v[3]));
         }
       }
-      __syncthreads();
+      // each wavefront reads back only its own block: LDS keeps a wavefront's
+      // accesses in order, so no workgroup barrier is needed here
+      __builtin_amdgcn_wave_barrier();
       const int chunk = lane & 3;
       const int64_t O2 = O >> 1;
       const int64_t col = (n0 >> 1) + 32 * wn + 8 * chunk;
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
           for (int j = 0; j < 4; ++j) base[(16 * i + q) * kEpiLd + 16 * j] = to_bf16(unscale(acc[i][j][q], ex));
         }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();   // own block only (as in the gated epilogue)
     {
       const int chunk = lane & 7;
       const int64_t col = n0 + 64 * wn + 8 * chunk;
