@@ -447,12 +447,31 @@ __device__ __forceinline__ void tile_stage(TileLds<DG>& L, const TileSrc& src, i
   }
 }
 
+// The first loads of a tile (stage 0's activations and codes, stage 1's codes,
+// the NF4 row exponents), issued ahead of its prologue: the tiled kernel issues
+// them right after the previous tile's K loop, so that their latency passes
+// under that tile's epilogue.
+template <Fmt F>
+__device__ __forceinline__ void tile_prefetch(const TileSrc& src, int nst, const int32_t* rexp, int rows,
+                                              RawA& ra, RawB (&rb)[2], int32_t& rxv) {
+  rxv = 0;
+  if constexpr (F == NF4) {
+    // rows past the expert read 0
+    const __amdgpu_buffer_rsrc_t RX =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(rexp), (short)0, rows * 4, 0x00020000);
+    if (threadIdx.x < BM) rxv = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(RX, threadIdx.x * 4u, 0, 0);
+  }
+  load_a(ra, src, 0, true);
+  load_b<F>(rb[0], src, 0, true);
+  load_b<F>(rb[1], src, 1, nst > 1);
+}
+
 // Main loop over the K stages of one tile (H = the wavefront's active 64-row
 // halves; every wavefront runs the same barriers whatever its H).
 template <Fmt F, bool DG, bool TAIL, int H>
 __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, int64_t C, int64_t K,
-                                           int wave, int lane, f32x4 (&acc)[8][4],
-                                           const __amdgpu_buffer_rsrc_t& RX, int32_t* rx) {
+                                           int wave, int lane, f32x4 (&acc)[8][4], RawA& ra,
+                                           RawB (&rb)[2], int32_t rxv, int32_t* rx) {
   const int wm = wave >> 2, wn = wave & 3;
   const int r16 = lane & 15;
   const uint32_t aoff = (uint32_t)swz(128 * wm + r16, lane >> 4);
@@ -472,20 +491,12 @@ __device__ __forceinline__ void run_tile_h(TileLds<DG>& L, const TileSrc& src, i
   uint32_t m4 = 0x04040404u, base = 0x03020100u;
   asm volatile("" : "+v"(base));
   asm volatile("" : "+s"(m4));
-  RawA ra;
-  RawB rb[2];
   BDec<F> dec;
   Ops ops;
-  // Prologue: stage 0 into buffer 0; raw data of stages 1 (activations) and
-  // 1, 2 (codes) in flight; the first half of stage 1's decode state. NF4: the
-  // tile's row exponents go to LDS for the epilogue (their load is issued first,
-  // so the wait for stage 0's activations covers it).
-  int32_t rxv = 0;
-  if constexpr (F == NF4)
-    if (threadIdx.x < BM) rxv = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(RX, threadIdx.x * 4u, 0, 0);
-  load_a(ra, src, 0, true);
-  load_b<F>(rb[0], src, 0, true);
-  load_b<F>(rb[1], src, 1, nst > 1);
+  // Prologue: stage 0 into buffer 0 from the registers tile_prefetch filled
+  // (during the previous tile's epilogue); raw data of stages 1 (activations)
+  // and 1, 2 (codes) in flight; the first half of stage 1's decode state. NF4:
+  // the tile's row exponents go to LDS for the epilogue.
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_a_piece<F, DG, TAIL>(ra, q, L.a[0], 0, C, wave, lane);
   if constexpr (F == NF4)
@@ -592,38 +603,87 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
   const int S = tp.S;
   const int32_t total = total0 + tp.unsplit + (total1 - tp.unsplit) * S;
 
-  for (int32_t base = 0; base < total; base += G) {
-    const int32_t u = base + slot;
-    if (u >= total) break;
-    int e, mt, nt, piece = 0;
-    bool split = false;
-    int32_t w = 0;   // split units: partial-sum slot
+  // Unit u: its expert, rows, output columns and contraction range.
+  struct Unit {
+    int e, piece, st0;
+    bool split;
+    int32_t w;   // split units: partial-sum slot
+    int64_t row0, n0, Cp, Kp;
+    int rows;
+  };
+  auto decode_unit = [&](int32_t u) -> Unit {
+    Unit t;
+    int mt, nt;
+    t.piece = 0;
+    t.split = false;
+    t.w = 0;
     if (u < total0) {
-      e = find_expert(p_u0, g.E, u);
-      const int32_t lu = u - p_u0[e];
+      t.e = find_expert(p_u0, g.E, u);
+      const int32_t lu = u - p_u0[t.e];
       mt = lu / n_tiles;
       nt = lu % n_tiles;
     } else {
       int32_t t1 = u - total0;
       if (t1 >= tp.unsplit) {
-        split = true;
-        w = t1 - tp.unsplit;
-        piece = w % S;
-        t1 = tp.unsplit + w / S;
+        t.split = true;
+        t.w = t1 - tp.unsplit;
+        t.piece = t.w % S;
+        t1 = tp.unsplit + t.w / S;
       }
-      e = find_expert(p_u1, g.E, t1);
-      mt = (p_off[e + 1] - p_off[e]) / BM;   // the remainder block
-      nt = t1 - p_u1[e];
+      t.e = find_expert(p_u1, g.E, t1);
+      mt = (p_off[t.e + 1] - p_off[t.e]) / BM;   // the remainder block
+      nt = t1 - p_u1[t.e];
     }
-    const int64_t row0 = (int64_t)p_off[e] + (int64_t)mt * BM;
-    const int rows = min(BM, (int)(p_off[e + 1] - row0));
-    const int64_t n0 = (int64_t)nt * BN;
+    t.row0 = (int64_t)p_off[t.e] + (int64_t)mt * BM;
+    t.rows = min(BM, (int)(p_off[t.e + 1] - t.row0));
+    t.n0 = (int64_t)nt * BN;
     // A piece reads like a tile of a shorter contraction: stages piece nst / S ..
     // (piece + 1) nst / S - 1, the last piece running to the end (with the
     // contraction's own tail).
-    const int st0 = split ? piece * nst / S : 0;
-    const int64_t Cp = !split ? C : piece == S - 1 ? C - (int64_t)st0 * BK : (int64_t)((piece + 1) * nst / S - st0) * BK;
-    const int64_t Kp = DG ? g.K : Cp;
+    t.st0 = t.split ? t.piece * nst / S : 0;
+    t.Cp = !t.split ? C
+           : t.piece == S - 1 ? C - (int64_t)t.st0 * BK
+                              : (int64_t)((t.piece + 1) * nst / S - t.st0) * BK;
+    t.Kp = DG ? g.K : t.Cp;
+    return t;
+  };
+  auto unit_src = [&](const Unit& t) { return tile_src<F, DG>(g, t.e, t.row0, t.rows, t.n0, wave, lane, t.st0); };
+  auto prefetch = [&](const Unit& t, const TileSrc& src, RawA& ra, RawB (&rb)[2], int32_t& rxv) {
+    tile_prefetch<F>(src, (int)((t.Cp + BK - 1) / BK), F == NF4 ? g.rexp + t.row0 : g.sizes, t.rows, ra, rb, rxv);
+  };
+
+  // NF4 forward: the first loads of the next unit go out between this unit's K
+  // loop and its epilogue (the other instantiations issue them at the start of
+  // the unit: there the extra live registers cost spills in the stage loop).
+  constexpr bool kPf = F == NF4 && !DG;
+  RawA ra;
+  RawB rb[2];
+  int32_t rxv = 0;
+  Unit cu{}, nu{};
+  TileSrc src{}, nsrc{};
+  int32_t u = slot;
+  if (kPf && u < total) {
+    cu = decode_unit(u);
+    src = unit_src(cu);
+    prefetch(cu, src, ra, rb, rxv);
+  }
+  auto advance = [&] {
+    if constexpr (kPf) {
+      cu = nu;
+      src = nsrc;
+    }
+  };
+  for (; u < total; u += G, advance()) {
+    if constexpr (!kPf) {
+      cu = decode_unit(u);
+      src = unit_src(cu);
+      prefetch(cu, src, ra, rb, rxv);
+    }
+    const int e = cu.e, piece = cu.piece;
+    const bool split = cu.split;
+    const int32_t w = cu.w;
+    const int64_t row0 = cu.row0, n0 = cu.n0;
+    const int rows = cu.rows;
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -631,17 +691,18 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const TileSrc src = tile_src<F, DG>(g, e, row0, rows, n0, wave, lane, st0);
-    // NF4 row exponents of the tile (rows past the expert read 0)
-    const __amdgpu_buffer_rsrc_t RX = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int32_t*>(F == NF4 ? g.rexp + row0 : g.sizes), (short)0, F == NF4 ? rows * 4 : 0, 0x00020000);
     const int vrows = __builtin_amdgcn_readfirstlane(rows - 128 * wm);
     if (vrows > 64)
-      run_tile_h<F, DG, TAIL, 2>(L, src, Cp, Kp, wave, lane, acc, RX, rx);
+      run_tile_h<F, DG, TAIL, 2>(L, src, cu.Cp, cu.Kp, wave, lane, acc, ra, rb, rxv, rx);
     else if (vrows > 0)
-      run_tile_h<F, DG, TAIL, 1>(L, src, Cp, Kp, wave, lane, acc, RX, rx);
+      run_tile_h<F, DG, TAIL, 1>(L, src, cu.Cp, cu.Kp, wave, lane, acc, ra, rb, rxv, rx);
     else
-      run_tile_h<F, DG, TAIL, 0>(L, src, Cp, Kp, wave, lane, acc, RX, rx);
+      run_tile_h<F, DG, TAIL, 0>(L, src, cu.Cp, cu.Kp, wave, lane, acc, ra, rb, rxv, rx);
+    if (kPf && u + G < total) {
+      nu = decode_unit(u + G);
+      nsrc = unit_src(nu);
+      prefetch(nu, nsrc, ra, rb, rxv);
+    }
 
     // NF4: the fp16 operand rows were multiplied by 2^-rexp[row] (exact), so each
     // result is multiplied by 2^rexp[row] (exact) where it is read out for its
